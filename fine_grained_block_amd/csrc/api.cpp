@@ -1,0 +1,179 @@
+// api.cpp — the C-ABI of libfgb: argument validation, device check, path selection, launches.
+//
+// Validation is synchronous and happens before anything is enqueued; there is no fallback
+// path (an unsupported request is an error: vLLM "FP8 W8A8", "GEMM kernel selection"; an
+// unsupported scale format raises: Transformers "Fine-grained FP8", "UE8M0 scale format").
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/fgb.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid and index arithmetic bound
+constexpr int kMaxDevices = 64;
+
+// 0 = unknown, 1 = gfx950, -1 = other
+int g_dev_ok[kMaxDevices];
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return FGB_ERR_DEVICE;
+  }
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return FGB_ERR_DEVICE;
+    }
+    g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return g_dev_ok[dev] == 1 ? FGB_OK : FGB_ERR_DEVICE;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FGB_OK : FGB_ERR_LAUNCH; }
+
+// Shared validation of the GEMM operands (dense: E = 1, offsets unused).
+int validate_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                  const uint8_t* w_q, const void* s_w, int s_w_fmt, const void* y, int y_dtype,
+                  int64_t ldy, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FGB_ERR_SHAPE;
+  if (N % FGB_BLOCK || K % FGB_BLOCK) return FGB_ERR_SHAPE;
+  if (s_w_fmt != FGB_SCALE_F32 && s_w_fmt != FGB_SCALE_UE8M0) return FGB_ERR_ENUM;
+  if (y_dtype != FGB_OUT_BF16 && y_dtype != FGB_OUT_F32) return FGB_ERR_ENUM;
+  if (M == 0) return FGB_OK;
+  if (!a_q || !s_a || !w_q || !s_w || !y) return FGB_ERR_NULL;
+  if (lda < K || ldy < N || ld_sa < M) return FGB_ERR_STRIDE;
+  const int64_t ybytes = y_dtype == FGB_OUT_BF16 ? 2 : 4;
+  if (!aligned16(a_q) || !aligned16(s_a) || !aligned16(w_q) || !aligned16(s_w) || !aligned16(y))
+    return FGB_ERR_ALIGN;
+  if (lda % 16 || (ldy * ybytes) % 16 || (ld_sa * 4) % 16) return FGB_ERR_ALIGN;
+  return FGB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fgb_status_string(int status) {
+  switch (status) {
+    case FGB_OK: return "FGB_OK";
+    case FGB_ERR_NULL: return "FGB_ERR_NULL: a required pointer is NULL";
+    case FGB_ERR_SHAPE: return "FGB_ERR_SHAPE: invalid size (N and K must be positive multiples of 128)";
+    case FGB_ERR_STRIDE: return "FGB_ERR_STRIDE: leading dimension smaller than the row length";
+    case FGB_ERR_ALIGN: return "FGB_ERR_ALIGN: pointer or row pitch not 16-byte aligned";
+    case FGB_ERR_ENUM: return "FGB_ERR_ENUM: unknown enum value";
+    case FGB_ERR_WORKSPACE: return "FGB_ERR_WORKSPACE: workspace missing or too small";
+    case FGB_ERR_DEVICE: return "FGB_ERR_DEVICE: no current device or the device is not gfx950";
+    case FGB_ERR_LAUNCH: return "FGB_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown fgb status";
+  }
+}
+
+int fgb_abi_version(void) { return FGB_ABI_VERSION; }
+
+int fgb_act_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                           int64_t ldq, float* s_a, int64_t ld_sa, void* stream) {
+  if (M < 0 || K <= 0 || M >= kMaxDim || K >= kMaxDim || K % FGB_BLOCK) return FGB_ERR_SHAPE;
+  if (M == 0) return FGB_OK;
+  if (!x || !q || !s_a) return FGB_ERR_NULL;
+  if (ldx < K || ldq < K || ld_sa < M) return FGB_ERR_STRIDE;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s_a)) return FGB_ERR_ALIGN;
+  if ((ldx * 2) % 16 || ldq % 16 || (ld_sa * 4) % 16) return FGB_ERR_ALIGN;
+  if ((M * (K / FGB_BLOCK)) >= kMaxDim) return FGB_ERR_SHAPE;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_act_quant(x, M, K, ldx, q, ldq, s_a, ld_sa, (hipStream_t)stream));
+}
+
+int fgb_weight_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* w_q, void* s_w,
+                              int s_w_fmt, void* stream) {
+  if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim || N % FGB_BLOCK || K % FGB_BLOCK) return FGB_ERR_SHAPE;
+  if (s_w_fmt != FGB_SCALE_F32 && s_w_fmt != FGB_SCALE_UE8M0) return FGB_ERR_ENUM;
+  if (N == 0 || K == 0) return FGB_OK;
+  if (!w || !w_q || !s_w) return FGB_ERR_NULL;
+  if (!aligned16(w) || !aligned16(w_q)) return FGB_ERR_ALIGN;
+  if (s_w_fmt == FGB_SCALE_F32 && ((uintptr_t)s_w & 3u)) return FGB_ERR_ALIGN;
+  if ((N / FGB_BLOCK) * (K / FGB_BLOCK) >= kMaxDim) return FGB_ERR_SHAPE;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_weight_quant(w, N, K, w_q, s_w, s_w_fmt, (hipStream_t)stream));
+}
+
+size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > 64 || N <= 0 || K <= 0 || N % FGB_BLOCK || K % FGB_BLOCK) return 0;
+  return fgb::decode_workspace_bytes(M, N, K);
+}
+
+int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                        const uint8_t* w_q, const void* s_w, int s_w_fmt, void* y, int y_dtype,
+                        int64_t ldy, int64_t M, int64_t N, int64_t K, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K);
+  if (st != FGB_OK || M == 0) return st;
+  const bool decode = M <= 64;
+  if (decode) {
+    const size_t need = fgb::decode_workspace_bytes(M, N, K);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FGB_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return FGB_ERR_ALIGN;
+  }
+  st = check_device();
+  if (st != FGB_OK) return st;
+  fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K, nullptr, 1};
+  if (decode) return launch_status(fgb::launch_gemm_decode(a, workspace, (hipStream_t)stream));
+  return launch_status(fgb::launch_gemm_prefill(a, (hipStream_t)stream));
+}
+
+size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, int32_t E) {
+  (void)total_M; (void)N; (void)K; (void)E;
+  return 0;
+}
+
+int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                                const uint8_t* w_q, const void* s_w, int s_w_fmt,
+                                const int32_t* expert_offsets, int32_t E, int64_t total_M,
+                                void* y, int y_dtype, int64_t ldy, int64_t N, int64_t K,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (E <= 0 || E > 65536) return FGB_ERR_SHAPE;
+  int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, total_M, N, K);
+  if (st != FGB_OK || total_M == 0) return st;
+  if (!expert_offsets) return FGB_ERR_NULL;
+  if (((uintptr_t)expert_offsets & 3u)) return FGB_ERR_ALIGN;
+  // tile-count bound: (ceil(total_M/128) + E) * N/128 workgroups
+  if (((total_M + 127) / 128 + E) * (N / 128) >= kMaxDim) return FGB_ERR_SHAPE;
+  st = check_device();
+  if (st != FGB_OK) return st;
+  fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, total_M, N, K,
+                  expert_offsets, E};
+  return launch_status(fgb::launch_gemm_grouped(a, (hipStream_t)stream));
+}
+
+int fgb_fp8_encode(const float* in, uint8_t* out, int64_t n, int fmt, int saturate, void* stream) {
+  if (n < 0) return FGB_ERR_SHAPE;
+  if (fmt < FGB_FP8_E4M3 || fmt > FGB_FP8_E4M3_INT) return FGB_ERR_ENUM;
+  if (n == 0) return FGB_OK;
+  if (!in || !out) return FGB_ERR_NULL;
+  if (((uintptr_t)in & 3u)) return FGB_ERR_ALIGN;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_encode(in, out, n, fmt, saturate, (hipStream_t)stream));
+}
+
+int fgb_fp8_decode(const uint8_t* in, float* out, int64_t n, int fmt, void* stream) {
+  if (n < 0) return FGB_ERR_SHAPE;
+  if (fmt < FGB_FP8_E4M3 || fmt > FGB_UE8M0) return FGB_ERR_ENUM;
+  if (n == 0) return FGB_OK;
+  if (!in || !out) return FGB_ERR_NULL;
+  if (((uintptr_t)out & 3u)) return FGB_ERR_ALIGN;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_decode(in, out, n, fmt, (hipStream_t)stream));
+}
+
+}  // extern "C"

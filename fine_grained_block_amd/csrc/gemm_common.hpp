@@ -1,0 +1,64 @@
+// gemm_common.hpp — pieces shared by the block-scaled FP8 GEMM kernels (gfx950).
+//
+// Matrix-core mapping.  gfx950's v_mfma_f32_16x16x128_f8f6f4 multiplies a 16x128 E4M3 tile by
+// a 128x16 E4M3 tile into 16x16 float32: exactly one 128-wide K-block (the activation group and
+// weight block edge of Transformers "Fine-grained FP8", intro) per instruction.  The per-block
+// product sum P therefore comes out of one instruction, and the block's scales are applied to
+// it in registers: acc += P * (s_a[m, kb] * s_w[n/128, kb]).
+//
+// Operand roles: the weight tile is the MFMA "A" operand (16 output features n) and the
+// activation tile the "B" operand (16 tokens m).  Each lane then holds D[n0+4*(lane/16)+r][m0 +
+// lane%16], r = 0..3: one token's scale per lane and four consecutive output features, which
+// store as one 8-byte bf16 group.
+//
+// Both operands are loaded with the same K-permutation (lane group g = lane/16 supplies bytes
+// 32g .. 32g+31 of the 128-byte K-block row), so the dot product is over the same k for A and B
+// whatever the hardware's internal k order within the instruction.
+#pragma once
+#include "fgb_device.hpp"
+
+namespace fgb {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  // format selects 0/0 = E4M3 for both operands; scale operands 0 select the unscaled opcode
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// Weight-block scale as float32 from either storage format.
+template <int SWF>
+__device__ __forceinline__ float load_sw(const void* s_w, int64_t idx) {
+  if constexpr (SWF == 0) {
+    return reinterpret_cast<const float*>(s_w)[idx];
+  } else {
+    return dec_ue8m0(reinterpret_cast<const uint8_t*>(s_w)[idx]);
+  }
+}
+
+// Store four consecutive output features of one token.
+template <int OUT>
+__device__ __forceinline__ void store4(void* y, int64_t ldy, int64_t m, int64_t n, v4f v) {
+  if constexpr (OUT == 0) {
+    uint16_t* p = reinterpret_cast<uint16_t*>(y) + m * ldy + n;
+    uint2 w;
+    w.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = w;
+  } else {
+    float* p = reinterpret_cast<float*>(y) + m * ldy + n;
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// Workgroup id remapping so that consecutive logical tiles run on the same XCD (workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2).  A bijection on [0, nwg).
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+  const int per = nwg / 8, rem = nwg % 8;
+  const int xcd = bid % 8, local = bid / 8;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+}
+
+}  // namespace fgb

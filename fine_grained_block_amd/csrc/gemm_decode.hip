@@ -1,0 +1,194 @@
+// gemm_decode.hip — split-K block-scaled FP8 GEMM for small M (decode, M <= 64), gfx950.
+//
+// Same result as the prefill path (Transformers "Fine-grained FP8", "DeepGEMM fast path"), but
+// for few tokens the weight stream dominates (bytes per weight: 1 for FP8, per the Baseten
+// NVFP4 summary, "Less memory, more compute"), so the kernel is organised to keep HBM busy:
+//   * a workgroup = 4 waves covers 64 weight rows (one 16-row MFMA tile per wave) and a slice
+//     of whole K-blocks; the grid is (N/64) x S slices, S chosen so ~2k waves stream W;
+//   * the activation slice [Mpad x slice] is staged once in LDS and shared by the 4 waves;
+//   * each wave streams its W rows straight into registers in the MFMA operand layout
+//     (32 contiguous bytes per lane), up to 8 K-blocks in flight;
+//   * S > 1 writes float32 partials to the workspace [S][M][N]; a second kernel adds them in
+//     slice order (deterministic) and rounds to the output type.
+#include "gemm_common.hpp"
+#include "internal.h"
+
+namespace fgb {
+
+namespace {
+
+constexpr int THREADS = 256;
+constexpr int ROWS_PER_WG = 64;
+constexpr int CH = 8;                 // K-blocks of W in flight per wave
+constexpr int LDS_LIMIT = 64 * 1024;  // activation slice budget
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+template <int MT, int SWF, int OUT>
+__global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kpw, int S, float* ws) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];  // [kpw][16*MT rows][128 B]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t K = p.K, N = p.N, M = p.M;
+  const int KB = (int)(K / 128);
+  const int nt = blockIdx.x / S, split = blockIdx.x - (blockIdx.x / S) * S;
+  const int kb0 = split * kpw;
+  const int kb1 = min(KB, kb0 + kpw);
+  const int nk = kb1 - kb0;
+  const int64_t n0 = (int64_t)nt * ROWS_PER_WG + wave * 16;  // this wave's 16 weight rows
+  const int64_t nb = n0 / 128;
+  constexpr int MROWS = 16 * MT;
+
+  // stage activations [MROWS x nk*128] into LDS (rows >= M replicate row M-1; discarded later)
+  {
+    const int chunks = MROWS * nk * 8;
+    for (int c = tid; c < chunks; c += THREADS) {
+      const int ch = c & 7;
+      const int row = (c >> 3) % MROWS;
+      const int kk = (c >> 3) / MROWS;
+      const int64_t m = row < M ? row : M - 1;
+      const int4 v = *reinterpret_cast<const int4*>(p.a_q + m * p.lda + (int64_t)(kb0 + kk) * 128 + ch * 16);
+      *reinterpret_cast<int4*>(a_lds + kk * MROWS * 128 + swz(row, ch)) = v;
+    }
+  }
+
+  const int g = lane >> 4;
+  const uint8_t* wrow = p.w_q + (n0 + (lane & 15)) * K + 32 * g;
+  int64_t m_lane[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int64_t m = j * 16 + (lane & 15);
+    m_lane[j] = m < M ? m : M - 1;
+  }
+
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  __syncthreads();
+
+  for (int c0 = 0; c0 < nk; c0 += CH) {
+    int4 wlo[CH], whi[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (c0 + u < nk) {
+        const uint8_t* src = wrow + (int64_t)(kb0 + c0 + u) * 128;
+        wlo[u] = *reinterpret_cast<const int4*>(src);
+        whi[u] = *reinterpret_cast<const int4*>(src + 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (c0 + u < nk) {
+        const int kb = kb0 + c0 + u;
+        const float sw = load_sw<SWF>(p.s_w, nb * KB + kb);
+        v8i af;
+        af[0] = wlo[u].x; af[1] = wlo[u].y; af[2] = wlo[u].z; af[3] = wlo[u].w;
+        af[4] = whi[u].x; af[5] = whi[u].y; af[6] = whi[u].z; af[7] = whi[u].w;
+        const uint8_t* ab = a_lds + (c0 + u) * MROWS * 128;
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const int r = j * 16 + (lane & 15);
+          const int4 lo = *reinterpret_cast<const int4*>(ab + swz(r, 2 * g));
+          const int4 hi = *reinterpret_cast<const int4*>(ab + swz(r, 2 * g + 1));
+          v8i bf;
+          bf[0] = lo.x; bf[1] = lo.y; bf[2] = lo.z; bf[3] = lo.w;
+          bf[4] = hi.x; bf[5] = hi.y; bf[6] = hi.z; bf[7] = hi.w;
+          const float sc = p.s_a[(int64_t)kb * p.ld_sa + m_lane[j]] * sw;
+          const v4f P = mfma_e4m3_16x16x128(af, bf);
+          acc[j] += P * sc;
+        }
+      }
+    }
+  }
+
+  const int64_t n = n0 + 4 * g;
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int64_t m = j * 16 + (lane & 15);
+    if (m < M) {
+      if (S == 1) {
+        store4<OUT>(p.y, p.ldy, m, n, acc[j]);
+      } else {
+        float* dst = ws + ((int64_t)split * M + m) * N + n;
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      }
+    }
+  }
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int S, int64_t M,
+                                                            int64_t N, void* y, int64_t ldy) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one float4 of y
+  const int64_t total = M * (N / 4);
+  if (q >= total) return;
+  const int64_t m = q / (N / 4), n = (q - m * (N / 4)) * 4;
+  float4 s = *reinterpret_cast<const float4*>(ws + m * N + n);
+  for (int i = 1; i < S; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(ws + ((int64_t)i * M + m) * N + n);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  store4<OUT>(y, ldy, m, n, v4f{s.x, s.y, s.z, s.w});
+}
+
+int mtiles(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
+int kb_per_wg(int64_t M, int64_t N, int64_t K) {
+  const int KB = (int)(K / 128);
+  const int64_t waves_per_split = N / 16;
+  int S = (int)((2048 + waves_per_split - 1) / waves_per_split);
+  S = S < 1 ? 1 : (S > KB ? KB : S);
+  int kpw = (KB + S - 1) / S;
+  const int lds_cap = LDS_LIMIT / (16 * mtiles(M) * 128);
+  if (kpw > lds_cap) kpw = lds_cap;
+  return kpw;
+}
+
+}  // namespace
+
+int decode_splits(int64_t M, int64_t N, int64_t K) {
+  const int KB = (int)(K / 128);
+  const int kpw = kb_per_wg(M, N, K);
+  return (KB + kpw - 1) / kpw;
+}
+
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = decode_splits(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream) {
+  const int kpw = kb_per_wg(a.M, a.N, a.K);
+  const int S = decode_splits(a.M, a.N, a.K);
+  const int MT = mtiles(a.M);
+  const size_t lds = (size_t)16 * MT * kpw * 128;
+  const dim3 grid((unsigned)((a.N / ROWS_PER_WG) * S)), block(THREADS);
+  float* ws = reinterpret_cast<float*>(workspace);
+#define FGB_DEC(MT_, SWF, OUT) \
+  hipLaunchKernelGGL((gemm_decode_kernel<MT_, SWF, OUT>), grid, block, lds, stream, a, kpw, S, ws)
+#define FGB_DEC_MT(SWF, OUT)        \
+  do {                              \
+    if (MT == 1) FGB_DEC(1, SWF, OUT); \
+    else if (MT == 2) FGB_DEC(2, SWF, OUT); \
+    else FGB_DEC(4, SWF, OUT);      \
+  } while (0)
+  const int out_direct = a.y_dtype;  // S == 1 writes y directly
+  if (a.s_w_fmt == 0) {
+    if (out_direct == 0) FGB_DEC_MT(0, 0); else FGB_DEC_MT(0, 1);
+  } else {
+    if (out_direct == 0) FGB_DEC_MT(1, 0); else FGB_DEC_MT(1, 1);
+  }
+#undef FGB_DEC_MT
+#undef FGB_DEC
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || S == 1) return err;
+  const int64_t total = a.M * (a.N / 4);
+  const dim3 rgrid((unsigned)((total + 255) / 256));
+  if (a.y_dtype == 0)
+    hipLaunchKernelGGL(splitk_reduce_kernel<0>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+}  // namespace fgb

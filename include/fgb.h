@@ -1,0 +1,153 @@
+/*
+ * fgb.h — fine-grained FP8 W8A8 block quantization and GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The scheme (Hugging Face Transformers, "Fine-grained FP8", intro and "DeepGEMM fast path"):
+ * weights are E4M3 with one scale per 128x128 block; activations are quantized at run time
+ * ("dynamic") per token in groups of 128 along the input dimension K; every FP8 linear is one
+ * block-scaled GEMM, and MoE expert matmuls use a grouped variant.  Weight scales are float32
+ * or packed UE8M0 powers of two ("UE8M0 scale format").  E4M3/E5M2 are defined on the vLLM
+ * "FP8 W8A8" page, "Two FP8 representations".
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless stated otherwise; the caller owns every buffer.
+ *     The library keeps no pointer after a call returns, allocates no device memory, and never
+ *     synchronizes: work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *   - Outputs must not alias inputs.
+ *   - Validation is synchronous: an invalid argument returns a negative status before anything
+ *     is enqueued.  There is no fallback path: a call either runs the gfx950 kernels or fails.
+ *     (An explicitly requested backend that the hardware cannot run is an error, not a silent
+ *     fallback: vLLM "FP8 W8A8", "GEMM kernel selection"; an unsupported scale format raises:
+ *     Transformers "Fine-grained FP8", "UE8M0 scale format".)
+ *   - Sizes and leading dimensions are in ELEMENTS.  Base pointers must be 16-byte aligned and
+ *     every row pitch in bytes a multiple of 16, else FGB_ERR_ALIGN.
+ *   - M == 0 (or total_M == 0) is a valid no-op returning FGB_OK.
+ *   - N and K must be multiples of 128 (the block edge), else FGB_ERR_SHAPE.
+ *   - Inputs must be finite and codes must not be NaN (0x7F/0xFF); otherwise results are
+ *     unspecified (no fault, but no meaning either).
+ */
+#ifndef FGB_H
+#define FGB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FGB_ABI_VERSION 1
+#define FGB_BLOCK 128
+
+typedef enum {
+  FGB_OK = 0,
+  FGB_ERR_NULL = -1,      /* a required pointer is NULL */
+  FGB_ERR_SHAPE = -2,     /* negative size, N or K not a multiple of 128, E <= 0, size too large */
+  FGB_ERR_STRIDE = -3,    /* a leading dimension smaller than its row length */
+  FGB_ERR_ALIGN = -4,     /* base pointer or row pitch not 16-byte aligned */
+  FGB_ERR_ENUM = -5,      /* unknown enum value */
+  FGB_ERR_WORKSPACE = -6, /* workspace NULL or smaller than the queried size */
+  FGB_ERR_DEVICE = -7,    /* no current device, or the device is not gfx950 */
+  FGB_ERR_LAUNCH = -8     /* the HIP runtime reported an error at launch */
+} fgb_status;
+
+typedef enum { FGB_SCALE_F32 = 0, FGB_SCALE_UE8M0 = 1 } fgb_scale_fmt; /* scale_fmt "float" | "ue8m0" */
+typedef enum { FGB_OUT_BF16 = 0, FGB_OUT_F32 = 1 } fgb_out_dtype;      /* F32: diagnostic/test mode */
+typedef enum {
+  FGB_FP8_E4M3 = 0,     /* hardware conversion path used by the quantizers */
+  FGB_FP8_E5M2 = 1,
+  FGB_UE8M0 = 2,
+  FGB_FP8_E4M3_INT = 3  /* encode only: integer bit-field encoder, to check the hardware path */
+} fgb_fp8_fmt;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* fgb_status_string(int status);
+
+/* FGB_ABI_VERSION of the loaded library. */
+int fgb_abi_version(void);
+
+/*
+ * Dynamic per-token, per-group activation quantization
+ * (Transformers "Fine-grained FP8", intro: one scale per token per 128-group of K).
+ *   x     bf16 bit patterns [M, ldx] row-major; group g of row m is x[m, 128g .. 128g+127].
+ *   q     E4M3 codes [M, ldq] row-major (written for k < K).
+ *   s_a   float32 scales, K-BLOCK-MAJOR: s_a[g * ld_sa + m], g < K/128, ld_sa >= M.
+ * For every group: a = max|x| (exact); s = fl32(a / 448) (IEEE float32 division);
+ * q = E4M3(fl32(x / s)) rounded to nearest-even and saturated to +-448; a == 0 gives s = 0 and
+ * codes +-0 by the sign of x.  Results are bit-exact.
+ * Requires K % 128 == 0, ldx >= K, ldq >= K, ld_sa >= M, ld_sa % 4 == 0.
+ */
+int fgb_act_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                           uint8_t* q, int64_t ldq, float* s_a, int64_t ld_sa, void* stream);
+
+/*
+ * Per 128x128 block weight quantization (Transformers "Fine-grained FP8", intro;
+ * "UE8M0 scale format" for fmt == FGB_SCALE_UE8M0).
+ *   w     bf16 bit patterns [N, K] row-major (dense, ld = K).
+ *   w_q   E4M3 codes [N, K] row-major.
+ *   s_w   [N/128, K/128] row-major: float32 (FGB_SCALE_F32: s = fl32(amax/448)) or one byte per
+ *         block (FGB_SCALE_UE8M0: the smallest power of two >= amax/448, code = log2(s) + 127,
+ *         clamped to 0..254; amax == 0 gives code 127).  Codes are E4M3(fl32(w / s)), RNE,
+ *         saturating.  Bit-exact.
+ */
+int fgb_weight_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* w_q, void* s_w,
+                              int s_w_fmt, void* stream);
+
+/* Host query: workspace bytes fgb_w8a8_block_gemm needs for this shape (0 if none). */
+size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Block-scaled W8A8 GEMM (Transformers "Fine-grained FP8", "DeepGEMM fast path"; vLLM
+ * "FP8 W8A8", intro: both operands 8-bit):
+ *   y[m, n] = sum_kb s_a[kb*ld_sa + m] * s_w[n/128, kb] * sum_{k in kb} A_q[m, k] * W_q[n, k]
+ * with every per-block product sum accumulated in float32 on the matrix cores, the scaled sum
+ * over K-blocks in float32, and the result rounded to bf16 (RNE) or stored as float32.
+ *   a_q   E4M3 [M, lda] row-major;  s_a  float32 K-block-major [K/128, ld_sa], ld_sa >= M;
+ *   w_q   E4M3 [N, K] row-major (the Linear layout; y = A . W^T), dense;
+ *   s_w   [N/128, K/128] row-major, float32 or UE8M0 bytes per s_w_fmt;
+ *   y     [M, ldy] row-major, bf16 bit patterns or float32 per y_dtype.
+ * M <= 64 selects the split-K streaming path; it needs `workspace` of
+ * fgb_gemm_workspace_bytes(M, N, K) bytes (float32 partial sums; contents on entry ignored).
+ */
+int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                        const uint8_t* w_q, const void* s_w, int s_w_fmt,
+                        void* y, int y_dtype, int64_t ldy,
+                        int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host query: workspace bytes fgb_grouped_w8a8_block_gemm needs (0 if none). */
+size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, int32_t E);
+
+/*
+ * Grouped (MoE expert) block-scaled GEMM (Transformers "Fine-grained FP8", "DeepGEMM fast path"
+ * and "UE8M0 scale format": expert matmuls over FP8 block weights).  Rows are sorted by
+ * expert; expert e owns rows expert_offsets[e] .. expert_offsets[e+1]-1 and computes the
+ * fgb_w8a8_block_gemm result with w_q + e*N*K and its own scales.
+ *   a_q [total_M, lda]; s_a [K/128, ld_sa], ld_sa >= total_M;
+ *   w_q [E, N, K]; s_w [E, N/128, K/128] (float32 or UE8M0 bytes);
+ *   expert_offsets  DEVICE int32 [E+1], offsets[0] == 0, nondecreasing, offsets[E] == total_M
+ *                   (a precondition: checking it would need a device synchronization);
+ *   total_M         host copy of offsets[E];
+ *   y [total_M, ldy].
+ * Experts with no rows are legal and write nothing.
+ */
+int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                                const uint8_t* w_q, const void* s_w, int s_w_fmt,
+                                const int32_t* expert_offsets, int32_t E, int64_t total_M,
+                                void* y, int y_dtype, int64_t ldy, int64_t N, int64_t K,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Element-wise codecs (vLLM "FP8 W8A8", "Two FP8 representations"; UE8M0 per Transformers
+ * "Fine-grained FP8", "UE8M0 scale format").
+ *   encode: float32 in[n] -> u8 out[n].  E4M3: RNE, saturating to +-448 (`saturate` ignored).
+ *           E5M2: RNE; saturate != 0 clamps to +-57344, else overflow gives +-inf.
+ *           UE8M0: the smallest power of two >= in/448 (the weight-scale rule), in >= 0.
+ *   decode: u8 in[n] -> float32 out[n] (E4M3, E5M2, UE8M0 = 2^(c-127), 0xFF = NaN).
+ */
+int fgb_fp8_encode(const float* in, uint8_t* out, int64_t n, int fmt, int saturate, void* stream);
+int fgb_fp8_decode(const uint8_t* in, float* out, int64_t n, int fmt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FGB_H */

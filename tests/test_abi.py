@@ -1,0 +1,146 @@
+"""C-ABI tests that run without a GPU: the library loads, exports every symbol the header
+declares, and rejects invalid arguments synchronously (before any device work).
+
+Calls with otherwise-valid arguments use fake device addresses; they must stop at the device
+check, so those cases only run where no GPU is present.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fgb.h")
+
+from fine_grained_block_amd import _lib  # noqa: E402
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation returns first
+ERR = dict(OK=0, NULL=-1, SHAPE=-2, STRIDE=-3, ALIGN=-4, ENUM=-5, WORKSPACE=-6, DEVICE=-7, LAUNCH=-8)
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fgb_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.lib_path):
+        pytest.fail("libfgb.so is not built (run `python -m fine_grained_block_amd.build`)")
+    return _lib.lib()
+
+
+def test_exports_every_header_symbol(L):
+    funcs = header_functions()
+    assert len(funcs) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.lib_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fgb_[a-z0-9_]+)", out))
+    missing = [f for f in funcs if f not in exported]
+    assert not missing, missing
+    assert set(funcs) == set(_lib.EXPORTS)
+    for f in funcs:
+        assert getattr(L, f) is not None
+
+
+def test_version_and_status_strings(L):
+    assert L.fgb_abi_version() == 1
+    for name, code in ERR.items():
+        s = L.fgb_status_string(code).decode()
+        assert name in s
+    assert L.fgb_status_string(12345).decode() == "unknown fgb status"
+
+
+def _gemm(L, **kw):
+    a = dict(a_q=FAKE, lda=1024, s_a=FAKE, ld_sa=256, w_q=FAKE, s_w=FAKE, fmt=0, y=FAKE, ydt=0,
+             ldy=512, M=256, N=512, K=1024, ws=None, wsb=0)
+    a.update(kw)
+    return L.fgb_w8a8_block_gemm(a["a_q"], a["lda"], a["s_a"], a["ld_sa"], a["w_q"], a["s_w"], a["fmt"],
+                                 a["y"], a["ydt"], a["ldy"], a["M"], a["N"], a["K"], a["ws"], a["wsb"], None)
+
+
+def test_gemm_validation(L):
+    assert _gemm(L, K=1000, lda=1008) == ERR["SHAPE"]
+    assert _gemm(L, N=500) == ERR["SHAPE"]
+    assert _gemm(L, M=-1) == ERR["SHAPE"]
+    assert _gemm(L, M=0) == ERR["OK"]          # no-op, before any pointer or device check
+    assert _gemm(L, fmt=2) == ERR["ENUM"]
+    assert _gemm(L, ydt=7) == ERR["ENUM"]
+    assert _gemm(L, a_q=None) == ERR["NULL"]
+    assert _gemm(L, s_w=None) == ERR["NULL"]
+    assert _gemm(L, lda=512) == ERR["STRIDE"]
+    assert _gemm(L, ldy=256) == ERR["STRIDE"]
+    assert _gemm(L, ld_sa=100) == ERR["STRIDE"]
+    assert _gemm(L, a_q=FAKE + 8) == ERR["ALIGN"]
+    assert _gemm(L, lda=1032) == ERR["ALIGN"]
+    assert _gemm(L, ld_sa=258) == ERR["ALIGN"]
+    # decode path needs a workspace when it splits K
+    need = L.fgb_gemm_workspace_bytes(1, 4096, 4096)
+    assert need > 0
+    assert _gemm(L, M=1, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=4) == ERR["WORKSPACE"]
+    assert _gemm(L, M=1, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=4, ws=FAKE, wsb=need - 1) == ERR["WORKSPACE"]
+    assert L.fgb_gemm_workspace_bytes(128, 4096, 4096) == 0
+
+
+@pytest.mark.skipif(_has_gpu(), reason="fake pointers must not reach a real device")
+def test_valid_arguments_stop_at_device_check(L):
+    assert _gemm(L) == ERR["DEVICE"]
+    assert L.fgb_act_quant_group128(FAKE, 64, 1024, 1024, FAKE, 1024, FAKE, 64, None) == ERR["DEVICE"]
+    assert L.fgb_fp8_decode(FAKE, FAKE, 256, 0, None) == ERR["DEVICE"]
+
+
+def test_act_quant_validation(L):
+    f = L.fgb_act_quant_group128
+    assert f(FAKE, 64, 1000, 1000, FAKE, 1008, FAKE, 64, None) == ERR["SHAPE"]
+    assert f(FAKE, 0, 1024, 1024, FAKE, 1024, FAKE, 64, None) == ERR["OK"]
+    assert f(None, 64, 1024, 1024, FAKE, 1024, FAKE, 64, None) == ERR["NULL"]
+    assert f(FAKE, 64, 1024, 512, FAKE, 1024, FAKE, 64, None) == ERR["STRIDE"]
+    assert f(FAKE, 64, 1024, 1024, FAKE, 1024, FAKE, 32, None) == ERR["STRIDE"]
+    assert f(FAKE, 64, 1024, 1028, FAKE, 1024, FAKE, 64, None) == ERR["ALIGN"]
+    assert f(FAKE, 64, 1024, 1024, FAKE, 1024, FAKE, 66, None) == ERR["ALIGN"]
+    assert f(FAKE + 2, 64, 1024, 1024, FAKE, 1024, FAKE, 64, None) == ERR["ALIGN"]
+
+
+def test_weight_quant_and_grouped_validation(L):
+    w = L.fgb_weight_quant_block128
+    assert w(FAKE, 130, 128, FAKE, FAKE, 0, None) == ERR["SHAPE"]
+    assert w(FAKE, 128, 128, FAKE, FAKE, 5, None) == ERR["ENUM"]
+    assert w(None, 128, 128, FAKE, FAKE, 0, None) == ERR["NULL"]
+    g = L.fgb_grouped_w8a8_block_gemm
+    args = [FAKE, 1024, FAKE, 256, FAKE, FAKE, 0, FAKE, 4, 256, FAKE, 0, 512, 512, 1024, None, 0, None]
+    bad = list(args); bad[8] = 0
+    assert g(*bad) == ERR["SHAPE"]
+    bad = list(args); bad[7] = None
+    assert g(*bad) == ERR["NULL"]
+    bad = list(args); bad[7] = FAKE + 2
+    assert g(*bad) == ERR["ALIGN"]
+    bad = list(args); bad[9] = 0
+    assert g(*bad) == ERR["OK"]
+    bad = list(args); bad[13] = 100
+    assert g(*bad) == ERR["SHAPE"]
+
+
+def test_codec_validation(L):
+    assert L.fgb_fp8_encode(FAKE, FAKE, 16, 9, 1, None) == ERR["ENUM"]
+    assert L.fgb_fp8_decode(FAKE, FAKE, 16, 3, None) == ERR["ENUM"]
+    assert L.fgb_fp8_encode(FAKE, FAKE, -1, 0, 1, None) == ERR["SHAPE"]
+    assert L.fgb_fp8_encode(None, FAKE, 16, 0, 1, None) == ERR["NULL"]
+    assert L.fgb_fp8_decode(FAKE, FAKE + 1, 16, 0, None) == ERR["ALIGN"]
+    assert L.fgb_fp8_encode(FAKE, FAKE, 0, 0, 1, None) == ERR["OK"]
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "lib_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.lib()

@@ -1,0 +1,128 @@
+"""GPU parity: w8a8_block_gemm (prefill and split-K decode paths) against the oracle.
+
+Operands are quantized by the oracle on the CPU and uploaded, so these tests isolate the GEMM;
+the end-to-end tests quantize on the GPU and compare with the oracle run from the same bf16
+inputs.  Tolerances: fp32 mode max|y - y_ref| <= 2e-3 max|y_ref|; bf16 mode per element
+|y - y_ref| <= 2e-3 max|y_ref| + 1 bf16 ulp of y_ref.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_amd as fgb
+import workloads
+from oracle import blockquant, gemm
+from tests.gemm_helpers import (bf16_tensor_to_f64, check_t1, check_t2, oracle_operands, ref,
+                                to_dev_bf16, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(ops, dev, out_dtype):
+    aq, sa, wq, sw = upload(*ops, dev)
+    y = fgb.gemm(aq, sa, wq, sw, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 1024, 1024),                         # tiny config (decode path: M <= 64)
+    (65, 256, 256), (128, 128, 128), (200, 384, 640), (300, 1024, 1024), (513, 768, 2048),
+    (1, 256, 1024), (8, 512, 384), (32, 1024, 2048), (64, 256, 128), (17, 128, 4096),
+])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_gemm_parity(dev, M, N, K, fmt):
+    ops = oracle_operands(M, N, K, key=1, fmt=fmt)
+    yref = ref(*ops, fmt=fmt)
+    y32 = _run(ops, dev, torch.float32).cpu().numpy()
+    check_t1(y32, yref)
+    y16 = _run(ops, dev, torch.bfloat16)
+    check_t2(bf16_tensor_to_f64(y16), yref)
+    # the bf16 epilogue is the RNE of the same float32 accumulators
+    assert np.array_equal(bf16_tensor_to_f64(y16), gemm.bf16_rne(y32.astype(np.float64)))
+
+
+@pytest.mark.parametrize("M", [1, 33, 64, 130, 512])
+def test_exact_integer_case(dev, M):
+    """Scales are all exactly 1 and every product sum is an integer below 2^24: the float32
+    result must equal the oracle bit for bit, and bf16 must be its RNE."""
+    rng = np.random.default_rng(M)
+    N, K = 384, 1024
+    ints = np.array([-4, -3, -2, -1, 0, 1, 2, 3, 4], dtype=np.float32)
+    A = rng.choice(ints, size=(M, K))
+    W = rng.choice(ints, size=(N, K))
+    A[:, ::128] = 448.0
+    W[:, 64::128] = -448.0
+    aq, sa = blockquant.act_quant(A)
+    wq, sw = blockquant.weight_quant(W)
+    yref = gemm.gemm_ref(aq, sa, wq, sw)
+    assert np.all(sa == 1) and np.all(sw == 1) and np.all(np.abs(yref) < 2 ** 24)
+    y32 = _run((aq, sa, wq, sw), dev, torch.float32).cpu().numpy()
+    assert np.array_equal(y32.astype(np.float64), yref)
+    y16 = _run((aq, sa, wq, sw), dev, torch.bfloat16)
+    assert np.array_equal(bf16_tensor_to_f64(y16), gemm.bf16_rne(yref))
+
+
+def test_homogeneity_in_weight_scales(dev):
+    ops = oracle_operands(96, 256, 512, key=2)
+    aq, sa, wq, sw = ops
+    y1 = _run(ops, dev, torch.float32).cpu().numpy()
+    y2 = _run((aq, sa, wq, (sw * np.float32(2)).astype(np.float32)), dev, torch.float32).cpu().numpy()
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_output_canaries_and_strides(dev):
+    """Writes stay inside [M, N] of a wider output buffer (ldy > N); the guard bytes keep
+    their pattern."""
+    M, N, K = 100, 256, 256
+    ops = oracle_operands(M, N, K, key=3)
+    aq, sa, wq, sw = upload(*ops, dev)
+    for dt in (torch.bfloat16, torch.float32):
+        buf = torch.full((M + 2, N + 64), -7.0, dtype=dt, device=dev)
+        y = buf[1:M + 1, 8:N + 8]
+        fgb.gemm(aq, sa, wq, sw, out=y)
+        torch.cuda.synchronize()
+        b = buf.float().cpu().numpy()
+        assert np.all(b[0] == -7) and np.all(b[M + 1] == -7)
+        assert np.all(b[:, :8] == -7) and np.all(b[:, N + 8:] == -7)
+        check_t2(b[1:M + 1, 8:N + 8].astype(np.float64), ref(*ops))
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 64])
+def test_decode_shapes_reduced(dev, M):
+    """Decode path at moderate (N, K), including several K splits."""
+    for N, K in [(4096, 4096), (1536, 14336)]:
+        ops = oracle_operands(M, N, K, key=4)
+        yref = ref(*ops)
+        y16 = _run(ops, dev, torch.bfloat16)
+        check_t2(bf16_tensor_to_f64(y16), yref)
+
+
+def test_end_to_end_linear(dev):
+    """quantize (GPU) + gemm (GPU) from bf16 inputs against the oracle from the same inputs."""
+    M, N, K = 256, 512, 1024
+    x = workloads.activations(M, K, key=(0, 5, 0, 0))
+    w = workloads.weights(N, K, key=(0, 5, 1, 0))
+    wq, sw = fgb.quantize_weight(to_dev_bf16(w, dev))
+    y = fgb.linear(to_dev_bf16(x, dev), wq, sw)
+    torch.cuda.synchronize()
+    yref = ref(*oracle_operands(M, N, K, x=x, w=w))
+    check_t2(bf16_tensor_to_f64(y), yref)
+
+
+def test_empty_m_is_noop(dev):
+    aq = torch.empty((0, 256), dtype=torch.uint8, device=dev)
+    sa = torch.empty((2, 4), dtype=torch.float32, device=dev)
+    wq = torch.zeros((128, 256), dtype=torch.uint8, device=dev)
+    sw = torch.ones((1, 2), dtype=torch.float32, device=dev)
+    y = fgb.gemm(aq, sa, wq, sw)
+    assert y.shape == (0, 128)
+
+
+def test_rejects_bad_shapes(dev):
+    aq = torch.zeros((16, 200), dtype=torch.uint8, device=dev)
+    sa = torch.zeros((2, 16), dtype=torch.float32, device=dev)
+    wq = torch.zeros((128, 200), dtype=torch.uint8, device=dev)
+    sw = torch.ones((1, 2), dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError, match="FGB_ERR_SHAPE"):
+        fgb.gemm(aq, sa, wq, sw)
