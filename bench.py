@@ -1,0 +1,327 @@
+"""Benchmark: fine-grained FP8 W8A8 linears on one MI355X.
+
+A step is one pass of the hot path over the Llama-3-8B-shaped prefill batch (M = 4096 tokens):
+for each of the four projections (QKV 6144x4096, O 4096x4096, gate+up 28672x4096, down
+4096x14336) the bf16 activations are quantized dynamically (1x128 groups) and the block-scaled
+FP8 GEMM produces bf16 outputs.  Weights are quantized once beforehand (offline, untimed);
+activations are resident in HBM when the timed region starts.
+
+Prints ONE JSON line.  `value` is the whole step's useful GEMM throughput (2*M*N*K summed over
+the four projections, divided by the step time, quantization included).  `roofline` is for the
+dominant kernel (the prefill GEMM), from HIP events recorded around every GEMM launch on the
+launch stream inside the timed region.  `cpu_baseline` times the CPU oracle on a bounded sample
+of the same workload.  `extra` carries the other rows of the hot path (decode, UE8M0 prefill,
+grouped MoE, quantization bandwidth), each timed on its own.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--suite", choices=["step", "all"], default="all",
+                   help="'step': only the headline step; 'all': also decode, UE8M0 prefill, MoE, quant")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=256, help="tokens in the oracle sample")
+    p.add_argument("--cpu-cols", type=int, default=2048, help="output features per projection in the oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fine_grained_block_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------------------------
+def headline_step(args, torch, fgb, workloads, np):
+    dev = torch.device("cuda:0")
+    M = workloads.LLAMA3_8B_PREFILL_M
+    layers = []
+    for i, (name, N, K) in enumerate(workloads.LLAMA3_8B_LINEARS):
+        x = torch.from_numpy(workloads.activations(M, K, key=(0, 1, 0, i)).view(np.int16)).to(dev).view(torch.bfloat16)
+        w = torch.from_numpy(workloads.weights(N, K, key=(0, 1, 1, i)).view(np.int16)).to(dev).view(torch.bfloat16)
+        wq, sw = fgb.quantize_weight(w)  # offline
+        del w
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        layers.append(dict(name=name, N=N, K=K, x=x, wq=wq, sw=sw, q=q, sa=sa, y=y))
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        for j, L in enumerate(layers):
+            if ev is not None:
+                ev[j][0].record()
+            fgb.quantize(L["x"], out=(L["q"], L["sa"]))
+            if ev is not None:
+                ev[j][1].record()
+            fgb.gemm(L["q"], L["sa"], L["wq"], L["sw"], out=L["y"])
+            if ev is not None:
+                ev[j][2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(args.steps):
+        step(evs[s])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    gemm_ms = [sum(evs[s][j][1].elapsed_time(evs[s][j][2]) for s in range(args.steps)) / args.steps for j in range(len(layers))]
+    quant_ms = [sum(evs[s][j][0].elapsed_time(evs[s][j][1]) for s in range(args.steps)) / args.steps for j in range(len(layers))]
+    flops = [2.0 * M * L["N"] * L["K"] for L in layers]
+    qbytes = [3.03125 * M * L["K"] for L in layers]
+    per = {}
+    for L, g, q, f, b in zip(layers, gemm_ms, quant_ms, flops, qbytes):
+        per[L["name"]] = dict(N=L["N"], K=L["K"], gemm_us=round(g * 1e3, 1), gemm_tflops=round(f / g / 1e9, 1),
+                              quant_us=round(q * 1e3, 1), quant_gbs=round(b / q / 1e6, 1))
+    return dict(M=M, ms_step=ms_step, wall_s=wall, gemm_ms=gemm_ms, quant_ms=quant_ms, flops=flops,
+                qbytes=qbytes, per=per)
+
+
+# ---------------------------------------------------------------------------------------------
+def _randn_bf16(torch, shape, gen, dev, outliers=True, std=1.0):
+    """Device-side draw of the same recipes as `workloads` (N(0,1) with 1% x20 outliers, or
+    N(0, std)), for the extra timing suites where bit-identity with the oracle is not needed."""
+    x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    if outliers:
+        n = x.numel()
+        idx = torch.randperm(n, generator=gen, device=dev)[: int(round(0.01 * n))]
+        x.view(-1)[idx] *= 20.0
+    else:
+        x *= std
+    return x.to(torch.bfloat16)
+
+
+def _graph_time(torch, fn, reps):
+    """Capture `reps` calls of fn(i) in a HIP graph, replay it, return microseconds per call."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(2):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (3 * reps)
+
+
+def _event_time(torch, fn, reps, flush=None):
+    ts = []
+    for i in range(reps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def extra_suites(torch, fgb, workloads, np):
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    out = {}
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        flush_buf.fill_(1)
+
+    # decode (split-K) — hipGraph loop over rotating weight copies (> 2x MALL in total)
+    dec = {}
+    for (name, N, K) in workloads.DECODE_SHAPES:
+        w = _randn_bf16(torch, (N, K), gen, dev, outliers=False, std=0.02)
+        wq0, sw = fgb.quantize_weight(w)
+        del w
+        copies = max(2, -(-2 * MALL_BYTES // (N * K)) + 1)
+        wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+        for M in workloads.DECODE_MS:
+            x = _randn_bf16(torch, (M, K), gen, dev)
+            q, sa = fgb.quantize(x)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(16, fgb.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+            us = _graph_time(torch, lambda i: fgb.gemm(q, sa, wqs[i % copies], sw, out=y, workspace=ws), 4 * copies)
+            byts = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * K / 128 + 2 * M * N
+            dec[f"{name}_{N}x{K}_M{M}"] = dict(us=round(us, 2), gbs=round(byts / us / 1e3, 1),
+                                                frac_hbm=round(byts / us / 1e3 / PEAK_HBM_GBS, 3))
+        del wqs, wq0
+    out["decode_splitk"] = dec
+
+    # DeepSeek-V3-shaped prefill with UE8M0 weight scales (M = 8192), flushed between calls
+    ds = {}
+    M = workloads.DEEPSEEK_V3_PREFILL_M
+    for (name, N, K) in workloads.DEEPSEEK_V3_LINEARS:
+        w = _randn_bf16(torch, (N, K), gen, dev, outliers=False, std=0.02)
+        wq, sw = fgb.quantize_weight(w, "ue8m0")
+        del w
+        x = _randn_bf16(torch, (M, K), gen, dev)
+        q, sa = fgb.quantize(x)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = _event_time(torch, lambda i: fgb.gemm(q, sa, wq, sw, out=y), 5, flush)
+        f = 2.0 * M * N * K
+        ds[f"{name}_{N}x{K}"] = dict(us=round(us, 1), tflops=round(f / us / 1e6, 1), frac_mfma=round(f / us / 1e6 / PEAK_FP8_TFLOPS, 3))
+        del wq, x, q, y
+    out["prefill_ue8m0_m8192"] = ds
+
+    # MoE grouped GEMM: 32 experts, 4096 tokens top-8 Zipf(1.1)
+    moe = {}
+    tok, offsets, counts = workloads.moe_routing()
+    off_d = torch.from_numpy(offsets).to(dev)
+    T = int(offsets[-1])
+    for nm, (N, K) in [("gate_up", workloads.MOE["gate_up"]), ("down", workloads.MOE["down"])]:
+        w = _randn_bf16(torch, (32 * N, K), gen, dev, outliers=False, std=0.02)
+        wq, sw = fgb.quantize_weight(w)  # 128-row blocks never straddle experts (N % 128 == 0)
+        del w
+        wq = wq.view(32, N, K)
+        sw = sw.view(32, N // 128, K // 128)
+        x = _randn_bf16(torch, (T, K), gen, dev)
+        q, sa = fgb.quantize(x)
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        us = _event_time(torch, lambda i: fgb.grouped_gemm(q, sa, wq, sw, off_d, out=y), 5, flush)
+        f = 2.0 * T * N * K
+        moe[f"{nm}_{N}x{K}"] = dict(us=round(us, 1), tflops=round(f / us / 1e6, 1), frac_mfma=round(f / us / 1e6 / PEAK_FP8_TFLOPS, 3))
+        del wq, x, q, y
+    moe["expert_rows_max_min"] = [int(counts.max()), int(counts.min())]
+    out["moe_grouped_e32"] = moe
+
+    # activation quantization bandwidth at the prefill shapes (flushed between calls)
+    qb = {}
+    for (M, K) in [(4096, 4096), (4096, 14336), (8192, 7168), (8192, 18432), (32768, 7168)]:
+        x = _randn_bf16(torch, (M, K), gen, dev)
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+        us = _event_time(torch, lambda i: fgb.quantize(x, out=(q, sa)), 7, flush)
+        b = 3.03125 * M * K
+        qb[f"{M}x{K}"] = dict(us=round(us, 1), gbs=round(b / us / 1e3, 1), frac_hbm=round(b / us / 1e3 / PEAK_HBM_GBS, 3))
+        del x, q, sa
+    out["act_quant"] = qb
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+def cpu_baseline(args, workloads, np):
+    """The CPU oracle (as it is) on a bounded sample of the step: the first `cpu_rows` tokens and
+    the first `cpu_cols` output features of each projection, full K; act_quant + gemm_ref.
+    Weight quantization of the sampled rows is offline (untimed), as on the GPU."""
+    from oracle import blockquant, gemm
+    R, C = args.cpu_rows, args.cpu_cols
+    prepared = []
+    for i, (name, N, K) in enumerate(workloads.LLAMA3_8B_LINEARS):
+        x = workloads.activations(workloads.LLAMA3_8B_PREFILL_M, K, key=(0, 1, 0, i))[:R]
+        w = workloads.weights(N, K, key=(0, 1, 1, i))[:C]
+        wq, sw = blockquant.weight_quant(w)
+        prepared.append((x, wq, sw, K))
+    t0 = time.perf_counter()
+    flops = 0.0
+    for x, wq, sw, K in prepared:
+        aq, sa = blockquant.act_quant(x)
+        gemm.gemm_ref(aq, sa, wq, sw)
+        flops += 2.0 * R * C * K
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=min(cores, threads), kind="oracle",
+                sample=f"first {R} tokens x first {C} output features of each of the 4 projections, full K "
+                       f"(act_quant + exact-partial float64 gemm_ref); {flops / 1e9:.2f} GFLOP in {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layers would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fine_grained_block_amd as fgb
+    import workloads
+
+    fgb.lib()
+    torch.cuda.init()
+    res = headline_step(args, torch, fgb, workloads, np)
+    total_flops = sum(res["flops"])
+    gemm_total_ms = sum(res["gemm_ms"])
+    achieved = total_flops / (gemm_total_ms * 1e-3) / 1e12  # TFLOP/s over the GEMM launches
+    extra = {"headline_per_projection": res["per"], "kernel_source_hash": kernel_source_hash()}
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            t = json.load(fh)
+        if t.get("kernel_source_hash") == extra["kernel_source_hash"]:
+            traffic = t.get("gemm_prefill_bytes_per_launch")
+    if args.suite == "all":
+        extra.update(extra_suites(torch, fgb, workloads, np))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, workloads, np)
+    line = {
+        "metric": "block-FP8 GEMM TFLOPS (% of FP8 MFMA peak); quant/decode GB/s (% HBM)",
+        "value": round(total_flops / (res["ms_step"] * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded: x ~ N(0,1) with 1% x20 outliers, W ~ N(0,0.02), bf16)",
+        "config": {"workload": "llama3_8b_prefill_m4096: act_quant_group128 + w8a8_block_gemm for "
+                               "qkv 6144x4096, o 4096x4096, gate_up 28672x4096, down 4096x14336; "
+                               "fp32 128x128 weight scales, bf16 out",
+                   "M": res["M"], "parallelism": "single_gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -43,9 +43,12 @@ template <int OUT>
 __device__ __forceinline__ void store4(void* y, int64_t ldy, int64_t m, int64_t n, v4f v) {
   if constexpr (OUT == 0) {
     uint16_t* p = reinterpret_cast<uint16_t*>(y) + m * ldy + n;
+    // float32 -> bf16 round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950)
     uint2 w;
-    w.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+    w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
     *reinterpret_cast<uint2*>(p) = w;
   } else {
     float* p = reinterpret_cast<float*>(y) + m * ldy + n;

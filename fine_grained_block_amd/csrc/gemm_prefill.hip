@@ -4,13 +4,19 @@
 // (Transformers "Fine-grained FP8", "DeepGEMM fast path"; grouped: the expert matmuls of the
 // same section and of "UE8M0 scale format").
 //
-// Workgroup: 256 threads (4 waves) computing a BN x BM tile of y^T (BN output features x BM
-// tokens).  Per K-block the W and A tiles (BN x 128 and BM x 128 bytes) are staged through LDS,
-// double-buffered: the global loads for block kb+1 are in flight while block kb is multiplied.
-// LDS rows are 128 bytes; 16-byte chunk c of row r lives at chunk c ^ (r & 7), so the 8 lanes
-// of a ds_read_b128 phase hit 8 different bank groups.
+// Workgroup: 512 threads (8 waves, 2 per SIMD) computing a BN x BM tile of y^T (BN output
+// features x BM tokens).  Per K-block the W and A tiles (BN x 128 and BM x 128 bytes) are
+// copied HBM/L2 -> LDS by the direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging),
+// two stages deep: while block kb is multiplied out of one stage, block kb+1 lands in the other.
+// Each stage is its own __shared__ array so the compiler can tell the in-flight copies from the
+// LDS reads of the current stage and does not wait for them.
 //
-// Each wave owns a (BN/2) x (BM/2) sub-tile = TN x TM MFMA tiles of 16x16.  For every K-block
+// LDS rows are 128 bytes; 16-byte chunk c of row r sits at chunk c ^ (r & 7).  A direct load
+// writes 64 lanes x 16 B contiguously (8 rows), so lane i fetches the global chunk that belongs
+// at its slot: row 8q + i/8, logical chunk (i%8) ^ (i/8).  Fragment reads (8 lanes = 8 rows at
+// one logical chunk) then touch 8 different bank groups.
+//
+// Each wave owns a (BN/WN) x (BM/WM) sub-tile = TN x TM MFMA tiles of 16x16.  For every K-block
 // one MFMA per tile yields the exact-product float32 partial P, and acc += P * (s_a * s_w).
 #include "gemm_common.hpp"
 #include "internal.h"
@@ -19,23 +25,47 @@ namespace fgb {
 
 namespace {
 
-constexpr int THREADS = 256;
 constexpr int KBYTES = 128;  // one K-block of E4M3 codes per row
 
-template <int BN, int BM>
-struct Tile {
-  static constexpr int TN = BN / 2 / 16;  // MFMA tiles per wave along n
-  static constexpr int TM = BM / 2 / 16;  // along m
-  static constexpr int W_LOADS = BN * KBYTES / 16 / THREADS;  // 16 B chunks per thread
-  static constexpr int A_LOADS = BM * KBYTES / 16 / THREADS;
+#define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
+#define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+template <int BN_, int BM_, int WN_, int WM_, int MINB_, int STAGES_>
+struct Cfg {
+  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
+  static constexpr int MINB = MINB_;      // workgroups per CU the register budget is sized for
+  static constexpr int STAGES = STAGES_;  // LDS stages: copies run STAGES-1 K-blocks ahead
+  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+  static constexpr int WAVES = WN * WM;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int TN = BN / WN / 16;  // MFMA tiles per wave along n
+  static constexpr int TM = BM / WM / 16;  // along m
   static constexpr int W_BYTES = BN * KBYTES;
   static constexpr int A_BYTES = BM * KBYTES;
   static constexpr int STAGE = W_BYTES + A_BYTES;
+  static constexpr int W_LD = BN / 8 / WAVES;  // direct loads (8 rows each) per wave per stage
+  static constexpr int A_LD = BM / 8 / WAVES;
+  static constexpr int NDMA = W_LD + A_LD;
+  static_assert(W_LD >= 1 && A_LD >= 1, "every wave loads whole 8-row groups");
+  static_assert((BN / WN) % 128 == 0 || 128 % (BN / WN) == 0, "a wave's rows stay in one weight block");
 };
+
+// s_waitcnt immediate that waits until at most N vector-memory operations are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+constexpr int vmcnt_imm() { return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Workgroup barrier without a memory fence: LDS written by the direct copies is complete once
+// each wave's own vmcnt wait returns, so only the execution barrier is needed.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * KBYTES + ((chunk ^ (row & 7)) << 4); }
 
-// Read one 16 x 128 fragment (lane row = lane%16, bytes 32g .. 32g+31 with g = lane/16).
+// One 16 x 128 fragment: lane row = lane%16, logical bytes 32g .. 32g+31 with g = lane/16.
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row0, int lane) {
   const int r = row0 + (lane & 15);
   const int g = lane >> 4;
@@ -47,16 +77,12 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row0, int lane)
   return v;
 }
 
-struct RowRange {
-  int64_t row0;     // first activation row of this tile
-  int64_t row_end;  // one past the last valid row (expert end or M)
-  int64_t expert;
-};
-
-template <int BN, int BM, int SWF, int OUT, bool GROUPED>
-__global__ __launch_bounds__(THREADS, 2) void gemm_prefill_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-  using T = Tile<BN, BM>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
+template <typename C, int SWF, int OUT, bool GROUPED>
+__global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  // one __shared__ array per stage, so the compiler can tell in-flight copies from reads
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[C::STAGES > 2 ? C::STAGE : 16];
 
   const int nwg = tiles_m * tiles_n;
   const int pid = xcd_remap((int)blockIdx.x, nwg);
@@ -73,152 +99,185 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_prefill_kernel(GemmArgs p, in
   const int KB = (int)(K / KBYTES);
   const int NBLK = (int)(N / 128);
 
-  RowRange rr;
+  int64_t row0, row_end;
   const uint8_t* wq = p.w_q;
   int64_t sw_base = 0;
   if constexpr (GROUPED) {
-    // find the expert owning logical m-tile pid_m
-    int cum = 0;
-    int e = 0;
+    int cum = 0, e = 0;
     int64_t r0 = 0, r1 = 0;
     bool found = false;
     for (; e < p.E; ++e) {
       r0 = p.offsets[e];
       r1 = p.offsets[e + 1];
-      const int mt = (int)((r1 - r0 + BM - 1) / BM);
+      const int mt = (int)((r1 - r0 + C::BM - 1) / C::BM);
       if (pid_m < cum + mt) { found = true; break; }
       cum += mt;
     }
     if (!found) return;  // padding tile beyond the real tile count
-    rr.row0 = r0 + (int64_t)(pid_m - cum) * BM;
-    rr.row_end = r1;
-    rr.expert = e;
+    row0 = r0 + (int64_t)(pid_m - cum) * C::BM;
+    row_end = r1;
     wq += (int64_t)e * N * K;
     sw_base = (int64_t)e * NBLK * KB;
   } else {
-    rr.row0 = (int64_t)pid_m * BM;
-    rr.row_end = p.M;
-    rr.expert = 0;
+    row0 = (int64_t)pid_m * C::BM;
+    row_end = p.M;
   }
-  const int64_t n0 = (int64_t)pid_n * BN;
+  const int64_t n0 = (int64_t)pid_n * C::BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % C::WN, wm = wave / C::WN;
 
-  // global -> register staging addresses
-  const int ld_chunk = tid & 7;
-  const int ld_row = tid >> 3;  // + 32 * i
-  const uint8_t* wsrc[T::W_LOADS];
-  const uint8_t* asrc[T::A_LOADS];
+  // direct-load sources: lane i of 8-row group q fetches row 8q + i/8, chunk (i%8) ^ (i/8)
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  // 32-bit per-lane byte offsets from workgroup-uniform bases (the library checks that every
+  // operand fits in 4 GiB), so the copies use the scalar-base addressing form
+  uint32_t woff[C::W_LD], aoff[C::A_LD];
+  const uint8_t* wbase = wq + n0 * K;
+  const uint8_t* abase = p.a_q;
 #pragma unroll
-  for (int i = 0; i < T::W_LOADS; ++i)
-    wsrc[i] = wq + (n0 + ld_row + 32 * i) * K + ld_chunk * 16;
-#pragma unroll
-  for (int i = 0; i < T::A_LOADS; ++i) {
-    int64_t row = rr.row0 + ld_row + 32 * i;
-    row = row < rr.row_end ? row : rr.row_end - 1;
-    asrc[i] = p.a_q + row * p.lda + ld_chunk * 16;
+  for (int i = 0; i < C::W_LD; ++i) {
+    const int q = wave + i * C::WAVES;
+    woff[i] = (uint32_t)((8 * q + lrow) * K + lchunk * 16);
   }
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) {
+    const int q = wave + i * C::WAVES;
+    int64_t row = row0 + 8 * q + lrow;
+    row = row < row_end ? row : row_end - 1;
+    aoff[i] = (uint32_t)(row * p.lda + lchunk * 16);
+  }
+  auto issue = [&](int kb, uint8_t* st) {
+    const uint8_t* wb = wbase + (int64_t)kb * KBYTES;
+    const uint8_t* ab = abase + (int64_t)kb * KBYTES;
+#pragma unroll
+    for (int i = 0; i < C::W_LD; ++i)
+      __builtin_amdgcn_global_load_lds(GPTR(wb + woff[i]), LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i)
+      __builtin_amdgcn_global_load_lds(GPTR(ab + aoff[i]),
+                                       LPTR(st + C::W_BYTES + (wave + i * C::WAVES) * 8 * KBYTES), 16, 0, 0);
+  };
+
   // per-lane activation scale rows (one token per lane per m-tile)
-  int64_t sa_row[T::TM];
+  uint32_t sa_row[C::TM];
 #pragma unroll
-  for (int j = 0; j < T::TM; ++j) {
-    int64_t row = rr.row0 + wm * (BM / 2) + j * 16 + (lane & 15);
-    sa_row[j] = row < rr.row_end ? row : rr.row_end - 1;
+  for (int j = 0; j < C::TM; ++j) {
+    const int64_t row = row0 + wm * (C::BM / C::WM) + j * 16 + (lane & 15);
+    sa_row[j] = (uint32_t)(row < row_end ? row : row_end - 1);
   }
-  const int64_t nb = (n0 + wn * (BN / 2)) / 128;  // weight block row of this wave (uniform)
+  const int64_t nb = (n0 + wn * (C::BN / C::WN)) / 128;  // this wave's weight block row
+  const float* sa_ptr = p.s_a;
+  const int64_t ld_sa = p.ld_sa;
+  const int64_t sw_row = sw_base + nb * KB;
 
-  int4 wreg[T::W_LOADS], areg[T::A_LOADS];
-  auto gload = [&](int kb) {
+  v4f acc[C::TN][C::TM];
 #pragma unroll
-    for (int i = 0; i < T::W_LOADS; ++i) wreg[i] = *reinterpret_cast<const int4*>(wsrc[i] + (int64_t)kb * KBYTES);
+  for (int i = 0; i < C::TN; ++i)
 #pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) areg[i] = *reinterpret_cast<const int4*>(asrc[i] + (int64_t)kb * KBYTES);
+    for (int j = 0; j < C::TM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // scales: block kb+1's load while block kb is multiplied; each step first folds the landed
+  // pair into per-token products sc[j] = s_a[m_j, kb] * s_w[nb, kb]
+  float sa_nxt[C::TM];
+  float sw_nxt = 0.0f;
+  auto load_scales = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < C::TM; ++j) sa_nxt[j] = (sa_ptr + (int64_t)kb * ld_sa)[sa_row[j]];
+    sw_nxt = load_sw<SWF>(p.s_w, sw_row + kb);
   };
-  auto sstore = [&](int buf) {
-    uint8_t* ws = smem + buf * T::STAGE;
-    uint8_t* as = ws + T::W_BYTES;
-#pragma unroll
-    for (int i = 0; i < T::W_LOADS; ++i) *reinterpret_cast<int4*>(ws + swz(ld_row + 32 * i, ld_chunk)) = wreg[i];
-#pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) *reinterpret_cast<int4*>(as + swz(ld_row + 32 * i, ld_chunk)) = areg[i];
-  };
 
-  v4f acc[T::TN][T::TM];
+  // Software pipeline over the wave's TN weight fragments: the MFMAs of fragment i are issued
+  // before the scale-FMAs of fragment i-1 consume their results, and fragment i+1 is read from
+  // LDS meanwhile, so matrix core, VALU and LDS work overlap instead of waiting on each other.
+  auto compute = [&](const uint8_t* st, const float* sc) {
+    const uint8_t* ws = st + wn * (C::BN / C::WN) * KBYTES;
+    const uint8_t* as = st + C::W_BYTES;
+    v8i bf[C::TM];
 #pragma unroll
-  for (int i = 0; i < T::TN; ++i)
+    for (int j = 0; j < C::TM; ++j) bf[j] = lds_frag(as, wm * (C::BM / C::WM) + j * 16, lane);
+    v8i af[2];
+    v4f P[2][C::TM];
+    af[0] = lds_frag(ws, 0, lane);
 #pragma unroll
-    for (int j = 0; j < T::TM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  float sa_cur[T::TM], sa_nxt[T::TM];
-  float sw_cur, sw_nxt = 0.0f;
-  gload(0);
+    for (int i = 0; i <= C::TN; ++i) {
+      if (i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
+      if (i < C::TN) {
 #pragma unroll
-  for (int j = 0; j < T::TM; ++j) sa_cur[j] = p.s_a[sa_row[j]];
-  sw_cur = load_sw<SWF>(p.s_w, sw_base + nb * KB);
-  sstore(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    const bool more = kb + 1 < KB;
-    if (more) {
-      gload(kb + 1);
+        for (int j = 0; j < C::TM; ++j) P[i & 1][j] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
+      }
+      if (i > 0) {
 #pragma unroll
-      for (int j = 0; j < T::TM; ++j) sa_nxt[j] = p.s_a[(int64_t)(kb + 1) * p.ld_sa + sa_row[j]];
-      sw_nxt = load_sw<SWF>(p.s_w, sw_base + nb * KB + kb + 1);
-    }
-    const uint8_t* ws = smem + buf * T::STAGE;
-    const uint8_t* as = ws + T::W_BYTES;
-    v8i bf[T::TM];
-#pragma unroll
-    for (int j = 0; j < T::TM; ++j) bf[j] = lds_frag(as, wm * (BM / 2) + j * 16, lane);
-    float sc[T::TM];
-#pragma unroll
-    for (int j = 0; j < T::TM; ++j) sc[j] = sa_cur[j] * sw_cur;
-#pragma unroll
-    for (int i = 0; i < T::TN; ++i) {
-      const v8i af = lds_frag(ws, wn * (BN / 2) + i * 16, lane);
-#pragma unroll
-      for (int j = 0; j < T::TM; ++j) {
-        const v4f P = mfma_e4m3_16x16x128(af, bf[j]);
-        acc[i][j] += P * sc[j];
+        for (int j = 0; j < C::TM; ++j) acc[i - 1][j] += P[(i - 1) & 1][j] * sc[j];
       }
     }
-    if (more) {
-      sstore(buf ^ 1);
+  };
+
+  // Block kb lives in stage kb % STAGES.  A step waits for its own block's copies (leaving the
+  // younger copies in flight), synchronizes, starts the scale loads for kb+1 and the copies for
+  // kb+STAGES-1 into the stage consumed one step earlier, and multiplies block kb.  Past the last
+  // block the loads are clamped to it (harmless re-reads into a stage no later step reads), so
+  // every step issues the same loads and one fixed vmcnt wait covers all of them.
+  auto step = [&](int kb, const uint8_t* cur, uint8_t* refill) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<C::STAGES == 3 ? C::NDMA : 0>());
+    wg_barrier();
+    float sc[C::TM];
 #pragma unroll
-      for (int j = 0; j < T::TM; ++j) sa_cur[j] = sa_nxt[j];
-      sw_cur = sw_nxt;
+    for (int j = 0; j < C::TM; ++j) sc[j] = sa_nxt[j] * sw_nxt;
+    load_scales(min(kb + 1, KB - 1));
+    issue(min(kb + C::STAGES - 1, KB - 1), refill);
+    compute(cur, sc);
+  };
+
+  issue(0, stage0);
+  load_scales(0);
+  if (C::STAGES == 3) issue(min(1, KB - 1), stage1);
+  if constexpr (C::STAGES == 2) {
+    for (int kb = 0; kb < KB; kb += 2) {
+      step(kb, stage0, stage1);
+      if (kb + 1 < KB) step(kb + 1, stage1, stage0);
     }
-    __syncthreads();
+  } else {
+    for (int kb = 0; kb < KB; kb += 3) {
+      step(kb, stage0, stage2);
+      if (kb + 1 < KB) step(kb + 1, stage1, stage0);
+      if (kb + 2 < KB) step(kb + 2, stage2, stage1);
+    }
   }
 
-  // epilogue
+  // epilogue: lane holds 4 consecutive output features of one token per MFMA tile
 #pragma unroll
-  for (int j = 0; j < T::TM; ++j) {
-    const int64_t m = rr.row0 + wm * (BM / 2) + j * 16 + (lane & 15);
-    if (m < rr.row_end) {
+  for (int j = 0; j < C::TM; ++j) {
+    const int64_t m = row0 + wm * (C::BM / C::WM) + j * 16 + (lane & 15);
+    if (m < row_end) {
 #pragma unroll
-      for (int i = 0; i < T::TN; ++i) {
-        const int64_t n = n0 + wn * (BN / 2) + i * 16 + 4 * (lane >> 4);
+      for (int i = 0; i < C::TN; ++i) {
+        const int64_t n = n0 + wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4);
         store4<OUT>(p.y, p.ldy, m, n, acc[i][j]);
       }
     }
   }
 }
 
-constexpr int BN_ = 128, BM_ = 128;
+#ifndef FGB_BIG_CFG
+#define FGB_BIG_CFG 256, 128, 2, 4, 1, 3
+#endif
+#ifndef FGB_HALF_CFG
+#define FGB_HALF_CFG 256, 128, 2, 4, 1, 3
+#endif
+using Big = Cfg<FGB_BIG_CFG>;
+using Half = Cfg<FGB_HALF_CFG>;
+using Narrow = Cfg<128, 128, 2, 2, 2, 2>;  // N % 256 != 0: 4 waves, wave tile 64 x 64
 
-template <bool GROUPED>
-hipError_t launch_impl(const GemmArgs& a, int tiles_m, hipStream_t stream) {
-  const int tiles_n = (int)(a.N / BN_);
+template <typename C, bool GROUPED>
+hipError_t launch_cfg(const GemmArgs& a, int tiles_m, hipStream_t stream) {
+  const int tiles_n = (int)(a.N / C::BN);
   const int nwg = tiles_m * tiles_n;
-  dim3 grid(nwg), block(THREADS);
-#define FGB_LAUNCH(SWF, OUT)                                                                   \
-  hipLaunchKernelGGL((gemm_prefill_kernel<BN_, BM_, SWF, OUT, GROUPED>), grid, block, 0, stream, a, \
+  dim3 grid(nwg), block(C::THREADS);
+#define FGB_LAUNCH(SWF, OUT)                                                                  \
+  hipLaunchKernelGGL((gemm_prefill_kernel<C, SWF, OUT, GROUPED>), grid, block, 0, stream, a, \
                      tiles_m, tiles_n)
   if (a.s_w_fmt == 0 && a.y_dtype == 0) FGB_LAUNCH(0, 0);
   else if (a.s_w_fmt == 0) FGB_LAUNCH(0, 1);
@@ -228,17 +287,37 @@ hipError_t launch_impl(const GemmArgs& a, int tiles_m, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Tile choice: 256 x 256 unless its last round of workgroups over the 256 CUs would be mostly
+// empty and the 256 x 128 tile fills the machine better; 128 x 128 when N is not a multiple of 256.
+enum class Pick { Big, Half, Narrow };
+
+template <typename C>
+int64_t tiles_for(int64_t M, int64_t N) { return ((M + C::BM - 1) / C::BM) * (N / C::BN); }
+
+double fill(int64_t tiles) { return (double)tiles / (double)(((tiles + 255) / 256) * 256); }
+
+Pick pick_tile(int64_t M, int64_t N) {
+  if (N % Big::BN != 0 || N % Half::BN != 0) return Pick::Narrow;
+  const double eff_big = fill(tiles_for<Big>(M, N));
+  const double eff_half = fill(tiles_for<Half>(M, N));
+  return eff_half > eff_big * 1.15 ? Pick::Half : Pick::Big;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
-  const int tiles_m = (int)((a.M + BM_ - 1) / BM_);
-  return launch_impl<false>(a, tiles_m, stream);
+  switch (pick_tile(a.M, a.N)) {
+    case Pick::Big: return launch_cfg<Big, false>(a, (int)((a.M + Big::BM - 1) / Big::BM), stream);
+    case Pick::Half: return launch_cfg<Half, false>(a, (int)((a.M + Half::BM - 1) / Half::BM), stream);
+    default: return launch_cfg<Narrow, false>(a, (int)((a.M + Narrow::BM - 1) / Narrow::BM), stream);
+  }
 }
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t stream) {
   // upper bound on the per-expert tile count: sum_e ceil(M_e/BM) <= ceil(total_M/BM) + E
-  const int tiles_m = (int)((a.M + BM_ - 1) / BM_) + a.E;
-  return launch_impl<true>(a, tiles_m, stream);
+  if (a.N % Half::BN == 0)
+    return launch_cfg<Half, true>(a, (int)((a.M + Half::BM - 1) / Half::BM) + a.E, stream);
+  return launch_cfg<Narrow, true>(a, (int)((a.M + Narrow::BM - 1) / Narrow::BM) + a.E, stream);
 }
 
 }  // namespace fgb
