@@ -22,7 +22,11 @@ constexpr int ROWS_PER_WG = 64;
 constexpr int CH = 8;                 // K-blocks of W in flight per wave
 constexpr int LDS_LIMIT = 64 * 1024;  // activation slice budget
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of LDS row r sits at c ^ ((r & 7) ^ (r>>3 & 1)): conflict-free 16-row fragment
+// reads on gfx950's 64-bank LDS.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
+}
 
 template <int MT, int SWF, int OUT>
 __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kpw, int S, float* ws) {

@@ -11,10 +11,13 @@
 // Each stage is its own __shared__ array so the compiler can tell the in-flight copies from the
 // LDS reads of the current stage and does not wait for them.
 //
-// LDS rows are 128 bytes; 16-byte chunk c of row r sits at chunk c ^ (r & 7).  A direct load
-// writes 64 lanes x 16 B contiguously (8 rows), so lane i fetches the global chunk that belongs
-// at its slot: row 8q + i/8, logical chunk (i%8) ^ (i/8).  Fragment reads (8 lanes = 8 rows at
-// one logical chunk) then touch 8 different bank groups.
+// LDS rows are 128 bytes; 16-byte chunk c of row r sits at chunk c ^ g(r), g(r) = (r & 7) ^ (r>>3 & 1).
+// gfx950 serves a ds_read_b128 16 lanes per cycle from 64 banks, i.e. two 128-byte rows per bank
+// line: the 16 rows of a fragment read at one logical chunk land on 16 distinct (row parity,
+// chunk) pairs, so the read is conflict-free (and so is any 8-row subset).  g depends on r mod 16
+// only, so every fragment (16 rows from a multiple of 16) uses the same per-lane address offsets.
+// A direct load writes 64 lanes x 16 B contiguously (8 rows), so lane i of 8-row group q fetches
+// the global chunk that belongs at its slot: row 8q + i/8, logical chunk (i%8) ^ g(8q + i/8).
 //
 // Each wave owns a (BN/WN) x (BM/WM) sub-tile = TN x TM MFMA tiles of 16x16.  For every K-block
 // one MFMA per tile yields the exact-product float32 partial P, and acc += P * (s_a * s_w).
@@ -63,7 +66,8 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * KBYTES + ((chunk ^ (row & 7)) << 4); }
+__host__ __device__ constexpr int swz_g(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * KBYTES + ((chunk ^ swz_g(row)) << 4); }
 
 // One 16 x 128 fragment: lane row = lane%16, logical bytes 32g .. 32g+31 with g = lane/16.
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row0, int lane) {
@@ -129,9 +133,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   const int wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
 
-  // direct-load sources: lane i of 8-row group q fetches row 8q + i/8, chunk (i%8) ^ (i/8)
+  // direct-load sources: lane i of 8-row group q fetches row 8q + i/8, chunk (i%8) ^ g(row)
   const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
   // 32-bit per-lane byte offsets from workgroup-uniform bases (the library checks that every
   // operand fits in 4 GiB), so the copies use the scalar-base addressing form
   uint32_t woff[C::W_LD], aoff[C::A_LD];
@@ -140,14 +143,16 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 #pragma unroll
   for (int i = 0; i < C::W_LD; ++i) {
     const int q = wave + i * C::WAVES;
-    woff[i] = (uint32_t)((8 * q + lrow) * K + lchunk * 16);
+    const int r = 8 * q + lrow;
+    woff[i] = (uint32_t)(r * K + (((lane & 7) ^ swz_g(r)) * 16));
   }
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i) {
     const int q = wave + i * C::WAVES;
-    int64_t row = row0 + 8 * q + lrow;
+    const int r = 8 * q + lrow;
+    int64_t row = row0 + r;
     row = row < row_end ? row : row_end - 1;
-    aoff[i] = (uint32_t)(row * p.lda + lchunk * 16);
+    aoff[i] = (uint32_t)(row * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
   }
   auto issue = [&](int kb, uint8_t* st) {
     const uint8_t* wb = wbase + (int64_t)kb * KBYTES;
