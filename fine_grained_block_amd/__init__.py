@@ -34,4 +34,5 @@ from .ops import (  # noqa: F401
     fp8_encode,
     fp8_decode,
     linear,
+    selftest_quotients,
 )

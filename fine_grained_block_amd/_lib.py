@@ -27,6 +27,7 @@ _SIGS = {
                                                    _c_i64, _vp, ctypes.c_size_t, _vp]),
     "fgb_fp8_encode": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp]),
     "fgb_fp8_decode": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp]),
+    "fgb_selftest_quotients": (ctypes.c_int, [_vp, _vp]),
 }
 EXPORTS = tuple(_SIGS)
 

@@ -12,6 +12,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid and index arithmetic bound
+constexpr int64_t kMax32 = (int64_t)1 << 32;   // bytes addressable by a 32-bit offset
 constexpr int kMaxDevices = 64;
 
 // 0 = unknown, 1 = gfx950, -1 = other
@@ -53,6 +54,10 @@ int validate_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_
   if (!aligned16(a_q) || !aligned16(s_a) || !aligned16(w_q) || !aligned16(s_w) || !aligned16(y))
     return FGB_ERR_ALIGN;
   if (lda % 16 || (ldy * ybytes) % 16 || (ld_sa * 4) % 16) return FGB_ERR_ALIGN;
+  // the kernels address A, one expert's W and the scales with 32-bit offsets, and hold a weight
+  // row's K/128 block scales in registers (K <= 32768)
+  if (M * lda >= kMax32 || N * K >= kMax32 || (K / FGB_BLOCK) * ld_sa * 4 >= kMax32) return FGB_ERR_SHAPE;
+  if (K > 32768) return FGB_ERR_SHAPE;
   return FGB_OK;
 }
 
@@ -174,6 +179,14 @@ int fgb_fp8_decode(const uint8_t* in, float* out, int64_t n, int fmt, void* stre
   int st = check_device();
   if (st != FGB_OK) return st;
   return launch_status(fgb::launch_decode(in, out, n, fmt, (hipStream_t)stream));
+}
+
+int fgb_selftest_quotients(unsigned long long* counts, void* stream) {
+  if (!counts) return FGB_ERR_NULL;
+  if (((uintptr_t)counts & 7u)) return FGB_ERR_ALIGN;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_selftest_quotients(counts, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -13,6 +13,7 @@ hipError_t launch_weight_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t*
 hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int fmt, int saturate,
                          hipStream_t stream);
 hipError_t launch_decode(const uint8_t* in, float* out, int64_t n, int fmt, hipStream_t stream);
+hipError_t launch_selftest_quotients(unsigned long long* counts, hipStream_t stream);
 
 // Block-scaled GEMM problem description (dense or grouped).
 struct GemmArgs {

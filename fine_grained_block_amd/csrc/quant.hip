@@ -19,17 +19,54 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-// Quantize 8 values (4 bf16 pairs) with scale divisor d (d == 1 for an all-zero group, where
-// every x is +-0 and the code keeps the sign).  Returns 8 E4M3 codes in two dwords.
-__device__ __forceinline__ uint2 quant8(const uint4 v, float d) {
-  float f0 = bf16_lo(v.x) / d, f1 = bf16_hi(v.x) / d;
-  float f2 = bf16_lo(v.y) / d, f3 = bf16_hi(v.y) / d;
-  float f4 = bf16_lo(v.z) / d, f5 = bf16_hi(v.z) / d;
-  float f6 = bf16_lo(v.w) / d, f7 = bf16_hi(v.w) / d;
-  uint32_t lo = cvt_pk_e4m3<false>(f0, f1, 0u);
-  lo = cvt_pk_e4m3<true>(f2, f3, lo);
-  uint32_t hi = cvt_pk_e4m3<false>(f4, f5, 0u);
-  hi = cvt_pk_e4m3<true>(f6, f7, hi);
+// Group divisor: the stored scale s, or 1 for an all-zero group (every x is +-0 there and the
+// code keeps the sign).  `r` is the correctly rounded reciprocal 1/d, `fast` says whether d is in
+// the range where the reciprocal-and-correct quotient below equals the IEEE quotient x/d.
+struct Divisor {
+  float d, r;
+  bool fast;
+};
+
+__device__ __forceinline__ Divisor make_divisor(float s) {
+  Divisor v;
+  v.d = (s == 0.0f) ? 1.0f : s;
+  v.r = 1.0f / v.d;  // IEEE division, correctly rounded
+  // 2^-100 <= d <= 2^100: reciprocal, products and residuals stay clear of under/overflow
+  const uint32_t e = (__float_as_uint(v.d) >> 23) & 0xFFu;
+  v.fast = e >= 27u && e <= 227u;
+  return v;
+}
+
+// fl32(x / d) without a division per element (Markstein, 1990; Muller et al., Handbook of
+// Floating-Point Arithmetic): with r = RN(1/d) and q0 = RN(x r), the residual x - q0 d is exact in
+// one FMA and RN(q0 + residual * r) is the correctly rounded quotient.  Outside the fast range
+// the IEEE division is used.  The equality with x / d over every bf16 (x, amax) pair is checked
+// exhaustively on the device by fgb_selftest_quotients.
+__device__ __forceinline__ float quot_fast(float x, const Divisor& v) {
+  const float q0 = x * v.r;
+  const float e = __builtin_fmaf(-q0, v.d, x);
+  // d > 0, so the quotient has x's sign; the correction step would turn x = -0 into +0
+  return __builtin_copysignf(__builtin_fmaf(e, v.r, q0), x);
+}
+
+__device__ __forceinline__ float quot(float x, const Divisor& v) { return v.fast ? quot_fast(x, v) : x / v.d; }
+
+// Quantize 8 values (4 bf16 pairs) by divisor v.  Returns 8 E4M3 codes in two dwords.  All
+// lanes of the wave must be active (the fast/slow choice is made for the whole wave).
+__device__ __forceinline__ uint2 quant8(const uint4 w, const Divisor& v) {
+  float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+  if (__all(v.fast)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = quot_fast(f[i], v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = quot(f[i], v);
+  }
+  uint32_t lo = cvt_pk_e4m3<false>(f[0], f[1], 0u);
+  lo = cvt_pk_e4m3<true>(f[2], f[3], lo);
+  uint32_t hi = cvt_pk_e4m3<false>(f[4], f[5], 0u);
+  hi = cvt_pk_e4m3<true>(f[6], f[7], hi);
   return make_uint2(lo, hi);
 }
 
@@ -42,51 +79,50 @@ __device__ __forceinline__ float absmax8(const uint4 v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// act_quant: 16 lanes per group (16 B = 8 bf16 each); a 256-thread block covers 16 groups per
-// step and AQ_UNROLL steps, with all loads issued before any arithmetic.  Groups are numbered
-// row-major (m, g), so a wave reads 4 consecutive groups = 1 KiB contiguous of one row.
+// act_quant: one wave per token row at a time (grid-stride over rows), 16 lanes per group (16 B =
+// 8 bf16 each), so a wave covers 4 consecutive groups = 1 KiB of the row per load and issues
+// AQ_UNROLL loads (16 groups) before any arithmetic.  No index division: rows and groups are
+// loop counters.
 // ---------------------------------------------------------------------------------------------
 constexpr int AQ_THREADS = 256;
+constexpr int AQ_WAVES = AQ_THREADS / 64;
 constexpr int AQ_UNROLL = 4;
-constexpr int AQ_GROUPS_PER_BLOCK = (AQ_THREADS / 16) * AQ_UNROLL;
 
 __global__ __launch_bounds__(AQ_THREADS) void act_quant_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t G, int64_t ldx,
+    const uint16_t* __restrict__ x, int64_t M, int G, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s_a, int64_t ld_sa) {
-  const int sub = threadIdx.x & 15;
-  const int64_t total = M * G;
-  const int64_t gbase = (int64_t)blockIdx.x * AQ_GROUPS_PER_BLOCK + (threadIdx.x >> 4);
-  uint4 v[AQ_UNROLL];
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 15, grp = lane >> 4;
+  for (int64_t m = (int64_t)blockIdx.x * AQ_WAVES + (threadIdx.x >> 6); m < M; m += (int64_t)gridDim.x * AQ_WAVES) {
+    const uint16_t* xr = x + m * ldx + sub * 8;
+    uint8_t* qr = q + m * ldq + sub * 8;
+    for (int g0 = 0; g0 < G; g0 += 4 * AQ_UNROLL) {
+      uint4 v[AQ_UNROLL];
 #pragma unroll
-  for (int u = 0; u < AQ_UNROLL; ++u) {
-    int64_t gi = gbase + u * (AQ_THREADS / 16);
-    if (gi < total) {
-      int64_t m = gi / G, g = gi - m * G;
-      v[u] = *reinterpret_cast<const uint4*>(x + m * ldx + g * kBlock + sub * 8);
-    } else {
-      v[u] = make_uint4(0, 0, 0, 0);
-    }
-  }
+      for (int u = 0; u < AQ_UNROLL; ++u) {
+        const int g = g0 + 4 * u + grp;
+        v[u] = g < G ? *reinterpret_cast<const uint4*>(xr + g * kBlock) : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-  for (int u = 0; u < AQ_UNROLL; ++u) {
-    int64_t gi = gbase + u * (AQ_THREADS / 16);
-    float amax = row16_max(absmax8(v[u]));
-    float s = amax / kE4M3Max;          // IEEE float32 division (correctly rounded)
-    float d = (s == 0.0f) ? 1.0f : s;
-    uint2 c = quant8(v[u], d);
-    if (gi < total) {
-      int64_t m = gi / G, g = gi - m * G;
-      *reinterpret_cast<uint2*>(q + m * ldq + g * kBlock + sub * 8) = c;
-      if (sub == 0) s_a[g * ld_sa + m] = s;
+      for (int u = 0; u < AQ_UNROLL; ++u) {
+        const int g = g0 + 4 * u + grp;
+        const float amax = row16_max(absmax8(v[u]));
+        const float s = amax / kE4M3Max;  // IEEE float32 division (correctly rounded)
+        const uint2 c = quant8(v[u], make_divisor(s));
+        if (g < G) {
+          *reinterpret_cast<uint2*>(qr + g * kBlock) = c;
+          if (sub == 0) s_a[g * ld_sa + m] = s;
+        }
+      }
     }
   }
 }
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, float* s_a, int64_t ld_sa, hipStream_t stream) {
-  const int64_t G = K / kBlock;
-  const int64_t total = M * G;
-  const int64_t blocks = (total + AQ_GROUPS_PER_BLOCK - 1) / AQ_GROUPS_PER_BLOCK;
+  const int G = (int)(K / kBlock);
+  int64_t blocks = (M + AQ_WAVES - 1) / AQ_WAVES;
+  if (blocks > 256 * 16) blocks = 256 * 16;  // grid-stride beyond 16 workgroups per CU
   hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(AQ_THREADS), 0, stream,
                      x, M, G, ldx, q, ldq, s_a, ld_sa);
   return hipGetLastError();
@@ -128,11 +164,11 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
     s = dec_ue8m0(code);
     if (t == 0) reinterpret_cast<uint8_t*>(s_w)[blockIdx.x] = (uint8_t)code;
   }
-  float d = (s == 0.0f) ? 1.0f : s;
+  const Divisor dv = make_divisor(s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int64_t row = nb * kBlock + r0 + 16 * i;
-    *reinterpret_cast<uint2*>(wq + row * K + kb * kBlock + chunk * 8) = quant8(v[i], d);
+    *reinterpret_cast<uint2*>(wq + row * K + kb * kBlock + chunk * 8) = quant8(v[i], dv);
   }
 }
 
@@ -202,6 +238,40 @@ hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int fmt, int 
 
 hipError_t launch_decode(const uint8_t* in, float* out, int64_t n, int fmt, hipStream_t stream) {
   hipLaunchKernelGGL(decode_kernel, dim3(ew_blocks(n)), dim3(256), 0, stream, in, out, n, fmt);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Self-test of the quotient used by the quantizers: for every positive finite bf16 amax and every
+// bf16 x with |x| <= amax (both signs), the scale s = fl32(amax/448) and the fast quotient must
+// give the same E4M3 code as the IEEE quotient x / s; counts[0] = code mismatches, counts[1] =
+// quotients differing in any bit.  One thread per (amax, x) pair of magnitudes.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void selftest_quotients_kernel(unsigned long long* counts) {
+  const uint32_t a_bits = blockIdx.y + 1u;          // 0x0001 .. 0x7F7F
+  const uint32_t x_bits = blockIdx.x * 256u + threadIdx.x;  // 0x0000 .. 0x7FFF
+  unsigned long long code_bad = 0, quot_bad = 0;
+  if (x_bits <= a_bits) {
+    const float amax = __uint_as_float(a_bits << 16);
+    const float s = amax / kE4M3Max;
+    const Divisor v = make_divisor(s);
+#pragma unroll
+    for (int sign = 0; sign < 2; ++sign) {
+      const float xv = __uint_as_float((x_bits << 16) | (sign ? 0x80000000u : 0u));
+      const float fq = quot(xv, v);
+      const float iq = xv / v.d;
+      quot_bad += __float_as_uint(fq) != __float_as_uint(iq);
+      const uint32_t cf = cvt_pk_e4m3<false>(fq, 0.0f, 0u) & 0xFFu;
+      const uint32_t ci = enc_e4m3_sat_int(iq);
+      code_bad += cf != ci;
+    }
+  }
+  if (code_bad) atomicAdd(&counts[0], code_bad);
+  if (quot_bad) atomicAdd(&counts[1], quot_bad);
+}
+
+hipError_t launch_selftest_quotients(unsigned long long* counts, hipStream_t stream) {
+  hipLaunchKernelGGL(selftest_quotients_kernel, dim3(0x8000 / 256, 0x7F7F), dim3(256), 0, stream, counts);
   return hipGetLastError();
 }
 

@@ -150,3 +150,14 @@ def fp8_decode(c: torch.Tensor, fmt: int = FP8_E4M3) -> torch.Tensor:
     out = torch.empty(c.shape, dtype=torch.float32, device=c.device)
     check("fgb_fp8_decode", lib().fgb_fp8_decode(_ptr(c), _ptr(out), c.numel(), fmt, _stream()))
     return out
+
+
+def selftest_quotients() -> tuple[int, int]:
+    """Exhaustive device check of the quantizers' fast quotient (see include/fgb.h).
+
+    Returns (pairs with differing E4M3 codes, pairs with differing float32 quotients).
+    """
+    counts = torch.zeros(2, dtype=torch.int64, device=torch.device("cuda", torch.cuda.current_device()))
+    check("fgb_selftest_quotients", lib().fgb_selftest_quotients(_ptr(counts), _stream()))
+    c = counts.cpu().tolist()
+    return int(c[0]), int(c[1])

@@ -105,6 +105,7 @@ size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   w_q   E4M3 [N, K] row-major (the Linear layout; y = A . W^T), dense;
  *   s_w   [N/128, K/128] row-major, float32 or UE8M0 bytes per s_w_fmt;
  *   y     [M, ldy] row-major, bf16 bit patterns or float32 per y_dtype.
+ * Size limits (FGB_ERR_SHAPE otherwise): K <= 32768; M*lda, N*K and (K/128)*ld_sa*4 below 2^32.
  * M <= 64 selects the split-K streaming path; it needs `workspace` of
  * fgb_gemm_workspace_bytes(M, N, K) bytes (float32 partial sums; contents on entry ignored).
  */
@@ -128,7 +129,8 @@ size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, i
  *                   (a precondition: checking it would need a device synchronization);
  *   total_M         host copy of offsets[E];
  *   y [total_M, ldy].
- * Experts with no rows are legal and write nothing.
+ * Experts with no rows are legal and write nothing.  Size limits as for fgb_w8a8_block_gemm
+ * (per expert for W).
  */
 int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
                                 const uint8_t* w_q, const void* s_w, int s_w_fmt,
@@ -146,6 +148,17 @@ int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
  */
 int fgb_fp8_encode(const float* in, uint8_t* out, int64_t n, int fmt, int saturate, void* stream);
 int fgb_fp8_decode(const uint8_t* in, float* out, int64_t n, int fmt, void* stream);
+
+/*
+ * Self-test of the quantizers' division.  The codes are defined with the IEEE float32 quotient
+ * x / s; the kernels form it as a correctly rounded reciprocal of s plus one FMA correction per
+ * element.  This call checks, for every positive finite bf16 amax and every bf16 x with
+ * |x| <= amax (both signs; about 1.07e9 pairs), s = fl32(amax/448) and both quotients, and
+ * ADDS to the device counters: counts[0] += pairs whose E4M3 codes differ, counts[1] += pairs
+ * whose float32 quotients differ in any bit.  counts: device, 2 x uint64, 8-byte aligned; the
+ * caller zeroes them.
+ */
+int fgb_selftest_quotients(unsigned long long* counts, void* stream);
 
 #ifdef __cplusplus
 }

@@ -113,3 +113,11 @@ def test_weight_quant(dev, fmt):
     else:
         assert np.array_equal(s_np.view(np.uint32), se.view(np.uint32))
     assert np.array_equal(q.cpu().numpy(), qe)
+
+
+def test_fast_quotient_selftest(dev):
+    """The quantizers' reciprocal-and-correct quotient gives the IEEE quotient's E4M3 code for
+    every positive finite bf16 amax and every bf16 |x| <= amax, both signs (~1.07e9 pairs)."""
+    code_bad, quot_bad = fgb.selftest_quotients()
+    assert code_bad == 0
+    print(f"float32 quotient mismatches (codes equal): {quot_bad}")
