@@ -3,11 +3,14 @@
 // Same result as the prefill path (Transformers "Fine-grained FP8", "DeepGEMM fast path"), but
 // for few tokens the weight stream dominates (bytes per weight: 1 for FP8, per the Baseten
 // NVFP4 summary, "Less memory, more compute"), so the kernel is organised to keep HBM busy:
-//   * a workgroup = 4 waves covers 64 weight rows (one 16-row MFMA tile per wave) and a slice
-//     of whole K-blocks; the grid is (N/64) x S slices, S chosen so ~2k waves stream W;
-//   * the activation slice [Mpad x slice] is staged once in LDS and shared by the 4 waves;
-//   * each wave streams its W rows straight into registers in the MFMA operand layout
-//     (32 contiguous bytes per lane), up to 8 K-blocks in flight;
+//   * a workgroup = 8 waves covers one 128-row weight block (16 rows per wave, one MFMA tile)
+//     and a slice of whole K-blocks; the grid is (N/128) x S slices, S chosen so ~4k waves
+//     (M <= 16) or ~2k waves stream W;
+//   * each wave streams its W rows straight into registers in the MFMA operand layout (32
+//     contiguous bytes per lane), two chunks of CH K-blocks in flight; the first chunk is
+//     requested before anything else;
+//   * the activation slice [Mpad x slice], its scales and the block's weight scales are staged
+//     once in LDS and shared by the 8 waves;
 //   * S > 1 writes float32 partials to the workspace [S][M][N]; a second kernel adds them in
 //     slice order (deterministic) and rounds to the output type.
 #include "gemm_common.hpp"
@@ -17,10 +20,11 @@ namespace fgb {
 
 namespace {
 
-constexpr int THREADS = 256;
-constexpr int ROWS_PER_WG = 64;
-constexpr int CH = 8;                 // K-blocks of W in flight per wave
-constexpr int LDS_LIMIT = 64 * 1024;  // activation slice budget
+constexpr int THREADS = 512;
+constexpr int WAVES = THREADS / 64;
+constexpr int ROWS_PER_WG = 16 * WAVES;  // one 128-row weight block
+constexpr int CH = 4;                    // K-blocks per register chunk (two chunks in flight)
+constexpr int LDS_LIMIT = 64 * 1024;     // activation slice + scales budget
 
 // 16-byte chunk c of LDS row r sits at c ^ ((r & 7) ^ (r>>3 & 1)): conflict-free 16-row fragment
 // reads on gfx950's 64-bank LDS.
@@ -28,41 +32,55 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
 }
 
+__host__ __device__ constexpr int lds_bytes_per_kb(int mt) { return 16 * mt * 128 + 16 * mt * 4 + 4; }
+
 template <int MT, int SWF, int OUT>
 __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kpw, int S, float* ws) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];  // [kpw][16*MT rows][128 B]
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int MROWS = 16 * MT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t K = p.K, N = p.N, M = p.M;
   const int KB = (int)(K / 128);
-  const int nt = blockIdx.x / S, split = blockIdx.x - (blockIdx.x / S) * S;
+  const int nt = blockIdx.x / S, split = blockIdx.x - nt * S;
   const int kb0 = split * kpw;
-  const int kb1 = min(KB, kb0 + kpw);
-  const int nk = kb1 - kb0;
+  const int nk = min(KB, kb0 + kpw) - kb0;
   const int64_t n0 = (int64_t)nt * ROWS_PER_WG + wave * 16;  // this wave's 16 weight rows
-  const int64_t nb = n0 / 128;
-  constexpr int MROWS = 16 * MT;
-
-  // stage activations [MROWS x nk*128] into LDS (rows >= M replicate row M-1; discarded later)
-  {
-    const int chunks = MROWS * nk * 8;
-    for (int c = tid; c < chunks; c += THREADS) {
-      const int ch = c & 7;
-      const int row = (c >> 3) % MROWS;
-      const int kk = (c >> 3) / MROWS;
-      const int64_t m = row < M ? row : M - 1;
-      const int4 v = *reinterpret_cast<const int4*>(p.a_q + m * p.lda + (int64_t)(kb0 + kk) * 128 + ch * 16);
-      *reinterpret_cast<int4*>(a_lds + kk * MROWS * 128 + swz(row, ch)) = v;
-    }
-  }
+  const int64_t nb = (int64_t)nt;                             // weight block row (128 rows)
+  uint8_t* a_lds = lds;                                                    // [kpw][MROWS][128]
+  float* sa_lds = reinterpret_cast<float*>(lds + kpw * MROWS * 128);       // [kpw][MROWS]
+  float* sw_lds = sa_lds + kpw * MROWS;                                    // [kpw]
 
   const int g = lane >> 4;
-  const uint8_t* wrow = p.w_q + (n0 + (lane & 15)) * K + 32 * g;
-  int64_t m_lane[MT];
+  const uint8_t* wrow = p.w_q + (n0 + (lane & 15)) * K + (int64_t)kb0 * 128 + 32 * g;
+  int4 wb[2][CH][2];
+  auto load_chunk = [&](int c, int buf) {
 #pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int64_t m = j * 16 + (lane & 15);
-    m_lane[j] = m < M ? m : M - 1;
+    for (int u = 0; u < CH; ++u) {
+      if (c + u < nk) {
+        const uint8_t* src = wrow + (int64_t)(c + u) * 128;
+        wb[buf][u][0] = *reinterpret_cast<const int4*>(src);
+        wb[buf][u][1] = *reinterpret_cast<const int4*>(src + 16);
+      }
+    }
+  };
+  load_chunk(0, 0);  // the weight stream starts first
+
+  // stage activations [MROWS x nk*128] (rows >= M replicate row M-1; their results are dropped),
+  // their scales, and the weight block's scales for the slice
+  for (int c = tid; c < MROWS * nk * 8; c += THREADS) {
+    const int ch = c & 7;
+    const int row = (c >> 3) % MROWS;
+    const int kk = (c >> 3) / MROWS;
+    const int64_t m = row < M ? row : M - 1;
+    const int4 v = *reinterpret_cast<const int4*>(p.a_q + m * p.lda + (int64_t)(kb0 + kk) * 128 + ch * 16);
+    *reinterpret_cast<int4*>(a_lds + kk * MROWS * 128 + swz(row, ch)) = v;
   }
+  for (int c = tid; c < MROWS * nk; c += THREADS) {
+    const int row = c % MROWS, kk = c / MROWS;
+    const int64_t m = row < M ? row : M - 1;
+    sa_lds[c] = p.s_a[(int64_t)(kb0 + kk) * p.ld_sa + m];
+  }
+  for (int c = tid; c < nk; c += THREADS) sw_lds[c] = load_sw<SWF>(p.s_w, nb * KB + kb0 + c);
 
   v4f acc[MT];
 #pragma unroll
@@ -70,25 +88,16 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kp
 
   __syncthreads();
 
-  for (int c0 = 0; c0 < nk; c0 += CH) {
-    int4 wlo[CH], whi[CH];
+  auto compute_chunk = [&](int c, int buf) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      if (c0 + u < nk) {
-        const uint8_t* src = wrow + (int64_t)(kb0 + c0 + u) * 128;
-        wlo[u] = *reinterpret_cast<const int4*>(src);
-        whi[u] = *reinterpret_cast<const int4*>(src + 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      if (c0 + u < nk) {
-        const int kb = kb0 + c0 + u;
-        const float sw = load_sw<SWF>(p.s_w, nb * KB + kb);
+      const int kk = c + u;
+      if (kk < nk) {
+        const float sw = sw_lds[kk];
         v8i af;
-        af[0] = wlo[u].x; af[1] = wlo[u].y; af[2] = wlo[u].z; af[3] = wlo[u].w;
-        af[4] = whi[u].x; af[5] = whi[u].y; af[6] = whi[u].z; af[7] = whi[u].w;
-        const uint8_t* ab = a_lds + (c0 + u) * MROWS * 128;
+        af[0] = wb[buf][u][0].x; af[1] = wb[buf][u][0].y; af[2] = wb[buf][u][0].z; af[3] = wb[buf][u][0].w;
+        af[4] = wb[buf][u][1].x; af[5] = wb[buf][u][1].y; af[6] = wb[buf][u][1].z; af[7] = wb[buf][u][1].w;
+        const uint8_t* ab = a_lds + kk * MROWS * 128;
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
           const int r = j * 16 + (lane & 15);
@@ -97,11 +106,20 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kp
           v8i bf;
           bf[0] = lo.x; bf[1] = lo.y; bf[2] = lo.z; bf[3] = lo.w;
           bf[4] = hi.x; bf[5] = hi.y; bf[6] = hi.z; bf[7] = hi.w;
-          const float sc = p.s_a[(int64_t)kb * p.ld_sa + m_lane[j]] * sw;
+          const float sc = sa_lds[kk * MROWS + r] * sw;
           const v4f P = mfma_e4m3_16x16x128(af, bf);
           acc[j] += P * sc;
         }
       }
+    }
+  };
+
+  for (int c = 0; c < nk; c += 2 * CH) {
+    if (c + CH < nk) load_chunk(c + CH, 1);
+    compute_chunk(c, 0);
+    if (c + CH < nk) {
+      if (c + 2 * CH < nk) load_chunk(c + 2 * CH, 0);
+      compute_chunk(c + CH, 1);
     }
   }
 
@@ -120,6 +138,8 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kp
   }
 }
 
+// Sum of the S partial slices in slice order; all loads of a group of 8 slices are issued
+// before they are added.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int S, int64_t M,
                                                             int64_t N, void* y, int64_t ldy) {
@@ -127,10 +147,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t total = M * (N / 4);
   if (q >= total) return;
   const int64_t m = q / (N / 4), n = (q - m * (N / 4)) * 4;
-  float4 s = *reinterpret_cast<const float4*>(ws + m * N + n);
-  for (int i = 1; i < S; ++i) {
-    const float4 v = *reinterpret_cast<const float4*>(ws + ((int64_t)i * M + m) * N + n);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  const float* base = ws + m * N + n;
+  const int64_t slice = M * N;
+  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int i0 = 0; i0 < S; i0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = i0 + u < S ? *reinterpret_cast<const float4*>(base + (int64_t)(i0 + u) * slice) : make_float4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u < S) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+    }
   }
   store4<OUT>(y, ldy, m, n, v4f{s.x, s.y, s.z, s.w});
 }
@@ -140,10 +168,11 @@ int mtiles(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 int kb_per_wg(int64_t M, int64_t N, int64_t K) {
   const int KB = (int)(K / 128);
   const int64_t waves_per_split = N / 16;
-  int S = (int)((2048 + waves_per_split - 1) / waves_per_split);
+  const int64_t target = M <= 16 ? 4096 : 2048;
+  int S = (int)((target + waves_per_split - 1) / waves_per_split);
   S = S < 1 ? 1 : (S > KB ? KB : S);
   int kpw = (KB + S - 1) / S;
-  const int lds_cap = LDS_LIMIT / (16 * mtiles(M) * 128);
+  const int lds_cap = LDS_LIMIT / lds_bytes_per_kb(mtiles(M));
   if (kpw > lds_cap) kpw = lds_cap;
   return kpw;
 }
@@ -165,22 +194,21 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
   const int kpw = kb_per_wg(a.M, a.N, a.K);
   const int S = decode_splits(a.M, a.N, a.K);
   const int MT = mtiles(a.M);
-  const size_t lds = (size_t)16 * MT * kpw * 128;
+  const size_t lds = (size_t)lds_bytes_per_kb(MT) * kpw;
   const dim3 grid((unsigned)((a.N / ROWS_PER_WG) * S)), block(THREADS);
   float* ws = reinterpret_cast<float*>(workspace);
 #define FGB_DEC(MT_, SWF, OUT) \
   hipLaunchKernelGGL((gemm_decode_kernel<MT_, SWF, OUT>), grid, block, lds, stream, a, kpw, S, ws)
-#define FGB_DEC_MT(SWF, OUT)        \
-  do {                              \
-    if (MT == 1) FGB_DEC(1, SWF, OUT); \
-    else if (MT == 2) FGB_DEC(2, SWF, OUT); \
-    else FGB_DEC(4, SWF, OUT);      \
+#define FGB_DEC_MT(SWF, OUT)                 \
+  do {                                       \
+    if (MT == 1) FGB_DEC(1, SWF, OUT);       \
+    else if (MT == 2) FGB_DEC(2, SWF, OUT);  \
+    else FGB_DEC(4, SWF, OUT);               \
   } while (0)
-  const int out_direct = a.y_dtype;  // S == 1 writes y directly
   if (a.s_w_fmt == 0) {
-    if (out_direct == 0) FGB_DEC_MT(0, 0); else FGB_DEC_MT(0, 1);
+    if (a.y_dtype == 0) FGB_DEC_MT(0, 0); else FGB_DEC_MT(0, 1);
   } else {
-    if (out_direct == 0) FGB_DEC_MT(1, 0); else FGB_DEC_MT(1, 1);
+    if (a.y_dtype == 0) FGB_DEC_MT(1, 0); else FGB_DEC_MT(1, 1);
   }
 #undef FGB_DEC_MT
 #undef FGB_DEC

@@ -187,11 +187,28 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // scales: block kb+1's load while block kb is multiplied; each step first folds the landed
   // pair into per-token products sc[j] = s_a[m_j, kb] * s_w[nb, kb]
   float sa_nxt[C::TM];
+  // UE8M0 weight-block scales s_w[nb, 0 .. KB-1] are decoded once into registers spread over the
+  // lanes (lane l holds block l + 64 t, K <= 32768) and broadcast with v_readlane.
+  float sw0 = 0.0f, sw1 = 0.0f, sw2 = 0.0f, sw3 = 0.0f;
+  if constexpr (SWF == 1) {
+    sw0 = lane < KB ? load_sw<SWF>(p.s_w, sw_row + lane) : 0.0f;
+    sw1 = lane + 64 < KB ? load_sw<SWF>(p.s_w, sw_row + lane + 64) : 0.0f;
+    sw2 = lane + 128 < KB ? load_sw<SWF>(p.s_w, sw_row + lane + 128) : 0.0f;
+    sw3 = lane + 192 < KB ? load_sw<SWF>(p.s_w, sw_row + lane + 192) : 0.0f;
+  }
+  auto sw_at = [&](int kb) -> float {
+    const int t = kb >> 6;
+    const float v = t == 0 ? sw0 : (t == 1 ? sw1 : (t == 2 ? sw2 : sw3));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kb & 63));
+  };
   float sw_nxt = 0.0f;
   auto load_scales = [&](int kb) {
 #pragma unroll
     for (int j = 0; j < C::TM; ++j) sa_nxt[j] = (sa_ptr + (int64_t)kb * ld_sa)[sa_row[j]];
-    sw_nxt = load_sw<SWF>(p.s_w, sw_row + kb);
+    // float32 scales: a wave-uniform (scalar) load is cheapest; UE8M0 bytes have no scalar load,
+    // so they are taken from the registers above
+    if constexpr (SWF == 0) sw_nxt = load_sw<SWF>(p.s_w, sw_row + kb);
+    else sw_nxt = sw_at(kb);
   };
 
   // Software pipeline over the wave's TN weight fragments: the MFMAs of fragment i are issued
