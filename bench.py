@@ -180,7 +180,7 @@ def extra_suites(torch, fgb, workloads, np):
             x = _randn_bf16(torch, (M, K), gen, dev)
             q, sa = fgb.quantize(x)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(max(16, fgb.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(256, fgb.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
             us = _graph_time(torch, lambda i: fgb.gemm(q, sa, wqs[i % copies], sw, out=y, workspace=ws), 4 * copies)
             byts = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * K / 128 + 2 * M * N
             dec[f"{name}_{N}x{K}_M{M}"] = dict(us=round(us, 2), gbs=round(byts / us / 1e3, 1),

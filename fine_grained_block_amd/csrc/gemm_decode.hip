@@ -12,7 +12,10 @@
 //   * the activation slice [Mpad x slice], its scales and the block's weight scales are staged
 //     once in LDS and shared by the 8 waves;
 //   * S > 1 writes float32 partials to the workspace [S][M][N]; a second kernel adds them in
-//     slice order (deterministic) and rounds to the output type.
+//     slice order (deterministic) and rounds to the output type.  (A reduction inside the same
+//     launch would need device-scope release fences, which on this multi-XCD part write back
+//     the L2 and cost far more than the second launch.)
+// M <= 16 takes a single-launch kernel that splits K over the waves of one workgroup instead.
 #include "gemm_common.hpp"
 #include "internal.h"
 
@@ -23,6 +26,7 @@ namespace {
 constexpr int THREADS = 512;
 constexpr int WAVES = THREADS / 64;
 constexpr int ROWS_PER_WG = 16 * WAVES;  // one 128-row weight block
+static_assert(128 % ROWS_PER_WG == 0, "a workgroup's rows stay inside one weight block");
 constexpr int CH = 4;                    // K-blocks per register chunk (two chunks in flight)
 constexpr int LDS_LIMIT = 64 * 1024;     // activation slice + scales budget
 
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kp
   const int kb0 = split * kpw;
   const int nk = min(KB, kb0 + kpw) - kb0;
   const int64_t n0 = (int64_t)nt * ROWS_PER_WG + wave * 16;  // this wave's 16 weight rows
-  const int64_t nb = (int64_t)nt;                             // weight block row (128 rows)
+  const int64_t nb = (int64_t)nt * ROWS_PER_WG / 128;         // weight block row of these rows
   uint8_t* a_lds = lds;                                                    // [kpw][MROWS][128]
   float* sa_lds = reinterpret_cast<float*>(lds + kpw * MROWS * 128);       // [kpw][MROWS]
   float* sw_lds = sa_lds + kpw * MROWS;                                    // [kpw]
@@ -163,6 +167,89 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   store4<OUT>(y, ldy, m, n, v4f{s.x, s.y, s.z, s.w});
 }
 
+// ---------------------------------------------------------------------------------------------
+// M <= 16: one workgroup per 16 weight rows and the whole K, its WK waves splitting the K-blocks
+// (contiguous slices) and adding their 16x16 partial tiles through LDS in wave order.  No
+// workspace, one launch; the activation fragments come straight from L2 (the whole activation
+// is at most 16 rows).
+// ---------------------------------------------------------------------------------------------
+constexpr int CHS = 2;  // K-blocks per register chunk in the small-M kernel (~100 VGPRs)
+
+template <int WK, int SWF, int OUT>
+__global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) {
+  __shared__ v4f red[WK > 1 ? WK - 1 : 1][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t K = p.K, M = p.M;
+  const int KB = (int)(K / 128);
+  const int per = (KB + WK - 1) / WK;
+  const int kb0 = min(KB, wave * per);
+  const int nk = min(KB, kb0 + per) - kb0;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t nb = n0 / 128;
+  const int g = lane >> 4;
+  const int64_t m = (lane & 15) < M ? (lane & 15) : M - 1;  // rows past M repeat row M-1
+  const uint8_t* wrow = p.w_q + (n0 + (lane & 15)) * K + (int64_t)kb0 * 128 + 32 * g;
+  const uint8_t* arow = p.a_q + m * p.lda + (int64_t)kb0 * 128 + 32 * g;
+  const float* sarow = p.s_a + (int64_t)kb0 * p.ld_sa + m;
+  const int64_t swbase = nb * KB + kb0;
+
+  int4 wv[2][CHS][2], av[2][CHS][2];
+  float sav[2][CHS];
+  auto load_chunk = [&](int c, int buf) {
+#pragma unroll
+    for (int u = 0; u < CHS; ++u) {
+      if (c + u < nk) {
+        const int64_t off = (int64_t)(c + u) * 128;
+        wv[buf][u][0] = *reinterpret_cast<const int4*>(wrow + off);
+        wv[buf][u][1] = *reinterpret_cast<const int4*>(wrow + off + 16);
+        av[buf][u][0] = *reinterpret_cast<const int4*>(arow + off);
+        av[buf][u][1] = *reinterpret_cast<const int4*>(arow + off + 16);
+        sav[buf][u] = sarow[(int64_t)(c + u) * p.ld_sa];
+      }
+    }
+  };
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute_chunk = [&](int c, int buf) {
+#pragma unroll
+    for (int u = 0; u < CHS; ++u) {
+      if (c + u < nk) {
+        v8i af, bf;
+        af[0] = wv[buf][u][0].x; af[1] = wv[buf][u][0].y; af[2] = wv[buf][u][0].z; af[3] = wv[buf][u][0].w;
+        af[4] = wv[buf][u][1].x; af[5] = wv[buf][u][1].y; af[6] = wv[buf][u][1].z; af[7] = wv[buf][u][1].w;
+        bf[0] = av[buf][u][0].x; bf[1] = av[buf][u][0].y; bf[2] = av[buf][u][0].z; bf[3] = av[buf][u][0].w;
+        bf[4] = av[buf][u][1].x; bf[5] = av[buf][u][1].y; bf[6] = av[buf][u][1].z; bf[7] = av[buf][u][1].w;
+        const float sc = sav[buf][u] * load_sw<SWF>(p.s_w, swbase + c + u);
+        acc += mfma_e4m3_16x16x128(af, bf) * sc;
+      }
+    }
+  };
+  load_chunk(0, 0);
+  for (int c = 0; c < nk; c += 2 * CHS) {
+    if (c + CHS < nk) load_chunk(c + CHS, 1);
+    compute_chunk(c, 0);
+    if (c + CHS < nk) {
+      if (c + 2 * CHS < nk) load_chunk(c + 2 * CHS, 0);
+      compute_chunk(c + CHS, 1);
+    }
+  }
+  if constexpr (WK > 1) {
+    if (wave > 0) red[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
+  }
+  if ((lane & 15) < M) store4<OUT>(p.y, p.ldy, lane & 15, n0 + 4 * g, acc);
+}
+
+// waves splitting K per 16-row tile for the small-M kernel: about 4k waves in total
+int small_waves(int64_t N, int64_t K) {
+  const int64_t tiles = N / 16;
+  int wk = 1;
+  while (wk < 8 && tiles * wk * 2 <= 4096 && wk * 2 <= K / 128) wk *= 2;
+  return wk;
+}
+
 int mtiles(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 int kb_per_wg(int64_t M, int64_t N, int64_t K) {
@@ -180,6 +267,7 @@ int kb_per_wg(int64_t M, int64_t N, int64_t K) {
 }  // namespace
 
 int decode_splits(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16) return 1;  // the small-M kernel needs no workspace
   const int KB = (int)(K / 128);
   const int kpw = kb_per_wg(M, N, K);
   return (KB + kpw - 1) / kpw;
@@ -191,6 +279,27 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream) {
+  if (a.M <= 16) {
+    const int wk = small_waves(a.N, a.K);
+    const dim3 grid((unsigned)(a.N / 16));
+#define FGB_SMALL(WK, SWF, OUT) \
+  hipLaunchKernelGGL((gemm_decode_small_kernel<WK, SWF, OUT>), grid, dim3(64 * WK), 0, stream, a)
+#define FGB_SMALL_WK(SWF, OUT)                  \
+  do {                                          \
+    if (wk == 1) FGB_SMALL(1, SWF, OUT);        \
+    else if (wk == 2) FGB_SMALL(2, SWF, OUT);   \
+    else if (wk == 4) FGB_SMALL(4, SWF, OUT);   \
+    else FGB_SMALL(8, SWF, OUT);                \
+  } while (0)
+    if (a.s_w_fmt == 0) {
+      if (a.y_dtype == 0) FGB_SMALL_WK(0, 0); else FGB_SMALL_WK(0, 1);
+    } else {
+      if (a.y_dtype == 0) FGB_SMALL_WK(1, 0); else FGB_SMALL_WK(1, 1);
+    }
+#undef FGB_SMALL_WK
+#undef FGB_SMALL
+    return hipGetLastError();
+  }
   const int kpw = kb_per_wg(a.M, a.N, a.K);
   const int S = decode_splits(a.M, a.N, a.K);
   const int MT = mtiles(a.M);

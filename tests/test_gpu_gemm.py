@@ -126,3 +126,18 @@ def test_rejects_bad_shapes(dev):
     sw = torch.ones((1, 2), dtype=torch.float32, device=dev)
     with pytest.raises(ValueError, match="FGB_ERR_SHAPE"):
         fgb.gemm(aq, sa, wq, sw)
+
+
+def test_decode_workspace_reuse_across_shapes(dev):
+    """One workspace buffer serves a sequence of split-K calls of different shapes (its contents
+    on entry do not matter)."""
+    shapes = [(64, 4096, 4096), (1, 1024, 2048), (33, 4096, 4096), (8, 1536, 14336), (1, 4096, 4096)]
+    need = max(fgb.gemm_workspace_bytes(*s) for s in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)  # NaN-patterned on entry
+    for rep in range(2):
+        for (M, N, K) in shapes:
+            ops = oracle_operands(M, N, K, key=6)
+            aq, sa, wq, sw = upload(*ops, dev)
+            y = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.float32, workspace=ws)
+            torch.cuda.synchronize()
+            check_t1(y.cpu().numpy(), ref(*ops))
