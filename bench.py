@@ -42,6 +42,10 @@ def parse():
     p.add_argument("--cpu-cols", type=int, default=4096, help="output features per projection in the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
+    p.add_argument("--derive-traffic", metavar="PMC_DIR",
+                   help="CPU only: read PMC_DIR/{FETCH_SIZE,WRITE_SIZE}/run_counter_collection.csv from "
+                        "rocprofv3 --pmc runs of '--suite step --copy-calibration' and write "
+                        "profiles/traffic.json")
     return p.parse_args()
 
 
@@ -52,6 +56,48 @@ def kernel_source_hash() -> str:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def derive_traffic(pmc_dir: str) -> dict:
+    """HBM bytes per prefill-GEMM launch from two rocprofv3 counter runs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by 1 GiB over what the same
+    counter read for the 1 GiB device copy (__amd_rocclr_copyBuffer) of the same run; the result
+    is the mean over the GEMM dispatches of one step, weighting each projection once.
+    """
+    import collections
+    import csv
+
+    def load(counter):
+        per = collections.OrderedDict()
+        with open(os.path.join(pmc_dir, counter, "run_counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                k = (int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]))
+                per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+        return per
+
+    out = {"kernel_source_hash": kernel_source_hash(), "per_grid": {}}
+    per_launch = 0.0
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = load(counter)
+        copy_kib = [v for k, v in d.items() if "copyBuffer" in k[1]]
+        if len(copy_kib) != 1:
+            raise SystemExit(f"{counter}: expected one 1 GiB copy dispatch, found {len(copy_kib)}")
+        factor = (1 << 20) / copy_kib[0]
+        out[counter.lower() + "_copy_factor"] = round(factor, 5)
+        grids = collections.defaultdict(list)
+        for k, v in d.items():
+            if "gemm_prefill_kernel" in k[1]:
+                grids[k[2]].append(v * 1024 * factor)
+        for g, vals in grids.items():
+            out["per_grid"].setdefault(str(g), {})[counter.lower() + "_bytes"] = round(sum(vals) / len(vals))
+        allv = [v for vals in grids.values() for v in vals]
+        per_launch += sum(allv) / len(allv)
+    out["gemm_prefill_hbm_bytes_per_launch"] = round(per_launch)
+    out["note"] = ("calibrated HBM fetch + write bytes per prefill-GEMM dispatch, mean over every "
+                   "GEMM dispatch of the run (each step launches the four projections once); "
+                   "per_grid splits it by launch grid (O and down share one grid)")
+    return out
 
 
 # ---------------------------------------------------------------------------------------------
@@ -276,6 +322,13 @@ def cpu_baseline(args, workloads, np):
 
 def main():
     args = parse()
+    if args.derive_traffic:
+        t = derive_traffic(args.derive_traffic)
+        with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+            json.dump(t, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(t))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the layers would shard); run with --gpus 1", file=sys.stderr)

@@ -84,11 +84,13 @@ def test_gemm_validation(L):
     assert _gemm(L, a_q=FAKE + 8) == ERR["ALIGN"]
     assert _gemm(L, lda=1032) == ERR["ALIGN"]
     assert _gemm(L, ld_sa=258) == ERR["ALIGN"]
-    # decode path needs a workspace when it splits K
-    need = L.fgb_gemm_workspace_bytes(1, 4096, 4096)
+    # the split-K decode path (16 < M <= 64) needs a workspace; M <= 16 and prefill do not
+    need = L.fgb_gemm_workspace_bytes(32, 4096, 4096)
     assert need > 0
-    assert _gemm(L, M=1, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=4) == ERR["WORKSPACE"]
-    assert _gemm(L, M=1, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=4, ws=FAKE, wsb=need - 1) == ERR["WORKSPACE"]
+    assert _gemm(L, M=32, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=32) == ERR["WORKSPACE"]
+    assert _gemm(L, M=32, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=32, ws=FAKE, wsb=need - 1) == ERR["WORKSPACE"]
+    assert L.fgb_gemm_workspace_bytes(16, 4096, 4096) == 0
+    assert L.fgb_gemm_workspace_bytes(1, 4096, 4096) == 0
     assert L.fgb_gemm_workspace_bytes(128, 4096, 4096) == 0
 
 
