@@ -15,7 +15,8 @@
 //     slice order (deterministic) and rounds to the output type.  (A reduction inside the same
 //     launch would need device-scope release fences, which on this multi-XCD part write back
 //     the L2 and cost far more than the second launch.)
-// M <= 16 takes a single-launch kernel that splits K over the waves of one workgroup instead.
+// M <= 16 takes a single-launch kernel that splits K over the waves of one workgroup instead
+// (for large weights a variant that streams the weights through per-wave LDS rings).
 #include "gemm_common.hpp"
 #include "internal.h"
 
@@ -167,6 +168,150 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   store4<OUT>(y, ldy, m, n, v4f{s.x, s.y, s.z, s.w});
 }
 
+#define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
+#define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+template <int V>
+constexpr int vmcnt_only() { return (V & 0xF) | ((V >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// gfx950 LDS: 16-byte chunk c of 128-byte row r at c ^ ((r & 7) ^ (r>>3 & 1))
+__device__ __forceinline__ int swz_g(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// ---------------------------------------------------------------------------------------------
+// M <= 16, large weights: same work split as the kernel below, but each wave streams its 16
+// weight rows (and the <= MR activation rows of its K-slice, and their scales) through a private
+// LDS ring of D stages with direct copies.  A copy instruction reads 8 whole 128-byte lines,
+// where loading the MFMA operand layout straight into registers touches 16 half-used lines per
+// instruction, which costs about four times as much address-unit time per byte on gfx950 and
+// limits the weight stream below the HBM rate.  No barrier is needed until the partial tiles are
+// added.  For small weights the extra LDS round trip costs more than it saves.
+template <int WK, int MR, int D, int SWF, int OUT>
+__global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
+  constexpr int WST = 16 * 128, AST = MR * 128, SST = 64 * 4;
+  constexpr int STAGE = WST + AST + SST;
+  constexpr int OPS = 2 + MR / 8 + 1;  // direct copies per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[WK * D * STAGE];
+  __shared__ v4f red[WK > 1 ? WK - 1 : 1][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t K = p.K, M = p.M;
+  const int KB = (int)(K / 128);
+  const int per = (KB + WK - 1) / WK;
+  const int kb0 = min(KB, wave * per);
+  const int nk = min(KB, kb0 + per) - kb0;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t nb = n0 / 128;
+  uint8_t* const wring = ring + wave * D * STAGE;
+
+  // copy sources: lane i of 8-row group q takes row 8q + i/8, logical chunk (i%8) ^ g(row)
+  uint32_t woff[2], aoff[MR / 8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 8 * q + (lane >> 3);
+    woff[q] = (uint32_t)(r * K + (((lane & 7) ^ swz_g(r)) * 16));
+  }
+#pragma unroll
+  for (int q = 0; q < MR / 8; ++q) {
+    const int r = 8 * q + (lane >> 3);
+    const int64_t m = r < M ? r : M - 1;
+    aoff[q] = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
+  }
+  const uint32_t soff = (uint32_t)(((lane & 15) < M ? (lane & 15) : M - 1) * 4);
+  const uint8_t* wbase = p.w_q + n0 * K;
+
+  auto issue = [&](int kk) {
+    uint8_t* st = wring + (kk % D) * STAGE;
+    const int64_t kb = kb0 + kk;
+    const uint8_t* wb = wbase + kb * 128;
+    const uint8_t* ab = p.a_q + kb * 128;
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(p.s_a + kb * p.ld_sa);
+    asm volatile("" : "+s"(wb));
+    asm volatile("" : "+s"(ab));
+    asm volatile("" : "+s"(sb));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t o = woff[q];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(GPTR(wb + o), LPTR(st + q * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < MR / 8; ++q) {
+      uint32_t o = aoff[q];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(GPTR(ab + o), LPTR(st + WST + q * 1024), 16, 0, 0);
+    }
+    uint32_t o = soff;
+    asm volatile("" : "+v"(o));
+    __builtin_amdgcn_global_load_lds(GPTR(sb + o), LPTR(st + WST + AST), 4, 0, 0);
+  };
+
+  // weight-block scales of this wave's slice, lane l holding block kb0 + l + 64 t (K <= 32768)
+  float sw0 = 0.0f, sw1 = 0.0f, sw2 = 0.0f, sw3 = 0.0f;
+  {
+    const int64_t b = nb * KB + kb0;
+    sw0 = lane < nk ? load_sw<SWF>(p.s_w, b + lane) : 0.0f;
+    sw1 = lane + 64 < nk ? load_sw<SWF>(p.s_w, b + lane + 64) : 0.0f;
+    sw2 = lane + 128 < nk ? load_sw<SWF>(p.s_w, b + lane + 128) : 0.0f;
+    sw3 = lane + 192 < nk ? load_sw<SWF>(p.s_w, b + lane + 192) : 0.0f;
+  }
+  auto sw_at = [&](int kk) -> float {
+    const int l = kk & 63, t = kk >> 6;
+    const int r0 = __builtin_amdgcn_readlane(__float_as_int(sw0), l);
+    const int r1 = __builtin_amdgcn_readlane(__float_as_int(sw1), l);
+    const int r2 = __builtin_amdgcn_readlane(__float_as_int(sw2), l);
+    const int r3 = __builtin_amdgcn_readlane(__float_as_int(sw3), l);
+    const int lo = (t & 1) ? r1 : r0, hi = (t & 1) ? r3 : r2;
+    return __int_as_float((t & 2) ? hi : lo);
+  };
+
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) issue(min(i, nk - 1));
+    for (int kk = 0; kk < nk; ++kk) {
+      // refill the stage consumed one block ago (clamped past the slice: never a pending stage)
+      issue(min(kk + D - 1, nk - 1));
+      __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * OPS>());
+      // The LDS reads are written as one asm block that also waits for them: the compiler cannot
+      // tell this wave's ring stages apart and would otherwise wait for every copy in flight.
+      const uint32_t st = (uint32_t)(uintptr_t)LPTR(wring + (kk % D) * STAGE);
+      const int r = lane & 15, g = lane >> 4;
+      const uint32_t aw0 = st + swz(r, 2 * g), aw1 = st + swz(r, 2 * g + 1);
+      const int ra = r & (MR - 1);
+      const uint32_t aa0 = st + WST + swz(ra, 2 * g), aa1 = st + WST + swz(ra, 2 * g + 1);
+      const uint32_t as = st + WST + AST + 4 * r;
+      v4i w0, w1, a0, a1;
+      float sa;
+      asm volatile(
+          "ds_read_b128 %0, %5\n\t"
+          "ds_read_b128 %1, %6\n\t"
+          "ds_read_b128 %2, %7\n\t"
+          "ds_read_b128 %3, %8\n\t"
+          "ds_read_b32 %4, %9\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(w0), "=&v"(w1), "=&v"(a0), "=&v"(a1), "=&v"(sa)
+          : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
+          : "memory");
+      v8i wf, af;
+      wf[0] = w0[0]; wf[1] = w0[1]; wf[2] = w0[2]; wf[3] = w0[3];
+      wf[4] = w1[0]; wf[5] = w1[1]; wf[6] = w1[2]; wf[7] = w1[3];
+      af[0] = a0[0]; af[1] = a0[1]; af[2] = a0[2]; af[3] = a0[3];
+      af[4] = a1[0]; af[5] = a1[1]; af[6] = a1[2]; af[7] = a1[3];
+      acc += mfma_e4m3_16x16x128(wf, af) * (sa * sw_at(kk));
+    }
+  }
+  if constexpr (WK > 1) {
+    if (wave > 0) red[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
+  }
+  if ((lane & 15) < M) store4<OUT>(p.y, p.ldy, lane & 15, n0 + 4 * (lane >> 4), acc);
+}
+
 // ---------------------------------------------------------------------------------------------
 // M <= 16: one workgroup per 16 weight rows and the whole K, its WK waves splitting the K-blocks
 // (contiguous slices) and adding their 16x16 partial tiles through LDS in wave order.  No
@@ -250,6 +395,9 @@ int small_waves(int64_t N, int64_t K) {
   return wk;
 }
 
+// weights from this size on take the LDS-ring kernel for M <= 16
+constexpr int64_t kRingMinWeightBytes = 48ll << 20;
+
 int mtiles(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 int kb_per_wg(int64_t M, int64_t N, int64_t K) {
@@ -279,6 +427,30 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream) {
+  if (a.M <= 16 && a.N * a.K >= kRingMinWeightBytes) {
+    const int wk = small_waves(a.N, a.K);
+    const dim3 grid((unsigned)(a.N / 16));
+#define FGB_RING(WK, SWF, OUT)                                                                              \
+  do {                                                                                                      \
+    if (a.M <= 8) hipLaunchKernelGGL((gemm_decode_ring_kernel<WK, 8, 5, SWF, OUT>), grid, dim3(64 * WK), 0, stream, a); \
+    else hipLaunchKernelGGL((gemm_decode_ring_kernel<WK, 16, 4, SWF, OUT>), grid, dim3(64 * WK), 0, stream, a);         \
+  } while (0)
+#define FGB_RING_WK(SWF, OUT)                  \
+  do {                                         \
+    if (wk == 1) FGB_RING(1, SWF, OUT);        \
+    else if (wk == 2) FGB_RING(2, SWF, OUT);   \
+    else if (wk == 4) FGB_RING(4, SWF, OUT);   \
+    else FGB_RING(8, SWF, OUT);                \
+  } while (0)
+    if (a.s_w_fmt == 0) {
+      if (a.y_dtype == 0) FGB_RING_WK(0, 0); else FGB_RING_WK(0, 1);
+    } else {
+      if (a.y_dtype == 0) FGB_RING_WK(1, 0); else FGB_RING_WK(1, 1);
+    }
+#undef FGB_RING_WK
+#undef FGB_RING
+    return hipGetLastError();
+  }
   if (a.M <= 16) {
     const int wk = small_waves(a.N, a.K);
     const dim3 grid((unsigned)(a.N / 16));

@@ -141,3 +141,42 @@ def test_decode_workspace_reuse_across_shapes(dev):
             y = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.float32, workspace=ws)
             torch.cuda.synchronize()
             check_t1(y.cpu().numpy(), ref(*ops))
+
+
+_RING_W = {}
+
+
+def _ring_weights(fmt):
+    """A 2048 x 24576 weight (exactly 48 MiB of codes, the size from which M <= 16 calls take the
+    LDS-ring decode kernel): random finite E4M3 codes and random block scales."""
+    if fmt not in _RING_W:
+        N, K = 2048, 24576
+        rng = np.random.default_rng(77)
+        codes = np.arange(256, dtype=np.uint8)
+        finite = codes[(codes & 0x7F) != 0x7F]
+        wq = rng.choice(finite, size=(N, K))
+        if fmt == "f32":
+            sw = (rng.uniform(0.25, 4.0, size=(N // 128, K // 128)) / 448).astype(np.float32)
+        else:
+            sw = rng.integers(112, 124, size=(N // 128, K // 128), dtype=np.uint8)
+        _RING_W[fmt] = (wq, sw)
+    return _RING_W[fmt]
+
+
+@pytest.mark.parametrize("M", [1, 7, 8, 9, 16])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_decode_large_weight_ring_kernel(dev, M, fmt):
+    """M <= 16 with a large weight (the LDS-ring decode kernel), both activation-row stagings
+    (M <= 8 and M <= 16); operands are random finite codes and scales."""
+    wq, sw = _ring_weights(fmt)
+    N, K = wq.shape
+    rng = np.random.default_rng(1000 + M)
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    aq = rng.choice(finite, size=(M, K))
+    sa = (rng.uniform(0.25, 4.0, size=(M, K // 128)) / 448).astype(np.float32)
+    yref = gemm.gemm_ref_fast(aq, sa, wq, sw, fmt)
+    y32 = _run((aq, sa, wq, sw), dev, torch.float32).cpu().numpy()
+    check_t1(y32, yref)
+    y16 = _run((aq, sa, wq, sw), dev, torch.bfloat16)
+    check_t2(bf16_tensor_to_f64(y16), yref)
