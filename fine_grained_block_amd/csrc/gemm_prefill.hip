@@ -7,7 +7,8 @@
 // Workgroup: 512 threads (8 waves, 2 per SIMD) computing a BN x BM tile of y^T (BN output
 // features x BM tokens).  Per K-block the W and A tiles (BN x 128 and BM x 128 bytes) are
 // copied HBM/L2 -> LDS by the direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging),
-// two stages deep: while block kb is multiplied out of one stage, block kb+1 lands in the other.
+// STAGES deep (three for the 256 x 128 tiles): while block kb is multiplied out of one stage, the
+// copies of the next blocks land in the others.
 // Each stage is its own __shared__ array so the compiler can tell the in-flight copies from the
 // LDS reads of the current stage and does not wait for them.
 //
@@ -21,6 +22,7 @@
 //
 // Each wave owns a (BN/WN) x (BM/WM) sub-tile = TN x TM MFMA tiles of 16x16.  For every K-block
 // one MFMA per tile yields the exact-product float32 partial P, and acc += P * (s_a * s_w).
+// bf16 output tiles are staged through LDS so that the stores write whole lines.
 #include "gemm_common.hpp"
 #include "internal.h"
 
@@ -90,8 +92,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 
   const int nwg = tiles_m * tiles_n;
   const int pid = xcd_remap((int)blockIdx.x, nwg);
-  // grouped ordering: bands of GROUP_M tile-rows share W tiles in L2
-  constexpr int GROUP_M = 8;
+  // grouped ordering: bands of GROUP_M tile-rows share W tiles in L2 (narrower bands for short K,
+  // where a tile's operands are in L2 only briefly)
+  const int GROUP_M = p.K <= 16 * KBYTES ? 4 : 8;
   const int in_group = GROUP_M * tiles_n;
   const int group_id = pid / in_group;
   const int first_m = group_id * GROUP_M;
@@ -269,15 +272,50 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     }
   }
 
-  // epilogue: lane holds 4 consecutive output features of one token per MFMA tile
+  // epilogue.  bf16 tiles of 128 tokens go through LDS (rows 0-63 in stage0, 64-127 in stage1,
+  // free once every wave is past its last block) so that the global stores write whole 128-byte
+  // lines; stored directly, a lane's 4 consecutive output features of one token make every store
+  // instruction touch 16 rows.
+  constexpr int ROWB = C::BN * 2 + 16;  // padded LDS row: the 16 rows of a fragment hit distinct banks
+  if constexpr (OUT == 0 && C::BM == 128 && 64 * ROWB <= C::STAGE) {
+    wg_barrier();
 #pragma unroll
-  for (int j = 0; j < C::TM; ++j) {
-    const int64_t m = row0 + wm * (C::BM / C::WM) + j * 16 + (lane & 15);
-    if (m < row_end) {
+    for (int j = 0; j < C::TM; ++j) {
+      const int ml = wm * (C::BM / C::WM) + j * 16 + (lane & 15);
+      uint8_t* const half = ml < 64 ? stage0 : stage1;
 #pragma unroll
       for (int i = 0; i < C::TN; ++i) {
-        const int64_t n = n0 + wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4);
-        store4<OUT>(p.y, p.ldy, m, n, acc[i][j]);
+        const int nl = wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4);
+        uint2 w;
+        w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][0]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][1]) << 16);
+        w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][2]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(half + (ml & 63) * ROWB + nl * 2) = w;
+      }
+    }
+    wg_barrier();
+    constexpr int CPR = C::BN * 2 / 16;  // 16-byte chunks per output row
+    for (int c = tid; c < C::BM * CPR; c += C::THREADS) {
+      const int ml = c / CPR, ch = c - ml * CPR;
+      const int64_t m = row0 + ml;
+      if (m < row_end) {
+        const uint8_t* half = ml < 64 ? stage0 : stage1;
+        const int4 v = *reinterpret_cast<const int4*>(half + (ml & 63) * ROWB + ch * 16);
+        *reinterpret_cast<int4*>(reinterpret_cast<uint16_t*>(p.y) + m * p.ldy + n0 + ch * 8) = v;
+      }
+    }
+  } else {
+    // lane holds 4 consecutive output features of one token per MFMA tile
+#pragma unroll
+    for (int j = 0; j < C::TM; ++j) {
+      const int64_t m = row0 + wm * (C::BM / C::WM) + j * 16 + (lane & 15);
+      if (m < row_end) {
+#pragma unroll
+        for (int i = 0; i < C::TN; ++i) {
+          const int64_t n = n0 + wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4);
+          store4<OUT>(p.y, p.ldy, m, n, acc[i][j]);
+        }
       }
     }
   }
