@@ -154,19 +154,6 @@ def headline_step(args, torch, fgb, workloads, np):
 
 
 # ---------------------------------------------------------------------------------------------
-def _randn_bf16(torch, shape, gen, dev, outliers=True, std=1.0):
-    """Device-side draw of the same recipes as `workloads` (N(0,1) with 1% x20 outliers, or
-    N(0, std)), for the extra timing suites where bit-identity with the oracle is not needed."""
-    x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
-    if outliers:
-        n = x.numel()
-        idx = torch.randperm(n, generator=gen, device=dev)[: int(round(0.01 * n))]
-        x.view(-1)[idx] *= 20.0
-    else:
-        x *= std
-    return x.to(torch.bfloat16)
-
-
 def _graph_time(torch, fn, reps):
     """Capture `reps` calls of fn(i) in a HIP graph, replay it, return microseconds per call."""
     s = torch.cuda.Stream()
@@ -208,8 +195,11 @@ def _event_time(torch, fn, reps, flush=None):
 
 def extra_suites(torch, fgb, workloads, np):
     dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(0)
+    seeds = iter(range(1000, 1000000))
+
+    def next_seed():
+        return next(seeds)
+
     out = {}
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -219,13 +209,13 @@ def extra_suites(torch, fgb, workloads, np):
     # decode (split-K) — hipGraph loop over rotating weight copies (> 2x MALL in total)
     dec = {}
     for (name, N, K) in workloads.DECODE_SHAPES:
-        w = _randn_bf16(torch, (N, K), gen, dev, outliers=False, std=0.02)
+        w = workloads.device_bf16((N, K), next_seed(), dev, outliers=False, std=0.02)
         wq0, sw = fgb.quantize_weight(w)
         del w
         copies = max(2, -(-2 * MALL_BYTES // (N * K)) + 1)
         wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
         for M in workloads.DECODE_MS:
-            x = _randn_bf16(torch, (M, K), gen, dev)
+            x = workloads.device_bf16((M, K), next_seed(), dev)
             q, sa = fgb.quantize(x)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             ws = torch.zeros(max(256, fgb.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
@@ -240,10 +230,10 @@ def extra_suites(torch, fgb, workloads, np):
     ds = {}
     M = workloads.DEEPSEEK_V3_PREFILL_M
     for (name, N, K) in workloads.DEEPSEEK_V3_LINEARS:
-        w = _randn_bf16(torch, (N, K), gen, dev, outliers=False, std=0.02)
+        w = workloads.device_bf16((N, K), next_seed(), dev, outliers=False, std=0.02)
         wq, sw = fgb.quantize_weight(w, "ue8m0")
         del w
-        x = _randn_bf16(torch, (M, K), gen, dev)
+        x = workloads.device_bf16((M, K), next_seed(), dev)
         q, sa = fgb.quantize(x)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         us = _event_time(torch, lambda i: fgb.gemm(q, sa, wq, sw, out=y), 5, flush)
@@ -258,12 +248,12 @@ def extra_suites(torch, fgb, workloads, np):
     off_d = torch.from_numpy(offsets).to(dev)
     T = int(offsets[-1])
     for nm, (N, K) in [("gate_up", workloads.MOE["gate_up"]), ("down", workloads.MOE["down"])]:
-        w = _randn_bf16(torch, (32 * N, K), gen, dev, outliers=False, std=0.02)
+        w = workloads.device_bf16((32 * N, K), next_seed(), dev, outliers=False, std=0.02)
         wq, sw = fgb.quantize_weight(w)  # 128-row blocks never straddle experts (N % 128 == 0)
         del w
         wq = wq.view(32, N, K)
         sw = sw.view(32, N // 128, K // 128)
-        x = _randn_bf16(torch, (T, K), gen, dev)
+        x = workloads.device_bf16((T, K), next_seed(), dev)
         q, sa = fgb.quantize(x)
         y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
         us = _event_time(torch, lambda i: fgb.grouped_gemm(q, sa, wq, sw, off_d, out=y), 5, flush)
@@ -279,7 +269,7 @@ def extra_suites(torch, fgb, workloads, np):
     for (M, K) in [(4096, 4096), (4096, 14336), (8192, 7168), (8192, 18432), (32768, 7168)]:
         per_call = 3.03125 * M * K
         copies = max(2, int(-(-2 * MALL_BYTES // per_call)) + 1)
-        xs = [_randn_bf16(torch, (M, K), gen, dev) for _ in range(min(copies, 2))]
+        xs = [workloads.device_bf16((M, K), next_seed(), dev) for _ in range(min(copies, 2))]
         xs += [xs[i % 2].clone() for i in range(copies - len(xs))]
         qs = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(copies)]
         sas = [torch.empty((K // 128, M), dtype=torch.float32, device=dev) for _ in range(copies)]

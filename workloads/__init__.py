@@ -129,3 +129,24 @@ def offsets_from_counts(counts) -> np.ndarray:
     off = np.zeros(len(counts) + 1, dtype=np.int32)
     off[1:] = np.cumsum(counts)
     return off
+
+
+# ---------------------------------------------------------------------------------------------
+# Device-side draws of the same recipes (for full-size runs, where host generation of hundreds of
+# millions of values would dominate).  torch's seeded generator on the given device; the values
+# are bf16 and any host-side check copies back exactly the bytes the device holds.
+# ---------------------------------------------------------------------------------------------
+def device_bf16(shape, seed: int, device, outliers: bool = True, std: float = 1.0):
+    """bf16 tensor: N(0,1) with round(1% of entries) x20 (outliers=True), or N(0, std)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    if outliers:
+        n = x.numel()
+        idx = torch.randperm(n, generator=gen, device=device)[: int(round(0.01 * n))]
+        x.view(-1)[idx] *= 20.0
+    else:
+        x *= std
+    return x.to(torch.bfloat16)
