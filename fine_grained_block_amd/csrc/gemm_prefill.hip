@@ -110,18 +110,37 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   const uint8_t* wq = p.w_q;
   int64_t sw_base = 0;
   if constexpr (GROUPED) {
-    int cum = 0, e = 0;
-    int64_t r0 = 0, r1 = 0;
-    bool found = false;
-    for (; e < p.E; ++e) {
-      r0 = p.offsets[e];
-      r1 = p.offsets[e + 1];
-      const int mt = (int)((r1 - r0 + C::BM - 1) / C::BM);
-      if (pid_m < cum + mt) { found = true; break; }
-      cum += mt;
+    // Expert of this tile: tiles are numbered expert by expert, ceil(rows_e / BM) each.  63
+    // experts per pass: lane l holds offsets[e0 + l], the tile counts are prefix-summed across
+    // the wave and a ballot finds the first expert whose tiles reach past pid_m.
+    const int lane0 = threadIdx.x & 63;
+    int cum = 0, e = -1, first = 0;
+    int r0 = 0, r1 = 0;
+    for (int e0 = 0; e0 < p.E; e0 += 63) {
+      const int idx = e0 + lane0;
+      const int off = idx <= p.E ? p.offsets[idx] : 0;
+      const int nxt = __shfl_down(off, 1);
+      const bool real = lane0 < 63 && idx < p.E;
+      const int mt = real ? (nxt - off + C::BM - 1) / C::BM : 0;
+      int inc = mt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(inc, d);
+        if (lane0 >= d) inc += t;
+      }
+      const unsigned long long hit = __ballot(real && cum + inc > pid_m);
+      if (hit) {
+        first = __ffsll((long long)hit) - 1;
+        e = e0 + first;
+        r0 = __shfl(off, first);
+        r1 = __shfl(nxt, first);
+        cum += __shfl(inc - mt, first);
+        break;
+      }
+      cum += __shfl(inc, 62);
     }
-    if (!found) return;  // padding tile beyond the real tile count
-    row0 = r0 + (int64_t)(pid_m - cum) * C::BM;
+    if (e < 0) return;  // padding tile beyond the real tile count
+    row0 = (int64_t)r0 + (int64_t)(pid_m - cum) * C::BM;
     row_end = r1;
     wq += (int64_t)e * N * K;
     sw_base = (int64_t)e * NBLK * KB;
