@@ -7,8 +7,8 @@
 // Workgroup: 512 threads (8 waves, 2 per SIMD) computing a BN x BM tile of y^T (BN output
 // features x BM tokens).  Per K-block the W and A tiles (BN x 128 and BM x 128 bytes) are
 // copied HBM/L2 -> LDS by the direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging),
-// STAGES deep (three for the 256 x 128 tiles): while block kb is multiplied out of one stage, the
-// copies of the next blocks land in the others.
+// STAGES deep (three for 256 x 128 tiles, two for 256 x 256): while block kb is multiplied out of
+// one stage, the copies of the next blocks land in the others.
 // Each stage is its own __shared__ array so the compiler can tell the in-flight copies from the
 // LDS reads of the current stage and does not wait for them.
 //
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % C::WN, wm = wave / C::WN;
 
   // direct-load sources: lane i of 8-row group q fetches row 8q + i/8, chunk (i%8) ^ g(row)
@@ -179,6 +179,12 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   auto issue = [&](int kb, uint8_t* st) {
     const uint8_t* wb = wbase + (int64_t)kb * KBYTES;
     const uint8_t* ab = abase + (int64_t)kb * KBYTES;
+    asm volatile("" : "+s"(wb));
+    asm volatile("" : "+s"(ab));
+#pragma unroll
+    for (int i = 0; i < C::W_LD; ++i) asm volatile("" : "+v"(woff[i]));
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i) asm volatile("" : "+v"(aoff[i]));
 #pragma unroll
     for (int i = 0; i < C::W_LD; ++i)
       __builtin_amdgcn_global_load_lds(GPTR(wb + woff[i]), LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, 0, 0);
@@ -226,7 +232,13 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   float sw_nxt = 0.0f;
   auto load_scales = [&](int kb) {
 #pragma unroll
-    for (int j = 0; j < C::TM; ++j) sa_nxt[j] = (sa_ptr + (int64_t)kb * ld_sa)[sa_row[j]];
+    for (int j = 0; j < C::TM; ++j) {
+      const float* sb = sa_ptr + (int64_t)kb * ld_sa;
+      asm volatile("" : "+s"(sb));
+      uint32_t o = sa_row[j] * 4u;
+      asm volatile("" : "+v"(o));
+      sa_nxt[j] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sb) + o);
+    }
     // float32 scales: a wave-uniform (scalar) load is cheapest; UE8M0 bytes have no scalar load,
     // so they are taken from the registers above
     if constexpr (SWF == 0) sw_nxt = load_sw<SWF>(p.s_w, sw_row + kb);
@@ -243,18 +255,32 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 #pragma unroll
     for (int j = 0; j < C::TM; ++j) bf[j] = lds_frag(as, wm * (C::BM / C::WM) + j * 16, lane);
     v8i af[2];
-    v4f P[2][C::TM];
     af[0] = lds_frag(ws, 0, lane);
+    if constexpr (C::TM >= 4) {
+      // TM >= 4 MFMAs per fragment cover the result latency of the first: the scale-FMAs of a
+      // fragment follow its own MFMAs, one partial buffer
+      v4f P[C::TM];
 #pragma unroll
-    for (int i = 0; i <= C::TN; ++i) {
-      if (i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
-      if (i < C::TN) {
+      for (int i = 0; i < C::TN; ++i) {
+        if (i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
 #pragma unroll
-        for (int j = 0; j < C::TM; ++j) P[i & 1][j] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
+        for (int j = 0; j < C::TM; ++j) P[j] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
+#pragma unroll
+        for (int j = 0; j < C::TM; ++j) acc[i][j] += P[j] * sc[j];
       }
-      if (i > 0) {
+    } else {
+      v4f P[2][C::TM];
 #pragma unroll
-        for (int j = 0; j < C::TM; ++j) acc[i - 1][j] += P[(i - 1) & 1][j] * sc[j];
+      for (int i = 0; i <= C::TN; ++i) {
+        if (i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
+        if (i < C::TN) {
+#pragma unroll
+          for (int j = 0; j < C::TM; ++j) P[i & 1][j] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
+        }
+        if (i > 0) {
+#pragma unroll
+          for (int j = 0; j < C::TM; ++j) acc[i - 1][j] += P[(i - 1) & 1][j] * sc[j];
+        }
       }
     }
   };
@@ -291,37 +317,42 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     }
   }
 
-  // epilogue.  bf16 tiles of 128 tokens go through LDS (rows 0-63 in stage0, 64-127 in stage1,
-  // free once every wave is past its last block) so that the global stores write whole 128-byte
+  // epilogue.  bf16 tiles go through LDS in rounds of two 64-row chunks (stage0 and stage1, free
+  // once every wave is past its last block) so that the global stores write whole 128-byte
   // lines; stored directly, a lane's 4 consecutive output features of one token make every store
   // instruction touch 16 rows.
   constexpr int ROWB = C::BN * 2 + 16;  // padded LDS row: the 16 rows of a fragment hit distinct banks
-  if constexpr (OUT == 0 && C::BM == 128 && 64 * ROWB <= C::STAGE) {
-    wg_barrier();
-#pragma unroll
-    for (int j = 0; j < C::TM; ++j) {
-      const int ml = wm * (C::BM / C::WM) + j * 16 + (lane & 15);
-      uint8_t* const half = ml < 64 ? stage0 : stage1;
-#pragma unroll
-      for (int i = 0; i < C::TN; ++i) {
-        const int nl = wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4);
-        uint2 w;
-        w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][0]) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][1]) << 16);
-        w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][2]) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(half + (ml & 63) * ROWB + nl * 2) = w;
-      }
-    }
-    wg_barrier();
+  if constexpr (OUT == 0 && C::BM % 128 == 0 && 64 * ROWB <= C::STAGE) {
     constexpr int CPR = C::BN * 2 / 16;  // 16-byte chunks per output row
-    for (int c = tid; c < C::BM * CPR; c += C::THREADS) {
-      const int ml = c / CPR, ch = c - ml * CPR;
-      const int64_t m = row0 + ml;
-      if (m < row_end) {
-        const uint8_t* half = ml < 64 ? stage0 : stage1;
-        const int4 v = *reinterpret_cast<const int4*>(half + (ml & 63) * ROWB + ch * 16);
-        *reinterpret_cast<int4*>(reinterpret_cast<uint16_t*>(p.y) + m * p.ldy + n0 + ch * 8) = v;
+#pragma unroll
+    for (int r = 0; r < C::BM / 128; ++r) {
+      wg_barrier();
+#pragma unroll
+      for (int j = 0; j < C::TM; ++j) {
+        const int ml = wm * (C::BM / C::WM) + j * 16 + (lane & 15);
+        if ((ml >> 7) == r) {
+          uint8_t* const half = (ml & 64) ? stage1 : stage0;
+#pragma unroll
+          for (int i = 0; i < C::TN; ++i) {
+            const int nl = wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4);
+            uint2 w;
+            w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][0]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][1]) << 16);
+            w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][2]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][3]) << 16);
+            *reinterpret_cast<uint2*>(half + (ml & 63) * ROWB + nl * 2) = w;
+          }
+        }
+      }
+      wg_barrier();
+      for (int c = tid; c < 128 * CPR; c += C::THREADS) {
+        const int mr = c / CPR, ch = c - mr * CPR;
+        const int64_t m = row0 + r * 128 + mr;
+        if (m < row_end) {
+          const uint8_t* half = mr < 64 ? stage0 : stage1;
+          const int4 v = *reinterpret_cast<const int4*>(half + (mr & 63) * ROWB + ch * 16);
+          *reinterpret_cast<int4*>(reinterpret_cast<uint16_t*>(p.y) + m * p.ldy + n0 + ch * 8) = v;
+        }
       }
     }
   } else {
@@ -341,7 +372,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 }
 
 #ifndef FGB_BIG_CFG
-#define FGB_BIG_CFG 256, 128, 2, 4, 1, 3
+#define FGB_BIG_CFG 256, 256, 2, 4, 1, 2
 #endif
 #ifndef FGB_HALF_CFG
 #define FGB_HALF_CFG 256, 128, 2, 4, 1, 3
@@ -366,8 +397,9 @@ hipError_t launch_cfg(const GemmArgs& a, int tiles_m, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile choice: 256 x 256 unless its last round of workgroups over the 256 CUs would be mostly
-// empty and the 256 x 128 tile fills the machine better; 128 x 128 when N is not a multiple of 256.
+// Tile choice: 256 x 256 (8 waves of 128 x 64, two stages) when K has at least 32 blocks and its
+// workgroups fill the 256 CUs about as well as the 256 x 128 tile's (three stages, waves of
+// 128 x 32); otherwise 256 x 128.  128 x 128 tiles with 2 stages when N % 256 != 0.
 enum class Pick { Big, Half, Narrow };
 
 template <typename C>
@@ -375,8 +407,9 @@ int64_t tiles_for(int64_t M, int64_t N) { return ((M + C::BM - 1) / C::BM) * (N 
 
 double fill(int64_t tiles) { return (double)tiles / (double)(((tiles + 255) / 256) * 256); }
 
-Pick pick_tile(int64_t M, int64_t N) {
+Pick pick_tile(int64_t M, int64_t N, int64_t K) {
   if (N % Big::BN != 0 || N % Half::BN != 0) return Pick::Narrow;
+  if (K < 32 * KBYTES) return Pick::Half;
   const double eff_big = fill(tiles_for<Big>(M, N));
   const double eff_half = fill(tiles_for<Half>(M, N));
   return eff_half > eff_big * 1.15 ? Pick::Half : Pick::Big;
@@ -385,7 +418,7 @@ Pick pick_tile(int64_t M, int64_t N) {
 }  // namespace
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
-  switch (pick_tile(a.M, a.N)) {
+  switch (pick_tile(a.M, a.N, a.K)) {
     case Pick::Big: return launch_cfg<Big, false>(a, (int)((a.M + Big::BM - 1) / Big::BM), stream);
     case Pick::Half: return launch_cfg<Half, false>(a, (int)((a.M + Half::BM - 1) / Half::BM), stream);
     default: return launch_cfg<Narrow, false>(a, (int)((a.M + Narrow::BM - 1) / Narrow::BM), stream);
