@@ -29,8 +29,9 @@ def _run(aq, sa, wq, sw, offsets, dev, dt):
 
 @pytest.mark.parametrize("counts", [[7, 0, 300, 130], [0, 0, 257, 0], [129], [1, 1, 1, 1, 1, 1, 1, 1], [0, 513]])
 @pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
-def test_grouped_parity(dev, counts, fmt):
-    E, N, K = len(counts), 256, 512
+@pytest.mark.parametrize("K", [512, 4096])  # K >= 4096 takes the 256 x 256 tiles
+def test_grouped_parity(dev, counts, fmt, K):
+    E, N = len(counts), 256
     offsets = workloads.offsets_from_counts(counts)
     T = int(offsets[-1])
     x = workloads.activations(T, K, key=(0, 31, 0, T))
@@ -43,8 +44,11 @@ def test_grouped_parity(dev, counts, fmt):
     check_t2(bf16_tensor_to_f64(y16), yref)
 
 
-def test_single_expert_equals_dense(dev):
-    T, N, K = 300, 384, 1024
+@pytest.mark.parametrize("N,K", [(384, 1024), (512, 4096)])
+def test_single_expert_equals_dense(dev, N, K):
+    """E = 1 equals the dense GEMM bit for bit (at (512, 4096) the grouped launch uses 256 x 256
+    tiles and the dense one 256 x 128: the per-block partials and their order are the same)."""
+    T = 300
     x = workloads.activations(T, K, key=(0, 32, 0, 0))
     aq, sa = blockquant.act_quant(x)
     wq, sw = _experts(1, N, K, key=5)
