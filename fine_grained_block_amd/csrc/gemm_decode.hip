@@ -302,6 +302,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
       acc += mfma_e4m3_16x16x128(wf, af) * (sa * sw_at(kk));
     }
   }
+  // the clamped copies past the slice must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
   if constexpr (WK > 1) {
     if (wave > 0) red[wave - 1][lane] = acc;
     __syncthreads();

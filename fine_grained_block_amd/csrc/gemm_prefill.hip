@@ -316,6 +316,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       if (kb + 2 < KB) step(kb + 2, stage2, stage1);
     }
   }
+  // The last steps re-issued copies of the final block (clamped) into stages that nothing reads
+  // any more; they must have landed before the stages are reused for the output tile below and
+  // before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
 
   // epilogue.  bf16 tiles go through LDS in rounds of two 64-row chunks (stage0 and stage1, free
   // once every wave is past its last block) so that the global stores write whole 128-byte
