@@ -28,13 +28,33 @@ __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// Global-memory accesses through address-space-1 pointers.  Pointers that reach a kernel inside a
+// struct argument are generic to the compiler, which then emits flat instructions; a flat access
+// also counts against lgkmcnt, so every later wait for LDS reads would wait for it as well.
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+  return *(const T __attribute__((address_space(1)))*)p;
+}
+template <typename T>
+__device__ __forceinline__ void gstore(void* p, T v) {
+  *(T __attribute__((address_space(1)))*)p = v;
+}
+
+__device__ __forceinline__ int4 gload_i4(const void* p) {
+  const v4i v = gload<v4i>(p);
+  return make_int4(v[0], v[1], v[2], v[3]);
+}
+
 // Weight-block scale as float32 from either storage format.
 template <int SWF>
 __device__ __forceinline__ float load_sw(const void* s_w, int64_t idx) {
   if constexpr (SWF == 0) {
-    return reinterpret_cast<const float*>(s_w)[idx];
+    return gload<float>(reinterpret_cast<const float*>(s_w) + idx);
   } else {
-    return dec_ue8m0(reinterpret_cast<const uint8_t*>(s_w)[idx]);
+    return dec_ue8m0(gload<uint8_t>(reinterpret_cast<const uint8_t*>(s_w) + idx));
   }
 }
 
@@ -44,15 +64,14 @@ __device__ __forceinline__ void store4(void* y, int64_t ldy, int64_t m, int64_t 
   if constexpr (OUT == 0) {
     uint16_t* p = reinterpret_cast<uint16_t*>(y) + m * ldy + n;
     // float32 -> bf16 round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950)
-    uint2 w;
-    w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
-          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
-    w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
-          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = w;
+    v2u w;
+    w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+    w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+    gstore<v2u>(p, w);
   } else {
-    float* p = reinterpret_cast<float*>(y) + m * ldy + n;
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    gstore<v4f>(reinterpret_cast<float*>(y) + m * ldy + n, v);
   }
 }
 

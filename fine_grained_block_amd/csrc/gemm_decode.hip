@@ -63,8 +63,8 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kp
     for (int u = 0; u < CH; ++u) {
       if (c + u < nk) {
         const uint8_t* src = wrow + (int64_t)(c + u) * 128;
-        wb[buf][u][0] = *reinterpret_cast<const int4*>(src);
-        wb[buf][u][1] = *reinterpret_cast<const int4*>(src + 16);
+        wb[buf][u][0] = gload_i4(src);
+        wb[buf][u][1] = gload_i4(src + 16);
       }
     }
   };
@@ -77,13 +77,13 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kp
     const int row = (c >> 3) % MROWS;
     const int kk = (c >> 3) / MROWS;
     const int64_t m = row < M ? row : M - 1;
-    const int4 v = *reinterpret_cast<const int4*>(p.a_q + m * p.lda + (int64_t)(kb0 + kk) * 128 + ch * 16);
+    const int4 v = gload_i4(p.a_q + m * p.lda + (int64_t)(kb0 + kk) * 128 + ch * 16);
     *reinterpret_cast<int4*>(a_lds + kk * MROWS * 128 + swz(row, ch)) = v;
   }
   for (int c = tid; c < MROWS * nk; c += THREADS) {
     const int row = c % MROWS, kk = c / MROWS;
     const int64_t m = row < M ? row : M - 1;
-    sa_lds[c] = p.s_a[(int64_t)(kb0 + kk) * p.ld_sa + m];
+    sa_lds[c] = gload<float>(p.s_a + (int64_t)(kb0 + kk) * p.ld_sa + m);
   }
   for (int c = tid; c < nk; c += THREADS) sw_lds[c] = load_sw<SWF>(p.s_w, nb * KB + kb0 + c);
 
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kp
         store4<OUT>(p.y, p.ldy, m, n, acc[j]);
       } else {
         float* dst = ws + ((int64_t)split * M + m) * N + n;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        gstore<v4f>(dst, acc[j]);
       }
     }
   }
@@ -154,24 +154,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t m = q / (N / 4), n = (q - m * (N / 4)) * 4;
   const float* base = ws + m * N + n;
   const int64_t slice = M * N;
-  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int i0 = 0; i0 < S; i0 += 8) {
-    float4 v[8];
+    v4f v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = i0 + u < S ? *reinterpret_cast<const float4*>(base + (int64_t)(i0 + u) * slice) : make_float4(0, 0, 0, 0);
+      v[u] = i0 + u < S ? gload<v4f>(base + (int64_t)(i0 + u) * slice) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (i0 + u < S) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+      if (i0 + u < S) s += v[u];
     }
   }
-  store4<OUT>(y, ldy, m, n, v4f{s.x, s.y, s.z, s.w});
+  store4<OUT>(y, ldy, m, n, s);
 }
 
 #define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
-
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 template <int V>
 constexpr int vmcnt_only() { return (V & 0xF) | ((V >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -347,11 +345,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
     for (int u = 0; u < CHS; ++u) {
       if (c + u < nk) {
         const int64_t off = (int64_t)(c + u) * 128;
-        wv[buf][u][0] = *reinterpret_cast<const int4*>(wrow + off);
-        wv[buf][u][1] = *reinterpret_cast<const int4*>(wrow + off + 16);
-        av[buf][u][0] = *reinterpret_cast<const int4*>(arow + off);
-        av[buf][u][1] = *reinterpret_cast<const int4*>(arow + off + 16);
-        sav[buf][u] = sarow[(int64_t)(c + u) * p.ld_sa];
+        wv[buf][u][0] = gload_i4(wrow + off);
+        wv[buf][u][1] = gload_i4(wrow + off + 16);
+        av[buf][u][0] = gload_i4(arow + off);
+        av[buf][u][1] = gload_i4(arow + off + 16);
+        sav[buf][u] = gload<float>(sarow + (int64_t)(c + u) * p.ld_sa);
       }
     }
   };
