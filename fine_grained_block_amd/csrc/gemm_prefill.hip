@@ -437,7 +437,8 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t stream) {
   // upper bound on the per-expert tile count: sum_e ceil(M_e/BM) <= ceil(total_M/BM) + E
-  if (a.N % Big::BN == 0 && a.K >= 32 * KBYTES)
+  // (256 x 256 tiles already from K = 2048 here: MoE down, K = 2048, +15% over 256 x 128)
+  if (a.N % Big::BN == 0 && a.K >= 16 * KBYTES)
     return launch_cfg<Big, true>(a, (int)((a.M + Big::BM - 1) / Big::BM) + a.E, stream);
   if (a.N % Half::BN == 0)
     return launch_cfg<Half, true>(a, (int)((a.M + Half::BM - 1) / Half::BM) + a.E, stream);
