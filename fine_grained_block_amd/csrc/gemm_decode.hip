@@ -1,11 +1,12 @@
-// gemm_decode.hip — split-K block-scaled FP8 GEMM for small M (decode, M <= 64), gfx950.
+// gemm_decode.hip — block-scaled FP8 GEMM for small M (decode, M <= 64), gfx950.
 //
 // Same result as the prefill path (Transformers "Fine-grained FP8", "DeepGEMM fast path"), but
 // for few tokens the weight stream dominates (bytes per weight: 1 for FP8, per the Baseten
-// NVFP4 summary, "Less memory, more compute"), so the kernel is organised to keep HBM busy:
+// NVFP4 summary, "Less memory, more compute"), so the kernels are organised to keep HBM busy.
+// 16 < M <= 64, split-K:
 //   * a workgroup = 8 waves covers one 128-row weight block (16 rows per wave, one MFMA tile)
-//     and a slice of whole K-blocks; the grid is (N/128) x S slices, S chosen so ~4k waves
-//     (M <= 16) or ~2k waves stream W;
+//     and a slice of whole K-blocks; the grid is (N/128) x S slices, S chosen so ~2k waves
+//     stream W;
 //   * each wave streams its W rows straight into registers in the MFMA operand layout (32
 //     contiguous bytes per lane), two chunks of CH K-blocks in flight; the first chunk is
 //     requested before anything else;
@@ -398,12 +399,12 @@ int small_waves(int64_t N, int64_t K) {
 // weights from this size on take the LDS-ring kernel for M <= 16
 constexpr int64_t kRingMinWeightBytes = 48ll << 20;
 
-int mtiles(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+int mtiles(int64_t M) { return M <= 32 ? 2 : 4; }  // split-K kernel: 16 < M <= 64
 
 int kb_per_wg(int64_t M, int64_t N, int64_t K) {
   const int KB = (int)(K / 128);
   const int64_t waves_per_split = N / 16;
-  const int64_t target = M <= 16 ? 4096 : 2048;
+  const int64_t target = 2048;  // waves streaming W
   int S = (int)((target + waves_per_split - 1) / waves_per_split);
   S = S < 1 ? 1 : (S > KB ? KB : S);
   int kpw = (KB + S - 1) / S;
@@ -482,8 +483,7 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
   hipLaunchKernelGGL((gemm_decode_kernel<MT_, SWF, OUT>), grid, block, lds, stream, a, kpw, S, ws)
 #define FGB_DEC_MT(SWF, OUT)                 \
   do {                                       \
-    if (MT == 1) FGB_DEC(1, SWF, OUT);       \
-    else if (MT == 2) FGB_DEC(2, SWF, OUT);  \
+    if (MT == 2) FGB_DEC(2, SWF, OUT);       \
     else FGB_DEC(4, SWF, OUT);               \
   } while (0)
   if (a.s_w_fmt == 0) {
