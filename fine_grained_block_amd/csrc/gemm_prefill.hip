@@ -6,8 +6,8 @@
 //
 // Workgroup: 512 threads (8 waves, 2 per SIMD) computing a BN x BM tile of y^T (BN output
 // features x BM tokens).  Per K-block the W and A tiles (BN x 128 and BM x 128 bytes) are
-// copied HBM/L2 -> LDS by the direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging),
-// STAGES deep (three for 256 x 128 tiles, two for 256 x 256): while block kb is multiplied out of
+// copied HBM/L2 -> LDS by the direct-to-LDS loads (buffer_load_dwordx4 ... lds: no VGPR staging),
+// together with the tile's activation scales, STAGES deep (three for 256 x 128 tiles, two for 256 x 256): while block kb is multiplied out of
 // one stage, the copies of the next blocks land in the others.
 // Each stage is its own __shared__ array so the compiler can tell the in-flight copies from the
 // LDS reads of the current stage and does not wait for them.
@@ -32,7 +32,6 @@ namespace {
 
 constexpr int KBYTES = 128;  // one K-block of E4M3 codes per row
 
-#define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
 
 template <int BN_, int BM_, int WN_, int WM_, int MINB_, int STAGES_>
@@ -50,7 +49,9 @@ struct Cfg {
   static constexpr int STAGE = W_BYTES + A_BYTES;
   static constexpr int W_LD = BN / 8 / WAVES;  // direct loads (8 rows each) per wave per stage
   static constexpr int A_LD = BM / 8 / WAVES;
+  static constexpr int SA_LD = BM / 64;  // waves that copy the tile's activation scales (64 tokens each)
   static constexpr int NDMA = W_LD + A_LD;
+  static_assert(SA_LD <= WAVES, "one activation-scale copy per wave at most");
   static_assert(W_LD >= 1 && A_LD >= 1, "every wave loads whole 8-row groups");
   static_assert((BN / WN) % 128 == 0 || 128 % (BN / WN) == 0, "a wave's rows stay in one weight block");
 };
@@ -89,6 +90,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage2[C::STAGES > 2 ? C::STAGE : 16];
+  // the tile's activation scales s_a[row0 .. row0+BM-1, kb], one array per stage like the tiles
+  __shared__ __attribute__((aligned(16))) float sas0[C::BM];
+  __shared__ __attribute__((aligned(16))) float sas1[C::BM];
+  __shared__ __attribute__((aligned(16))) float sas2[C::STAGES > 2 ? C::BM : 4];
 
   const int nwg = tiles_m * tiles_n;
   const int pid = xcd_remap((int)blockIdx.x, nwg);
@@ -176,35 +181,43 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     row = row < row_end ? row : row_end - 1;
     aoff[i] = (uint32_t)(row * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
   }
-  auto issue = [&](int kb, uint8_t* st) {
-    const uint8_t* wb = wbase + (int64_t)kb * KBYTES;
-    const uint8_t* ab = abase + (int64_t)kb * KBYTES;
-    asm volatile("" : "+s"(wb));
-    asm volatile("" : "+s"(ab));
-#pragma unroll
-    for (int i = 0; i < C::W_LD; ++i) asm volatile("" : "+v"(woff[i]));
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) asm volatile("" : "+v"(aoff[i]));
+  // activation-scale copy: lane l of wave w < SA_LD fetches the scale of token row0 + 64w + l
+  // (clamped to the last row, like the tile rows)
+  uint32_t saoff = 0;
+  if (wave < C::SA_LD) {
+    int64_t row = row0 + 64 * wave + lane;
+    row = row < row_end ? row : row_end - 1;
+    saoff = (uint32_t)(row * 4);
+  }
+  // The copies use the buffer form of the direct-to-LDS load (MUBUF).  The global form is a FLAT
+  // instruction that touches both global memory and LDS, after which the compiler can no longer
+  // count LDS reads and waits for all of them (lgkmcnt(0)) wherever it needs one; with buffer
+  // loads it waits only for the reads the next instruction uses.  32-bit offsets; the range check
+  // is off (num_records = 2^32 - 1): the library validated every operand's extent.
+  auto issue = [&](int kb, uint8_t* st, float* sas) {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
+    const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.s_a, 0, -1, 0x00020000);
+    if (wave < C::SA_LD)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * wave), 4, saoff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
+    const uint32_t koff = (uint32_t)kb * KBYTES;
 #pragma unroll
     for (int i = 0; i < C::W_LD; ++i)
-      __builtin_amdgcn_global_load_lds(GPTR(wb + woff[i]), LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, woff[i],
+                                               koff, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::A_LD; ++i)
-      __builtin_amdgcn_global_load_lds(GPTR(ab + aoff[i]),
-                                       LPTR(st + C::W_BYTES + (wave + i * C::WAVES) * 8 * KBYTES), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + C::W_BYTES + (wave + i * C::WAVES) * 8 * KBYTES), 16,
+                                               aoff[i], koff, 0, 0);
+#endif
   };
 
-  // per-lane activation scale rows (one token per lane per m-tile)
-  uint32_t sa_row[C::TM];
+  // this lane's tokens within the tile (one per m-tile)
+  int tok[C::TM];
 #pragma unroll
-  for (int j = 0; j < C::TM; ++j) {
-    const int64_t row = row0 + wm * (C::BM / C::WM) + j * 16 + (lane & 15);
-    sa_row[j] = (uint32_t)(row < row_end ? row : row_end - 1);
-  }
+  for (int j = 0; j < C::TM; ++j) tok[j] = wm * (C::BM / C::WM) + j * 16 + (lane & 15);
   const int64_t nb = (n0 + wn * (C::BN / C::WN)) / 128;  // this wave's weight block row
-  const float* sa_ptr = p.s_a;
-  const int64_t ld_sa = p.ld_sa;
-  const int64_t sw_row = sw_base + nb * KB;
 
   v4f acc[C::TN][C::TM];
 #pragma unroll
@@ -212,69 +225,73 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 #pragma unroll
     for (int j = 0; j < C::TM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // scales: block kb+1's load while block kb is multiplied; each step first folds the landed
-  // pair into per-token products sc[j] = s_a[m_j, kb] * s_w[nb, kb]
-  float sa_nxt[C::TM];
-  // The weight-block scales s_w[nb, 0 .. KB-1] (either format) are loaded once into registers
-  // spread over the lanes (lane l holds block l + 64 t, K <= 32768) and broadcast with v_readlane:
-  // no per-block load (a uniform address would become a scalar load, whose lgkmcnt wait would
-  // hold up the LDS reads that share that counter).
-  float sw0 = lane < KB ? load_sw<SWF>(p.s_w, sw_row + lane) : 0.0f;
-  float sw1 = lane + 64 < KB ? load_sw<SWF>(p.s_w, sw_row + lane + 64) : 0.0f;
-  float sw2 = lane + 128 < KB ? load_sw<SWF>(p.s_w, sw_row + lane + 128) : 0.0f;
-  float sw3 = lane + 192 < KB ? load_sw<SWF>(p.s_w, sw_row + lane + 192) : 0.0f;
-  auto sw_at = [&](int kb) -> float {
-    // broadcast first (scalar values), then select without branches
-    const int l = kb & 63, t = kb >> 6;
-    const int r0 = __builtin_amdgcn_readlane(__float_as_int(sw0), l);
-    const int r1 = __builtin_amdgcn_readlane(__float_as_int(sw1), l);
-    const int r2 = __builtin_amdgcn_readlane(__float_as_int(sw2), l);
-    const int r3 = __builtin_amdgcn_readlane(__float_as_int(sw3), l);
-    const int lo = (t & 1) ? r1 : r0, hi = (t & 1) ? r3 : r2;
-    return __int_as_float((t & 2) ? hi : lo);
-  };
-  float sw_nxt = 0.0f;
-  auto load_scales = [&](int kb) {
-#pragma unroll
-    for (int j = 0; j < C::TM; ++j) {
-      const float* sb = sa_ptr + (int64_t)kb * ld_sa;
-      asm volatile("" : "+s"(sb));
-      uint32_t o = sa_row[j] * 4u;
-      asm volatile("" : "+v"(o));
-      // Measured: the three-stage 256 x 128 kernel runs 7-9% faster with generic (flat) loads of
-      // the activation scales and a per-block generic load of a float32 weight scale than with
-      // global loads and the register copy below, the two-stage 256 x 256 kernel 2% slower.
-      if constexpr (C::STAGES == 3) sa_nxt[j] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sb) + o);
-      else sa_nxt[j] = gload<float>(reinterpret_cast<const char*>(sb) + o);
-    }
-    if constexpr (SWF == 0 && C::STAGES == 3) sw_nxt = reinterpret_cast<const float*>(p.s_w)[sw_row + kb];
-    else sw_nxt = sw_at(kb);
-  };
+  // The weight-block scales of the tile's block rows, s_w[n0/128 + b, 0 .. KB-1] (either format,
+  // decoded to float32), are staged once in LDS (K <= 32768); a step reads its wave's value with
+  // one broadcast LDS read.
+  constexpr int NBT = C::BN / 128 > 0 ? C::BN / 128 : 1;
+  __shared__ __attribute__((aligned(16))) float sws[NBT * 256];
+  for (int idx = tid; idx < NBT * KB; idx += C::THREADS) {
+    const int b = idx / KB, k = idx - b * KB;
+    sws[b * 256 + k] = load_sw<SWF>(p.s_w, sw_base + (n0 / 128 + b) * KB + k);
+  }
+  const float* sw_lds = sws + (int)(nb - n0 / 128) * 256;
 
-  // Software pipeline over the wave's TN weight fragments: the MFMAs of fragment i are issued
-  // before the scale-FMAs of fragment i-1 consume their results, and fragment i+1 is read from
-  // LDS meanwhile, so matrix core, VALU and LDS work overlap instead of waiting on each other.
-  auto compute = [&](const uint8_t* st, const float* sc) {
+  // One K-block of the wave's sub-tile: one MFMA per 16x16 tile gives the partial P, then
+  // acc += P * (s_a * s_w).  The MFMAs, the scale-FMAs and the fragment reads are interleaved so
+  // that matrix core, VALU and LDS work overlap instead of waiting on each other.
+  auto compute = [&](const uint8_t* st, const float* sas_cur, const float* swp) {
     const uint8_t* ws = st + wn * (C::BN / C::WN) * KBYTES;
-    const uint8_t* as = st + C::W_BYTES;
-    v8i bf[C::TM];
-#pragma unroll
-    for (int j = 0; j < C::TM; ++j) bf[j] = lds_frag(as, wm * (C::BM / C::WM) + j * 16, lane);
-    v8i af[2];
-    af[0] = lds_frag(ws, 0, lane);
+    const uint8_t* as = st + C::W_BYTES + wm * (C::BM / C::WM) * KBYTES;
+    float sc[C::TM];
     if constexpr (C::TM >= 4) {
-      // TM >= 4 MFMAs per fragment cover the result latency of the first: the scale-FMAs of a
-      // fragment follow its own MFMAs, one partial buffer
-      v4f P[C::TM];
+      // LDS reads in the order of first use (they complete in order, so a wait covers only what
+      // the next MFMA needs): the first W and A fragments and the scales, then A fragment j+1 with
+      // MFMA j of the first W fragment and W fragment i+1 with the first MFMA of W fragment i.
+      v8i af[2], bf[C::TM];
+      af[0] = lds_frag(ws, 0, lane);
+      bf[0] = lds_frag(as, 0, lane);
+      float sav[C::TM];
 #pragma unroll
-      for (int i = 0; i < C::TN; ++i) {
-        if (i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
+      for (int j = 0; j < C::TM; ++j) sav[j] = sas_cur[tok[j]];
+      const float swv = *swp;
+      __builtin_amdgcn_sched_barrier(0);
+      // MFMA t = (i, j) in i-major order; the scale-FMAs of MFMA t - LAG (one W fragment earlier)
+      // follow MFMA t, by which time its result is long complete.  The order is pinned: left to
+      // itself the scheduler hoists every fragment read to the top, which costs registers and
+      // makes the first MFMA wait for all of them.
+      constexpr int LAG = C::TM;
+      constexpr int T = C::TN * C::TM;
+      v4f P[LAG + 1];
 #pragma unroll
-        for (int j = 0; j < C::TM; ++j) P[j] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
+      for (int t = 0; t < T + LAG; ++t) {
+        if (t < T) {
+          const int i = t / C::TM, j = t % C::TM;
+          if (i == 0 && j + 1 < C::TM) bf[j + 1] = lds_frag(as, (j + 1) * 16, lane);
+          P[t % (LAG + 1)] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
+          // fragment i+1 into the buffer whose MFMAs (fragment i-1) are all issued
+          if (j == 0 && i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
+        }
+        if (t == LAG) {
 #pragma unroll
-        for (int j = 0; j < C::TM; ++j) acc[i][j] += P[j] * sc[j];
+          for (int j = 0; j < C::TM; ++j) sc[j] = sav[j] * swv;
+        }
+        if (t >= LAG) {
+          const int u = t - LAG;
+          acc[u / C::TM][u % C::TM] += P[u % (LAG + 1)] * sc[u % C::TM];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      // fewer token tiles per wave: all of the block's A fragments first, two P buffers (the
+      // scale-FMAs of W fragment i-1 follow the MFMAs of fragment i)
+      const float swv = *swp;
+#pragma unroll
+      for (int j = 0; j < C::TM; ++j) sc[j] = sas_cur[tok[j]] * swv;
+      v8i bf[C::TM];
+#pragma unroll
+      for (int j = 0; j < C::TM; ++j) bf[j] = lds_frag(as, j * 16, lane);
+      v8i af[2];
+      af[0] = lds_frag(ws, 0, lane);
       v4f P[2][C::TM];
 #pragma unroll
       for (int i = 0; i <= C::TN; ++i) {
@@ -291,35 +308,31 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     }
   };
 
-  // Block kb lives in stage kb % STAGES.  A step waits for its own block's copies (leaving the
-  // younger copies in flight), synchronizes, starts the scale loads for kb+1 and the copies for
+  // Block kb (tiles and activation scales) lives in stage kb % STAGES.  A step waits for its own
+  // block's copies (leaving the younger copies in flight), synchronizes, starts the copies for
   // kb+STAGES-1 into the stage consumed one step earlier, and multiplies block kb.  Past the last
   // block the loads are clamped to it (harmless re-reads into a stage no later step reads), so
   // every step issues the same loads and one fixed vmcnt wait covers all of them.
-  auto step = [&](int kb, const uint8_t* cur, uint8_t* refill) {
+  auto step = [&](int kb, const uint8_t* cur, const float* sas_cur, uint8_t* refill, float* sas_refill) {
+    // own copies of block kb (and its scales) landed, leaving the younger ones in flight
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<C::STAGES == 3 ? C::NDMA : 0>());
     wg_barrier();
-    float sc[C::TM];
-#pragma unroll
-    for (int j = 0; j < C::TM; ++j) sc[j] = sa_nxt[j] * sw_nxt;
-    load_scales(min(kb + 1, KB - 1));
-    issue(min(kb + C::STAGES - 1, KB - 1), refill);
-    compute(cur, sc);
+    issue(min(kb + C::STAGES - 1, KB - 1), refill, sas_refill);
+    compute(cur, sas_cur, sw_lds + kb);
   };
 
-  issue(0, stage0);
-  load_scales(0);
-  if (C::STAGES == 3) issue(min(1, KB - 1), stage1);
+  issue(0, stage0, sas0);
+  if (C::STAGES == 3) issue(min(1, KB - 1), stage1, sas1);
   if constexpr (C::STAGES == 2) {
     for (int kb = 0; kb < KB; kb += 2) {
-      step(kb, stage0, stage1);
-      if (kb + 1 < KB) step(kb + 1, stage1, stage0);
+      step(kb, stage0, sas0, stage1, sas1);
+      if (kb + 1 < KB) step(kb + 1, stage1, sas1, stage0, sas0);
     }
   } else {
     for (int kb = 0; kb < KB; kb += 3) {
-      step(kb, stage0, stage2);
-      if (kb + 1 < KB) step(kb + 1, stage1, stage0);
-      if (kb + 2 < KB) step(kb + 2, stage2, stage1);
+      step(kb, stage0, sas0, stage2, sas2);
+      if (kb + 1 < KB) step(kb + 1, stage1, sas1, stage0, sas0);
+      if (kb + 2 < KB) step(kb + 2, stage2, sas2, stage1, sas1);
     }
   }
   // The last steps re-issued copies of the final block (clamped) into stages that nothing reads
