@@ -31,6 +31,10 @@ namespace fgb {
 namespace {
 
 constexpr int KBYTES = 128;  // one K-block of E4M3 codes per row
+// Waves with four token tiles issue the copies of the next block spread over the first MFMAs of
+// the current one, one every SPACING MFMAs, rather than in a burst after the barrier (+2-5% on
+// the 256 x 256 tiles; later issue leaves the copies too little time).
+constexpr int SPACING = 2;
 
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
 
@@ -49,7 +53,7 @@ struct Cfg {
   static constexpr int STAGE = W_BYTES + A_BYTES;
   static constexpr int W_LD = BN / 8 / WAVES;  // direct loads (8 rows each) per wave per stage
   static constexpr int A_LD = BM / 8 / WAVES;
-  static constexpr int SA_LD = BM / 64;  // waves that copy the tile's activation scales (64 tokens each)
+  static constexpr int SA_LD = BM / 64;  // 64-token copies of the tile's activation scales
   static constexpr int NDMA = W_LD + A_LD;
   static_assert(SA_LD <= WAVES, "one activation-scale copy per wave at most");
   static_assert(W_LD >= 1 && A_LD >= 1, "every wave loads whole 8-row groups");
@@ -181,11 +185,14 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     row = row < row_end ? row : row_end - 1;
     aoff[i] = (uint32_t)(row * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
   }
-  // activation-scale copy: lane l of wave w < SA_LD fetches the scale of token row0 + 64w + l
-  // (clamped to the last row, like the tile rows)
-  uint32_t saoff = 0;
-  if (wave < C::SA_LD) {
-    int64_t row = row0 + 64 * wave + lane;
+  // activation-scale copy: lane l of wave w fetches the scale of token row0 + 64 (w % SA_LD) + l
+  // (clamped to the last row, like the tile rows).  Waves past SA_LD repeat a copy of an earlier
+  // wave (same bytes to the same place) rather than skip it: a branch here would leave the
+  // compiler unable to count the LDS reads that follow and make it wait for all of them.
+  const int sa_grp = wave % C::SA_LD;
+  uint32_t saoff;
+  {
+    int64_t row = row0 + 64 * sa_grp + lane;
     row = row < row_end ? row : row_end - 1;
     saoff = (uint32_t)(row * 4);
   }
@@ -194,13 +201,33 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // count LDS reads and waits for all of them (lgkmcnt(0)) wherever it needs one; with buffer
   // loads it waits only for the reads the next instruction uses.  32-bit offsets; the range check
   // is off (num_records = 2^32 - 1): the library validated every operand's extent.
+  // copy d of block kb: 0 = the activation scales, then the W_LD weight and the
+  // A_LD activation 8-row groups
+  constexpr int NPART = 1 + C::W_LD + C::A_LD;
+  auto issue_part = [&](int kb, uint8_t* st, float* sas, int d) {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
+    const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.s_a, 0, -1, 0x00020000);
+    const uint32_t koff = (uint32_t)kb * KBYTES;
+    if (d == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * sa_grp), 4, saoff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
+    } else if (d <= C::W_LD) {
+      const int i = d - 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, woff[i], koff, 0, 0);
+    } else {
+      const int i = d - 1 - C::W_LD;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + C::W_BYTES + (wave + i * C::WAVES) * 8 * KBYTES), 16,
+                                               aoff[i], koff, 0, 0);
+    }
+#endif
+  };
   auto issue = [&](int kb, uint8_t* st, float* sas) {
 #if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.s_a, 0, -1, 0x00020000);
-    if (wave < C::SA_LD)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * wave), 4, saoff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * sa_grp), 4, saoff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
     const uint32_t koff = (uint32_t)kb * KBYTES;
 #pragma unroll
     for (int i = 0; i < C::W_LD; ++i)
@@ -239,22 +266,22 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // One K-block of the wave's sub-tile: one MFMA per 16x16 tile gives the partial P, then
   // acc += P * (s_a * s_w).  The MFMAs, the scale-FMAs and the fragment reads are interleaved so
   // that matrix core, VALU and LDS work overlap instead of waiting on each other.
-  auto compute = [&](const uint8_t* st, const float* sas_cur, const float* swp) {
+  // (the copies of block kb_next are issued spread over the MFMAs when SPACING > 0)
+  auto compute = [&](const uint8_t* st, const float* sas_cur, const float* swp, int kb_next, uint8_t* refill,
+                     float* sas_refill) {
     const uint8_t* ws = st + wn * (C::BN / C::WN) * KBYTES;
     const uint8_t* as = st + C::W_BYTES + wm * (C::BM / C::WM) * KBYTES;
     float sc[C::TM];
     if constexpr (C::TM >= 4) {
       // LDS reads in the order of first use (they complete in order, so a wait covers only what
-      // the next MFMA needs): the first W and A fragments and the scales, then A fragment j+1 with
-      // MFMA j of the first W fragment and W fragment i+1 with the first MFMA of W fragment i.
+      // the next MFMA needs): the first W fragment and the A fragments, then W fragment i+1 with
+      // the first MFMA of W fragment i, the scales with the second MFMA.
       v8i af[2], bf[C::TM];
       af[0] = lds_frag(ws, 0, lane);
-      bf[0] = lds_frag(as, 0, lane);
-      float sav[C::TM];
 #pragma unroll
-      for (int j = 0; j < C::TM; ++j) sav[j] = sas_cur[tok[j]];
-      const float swv = *swp;
+      for (int j = 0; j < C::TM; ++j) bf[j] = lds_frag(as, j * 16, lane);
       __builtin_amdgcn_sched_barrier(0);
+      float sav[C::TM], swv = 0.0f;
       // MFMA t = (i, j) in i-major order; the scale-FMAs of MFMA t - LAG (one W fragment earlier)
       // follow MFMA t, by which time its result is long complete.  The order is pinned: left to
       // itself the scheduler hoists every fragment read to the top, which costs registers and
@@ -264,12 +291,22 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       v4f P[LAG + 1];
 #pragma unroll
       for (int t = 0; t < T + LAG; ++t) {
+        if constexpr (SPACING > 0) {
+          // every copy issued within the loop (T + LAG iterations)
+          constexpr int SP = (NPART - 1) * SPACING < T + LAG ? SPACING : (T + LAG - 1) / (NPART - 1);
+          static_assert(SP >= 1 && (NPART - 1) * SP < T + LAG, "copies fit the MFMA sequence");
+          if (t % SP == 0 && t / SP < NPART) issue_part(kb_next, refill, sas_refill, t / SP);
+        }
         if (t < T) {
           const int i = t / C::TM, j = t % C::TM;
-          if (i == 0 && j + 1 < C::TM) bf[j + 1] = lds_frag(as, (j + 1) * 16, lane);
           P[t % (LAG + 1)] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
           // fragment i+1 into the buffer whose MFMAs (fragment i-1) are all issued
           if (j == 0 && i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
+          if (t == 1) {
+#pragma unroll
+            for (int jj = 0; jj < C::TM; ++jj) sav[jj] = sas_cur[tok[jj]];
+            swv = *swp;
+          }
         }
         if (t == LAG) {
 #pragma unroll
@@ -317,8 +354,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     // own copies of block kb (and its scales) landed, leaving the younger ones in flight
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<C::STAGES == 3 ? C::NDMA : 0>());
     wg_barrier();
-    issue(min(kb + C::STAGES - 1, KB - 1), refill, sas_refill);
-    compute(cur, sas_cur, sw_lds + kb);
+    const int kb_next = min(kb + C::STAGES - 1, KB - 1);
+    if (!(SPACING > 0 && C::TM >= 4)) issue(kb_next, refill, sas_refill);
+    compute(cur, sas_cur, sw_lds + kb, kb_next, refill, sas_refill);
   };
 
   issue(0, stage0, sas0);
