@@ -206,7 +206,7 @@ def extra_suites(torch, fgb, workloads, np):
     def flush():
         flush_buf.fill_(1)
 
-    # decode (split-K) — hipGraph loop over rotating weight copies (> 2x MALL in total)
+    # decode — hipGraph loop over rotating weight copies (> 2x MALL in total)
     dec = {}
     for (name, N, K) in workloads.DECODE_SHAPES:
         w = workloads.device_bf16((N, K), next_seed(), dev, outliers=False, std=0.02)
@@ -224,7 +224,7 @@ def extra_suites(torch, fgb, workloads, np):
             dec[f"{name}_{N}x{K}_M{M}"] = dict(us=round(us, 2), gbs=round(byts / us / 1e3, 1),
                                                 frac_hbm=round(byts / us / 1e3 / PEAK_HBM_GBS, 3))
         del wqs, wq0
-    out["decode_splitk"] = dec
+    out["decode"] = dec
 
     # DeepSeek-V3-shaped prefill with UE8M0 weight scales (M = 8192), flushed between calls
     ds = {}

@@ -2,22 +2,16 @@
 //
 // Same result as the prefill path (Transformers "Fine-grained FP8", "DeepGEMM fast path"), but
 // for few tokens the weight stream dominates (bytes per weight: 1 for FP8, per the Baseten
-// NVFP4 summary, "Less memory, more compute"), so the kernels are organised to keep HBM busy.
-// 16 < M <= 64, split-K:
-//   * a workgroup = 8 waves covers one 128-row weight block (16 rows per wave, one MFMA tile)
-//     and a slice of whole K-blocks; the grid is (N/128) x S slices, S chosen so ~2k waves
-//     stream W;
-//   * each wave streams its W rows straight into registers in the MFMA operand layout (32
-//     contiguous bytes per lane), two chunks of CH K-blocks in flight; the first chunk is
-//     requested before anything else;
-//   * the activation slice [Mpad x slice], its scales and the block's weight scales are staged
-//     once in LDS and shared by the 8 waves;
-//   * S > 1 writes float32 partials to the workspace [S][M][N]; a second kernel adds them in
-//     slice order (deterministic) and rounds to the output type.  (A reduction inside the same
-//     launch would need device-scope release fences, which on this multi-XCD part write back
-//     the L2 and cost far more than the second launch.)
-// M <= 16 takes a single-launch kernel that splits K over the waves of one workgroup instead
-// (for large weights a variant that streams the weights through per-wave LDS rings).
+// NVFP4 summary, "Less memory, more compute"), so the kernels are organised to keep HBM busy:
+//   * M <= 16: one workgroup per 16 weight rows and the whole K, its waves splitting the
+//     K-blocks; weights >= 48 MiB stream through per-wave LDS rings with whole-line direct
+//     copies, smaller ones load the MFMA operand layout straight into registers.  One launch.
+//   * 16 < M <= 64: a workgroup of 8 waves per 128-row weight block over a K slice, weights,
+//     activations and their scales streamed through a 4-stage LDS ring shared by the waves; K is
+//     sliced only to occupy the CUs, and sliced shapes add their float32 partials [S][M][N] in a
+//     second, ordered launch.  (A reduction inside the same launch would need device-scope
+//     release fences, which on this multi-XCD part write back the L2 and cost more than the
+//     second launch.)
 #include "gemm_common.hpp"
 #include "internal.h"
 
@@ -25,123 +19,10 @@ namespace fgb {
 
 namespace {
 
-constexpr int THREADS = 512;
-constexpr int WAVES = THREADS / 64;
-constexpr int ROWS_PER_WG = 16 * WAVES;  // one 128-row weight block
-static_assert(128 % ROWS_PER_WG == 0, "a workgroup's rows stay inside one weight block");
-constexpr int CH = 4;                    // K-blocks per register chunk (two chunks in flight)
-constexpr int LDS_LIMIT = 64 * 1024;     // activation slice + scales budget
-
 // 16-byte chunk c of LDS row r sits at c ^ ((r & 7) ^ (r>>3 & 1)): conflict-free 16-row fragment
 // reads on gfx950's 64-bank LDS.
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
-}
-
-__host__ __device__ constexpr int lds_bytes_per_kb(int mt) { return 16 * mt * 128 + 16 * mt * 4 + 4; }
-
-template <int MT, int SWF, int OUT>
-__global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs p, int kpw, int S, float* ws) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr int MROWS = 16 * MT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t K = p.K, N = p.N, M = p.M;
-  const int KB = (int)(K / 128);
-  const int nt = blockIdx.x / S, split = blockIdx.x - nt * S;
-  const int kb0 = split * kpw;
-  const int nk = min(KB, kb0 + kpw) - kb0;
-  const int64_t n0 = (int64_t)nt * ROWS_PER_WG + wave * 16;  // this wave's 16 weight rows
-  const int64_t nb = (int64_t)nt * ROWS_PER_WG / 128;         // weight block row of these rows
-  uint8_t* a_lds = lds;                                                    // [kpw][MROWS][128]
-  float* sa_lds = reinterpret_cast<float*>(lds + kpw * MROWS * 128);       // [kpw][MROWS]
-  float* sw_lds = sa_lds + kpw * MROWS;                                    // [kpw]
-
-  const int g = lane >> 4;
-  const uint8_t* wrow = p.w_q + (n0 + (lane & 15)) * K + (int64_t)kb0 * 128 + 32 * g;
-  int4 wb[2][CH][2];
-  auto load_chunk = [&](int c, int buf) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      if (c + u < nk) {
-        const uint8_t* src = wrow + (int64_t)(c + u) * 128;
-        wb[buf][u][0] = gload_i4(src);
-        wb[buf][u][1] = gload_i4(src + 16);
-      }
-    }
-  };
-  load_chunk(0, 0);  // the weight stream starts first
-
-  // stage activations [MROWS x nk*128] (rows >= M replicate row M-1; their results are dropped),
-  // their scales, and the weight block's scales for the slice
-  for (int c = tid; c < MROWS * nk * 8; c += THREADS) {
-    const int ch = c & 7;
-    const int row = (c >> 3) % MROWS;
-    const int kk = (c >> 3) / MROWS;
-    const int64_t m = row < M ? row : M - 1;
-    const int4 v = gload_i4(p.a_q + m * p.lda + (int64_t)(kb0 + kk) * 128 + ch * 16);
-    *reinterpret_cast<int4*>(a_lds + kk * MROWS * 128 + swz(row, ch)) = v;
-  }
-  for (int c = tid; c < MROWS * nk; c += THREADS) {
-    const int row = c % MROWS, kk = c / MROWS;
-    const int64_t m = row < M ? row : M - 1;
-    sa_lds[c] = gload<float>(p.s_a + (int64_t)(kb0 + kk) * p.ld_sa + m);
-  }
-  for (int c = tid; c < nk; c += THREADS) sw_lds[c] = load_sw<SWF>(p.s_w, nb * KB + kb0 + c);
-
-  v4f acc[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  __syncthreads();
-
-  auto compute_chunk = [&](int c, int buf) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int kk = c + u;
-      if (kk < nk) {
-        const float sw = sw_lds[kk];
-        v8i af;
-        af[0] = wb[buf][u][0].x; af[1] = wb[buf][u][0].y; af[2] = wb[buf][u][0].z; af[3] = wb[buf][u][0].w;
-        af[4] = wb[buf][u][1].x; af[5] = wb[buf][u][1].y; af[6] = wb[buf][u][1].z; af[7] = wb[buf][u][1].w;
-        const uint8_t* ab = a_lds + kk * MROWS * 128;
-#pragma unroll
-        for (int j = 0; j < MT; ++j) {
-          const int r = j * 16 + (lane & 15);
-          const int4 lo = *reinterpret_cast<const int4*>(ab + swz(r, 2 * g));
-          const int4 hi = *reinterpret_cast<const int4*>(ab + swz(r, 2 * g + 1));
-          v8i bf;
-          bf[0] = lo.x; bf[1] = lo.y; bf[2] = lo.z; bf[3] = lo.w;
-          bf[4] = hi.x; bf[5] = hi.y; bf[6] = hi.z; bf[7] = hi.w;
-          const float sc = sa_lds[kk * MROWS + r] * sw;
-          const v4f P = mfma_e4m3_16x16x128(af, bf);
-          acc[j] += P * sc;
-        }
-      }
-    }
-  };
-
-  for (int c = 0; c < nk; c += 2 * CH) {
-    if (c + CH < nk) load_chunk(c + CH, 1);
-    compute_chunk(c, 0);
-    if (c + CH < nk) {
-      if (c + 2 * CH < nk) load_chunk(c + 2 * CH, 0);
-      compute_chunk(c + CH, 1);
-    }
-  }
-
-  const int64_t n = n0 + 4 * g;
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int64_t m = j * 16 + (lane & 15);
-    if (m < M) {
-      if (S == 1) {
-        store4<OUT>(p.y, p.ldy, m, n, acc[j]);
-      } else {
-        float* dst = ws + ((int64_t)split * M + m) * N + n;
-        gstore<v4f>(dst, acc[j]);
-      }
-    }
-  }
 }
 
 // Sum of the S partial slices in slice order; all loads of a group of 8 slices are issued
@@ -314,6 +195,177 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// 16 < M <= 64: a workgroup of 8 waves owns one 128-row weight block (16 rows per wave) over a
+// slice of K-blocks.  The block's weight rows, the 16*MT activation rows (rows >= M repeat row
+// M-1; their results are dropped) and the activation scales of each K-block stream through a
+// ring of D LDS stages shared by the waves, with whole-line buffer-form direct copies issued
+// D-1 blocks ahead and one barrier per block; the activation stream is read once per 128 weight
+// rows.  Slices (S > 1) write float32 partials [S][M][N] for the ordered reduction launch.
+// ---------------------------------------------------------------------------------------------
+template <int MT, int D, int SWF, int OUT>
+__global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int kpw, int S, float* ws) {
+  constexpr int MROWS = 16 * MT;
+  constexpr int WB = 128 * 128, AB = MROWS * 128, SB = 64 * 4;
+  constexpr int STAGE = WB + AB + SB;
+  constexpr int A_GRP = MROWS / 8;                 // 8-row copy groups of the activation rows
+  constexpr int OPS = 2 + 1 + 1;                   // copies per wave per block: W, A, scales
+  static_assert(D >= 3 && D <= 6, "three to six stages");
+  static_assert(MT == 2 || MT == 4, "32 or 64 activation rows");
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[D > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st4[D > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st5[D > 5 ? STAGE : 16];
+  __shared__ float sws[256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t K = p.K, N = p.N, M = p.M;
+  const int KB = (int)(K / 128);
+  const int nt = blockIdx.x / S, split = blockIdx.x - nt * S;
+  const int kb0 = split * kpw;
+  const int nk = min(KB, kb0 + kpw) - kb0;
+  const int64_t n0 = (int64_t)nt * 128;
+
+  // copy sources: lane i of 8-row group q takes row 8q + i/8, logical chunk (i%8) ^ g(row); the
+  // activation groups past A_GRP repeat earlier ones (same bytes to the same place: no branch)
+  uint32_t woff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (wave + 8 * i) + (lane >> 3);
+    woff[i] = (uint32_t)(r * K + (((lane & 7) ^ swz_g(r)) * 16));
+  }
+  const int aq = wave % A_GRP;
+  uint32_t aoff;
+  {
+    const int r = 8 * aq + (lane >> 3);
+    const int64_t m = r < M ? r : M - 1;
+    aoff = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
+  }
+  const uint32_t soff = (uint32_t)((lane < M ? lane : M - 1) * 4);
+
+  auto issue = [&](int kk, uint8_t* st) {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
+    const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_q + n0 * K), 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.s_a, 0, -1, 0x00020000);
+    const int kb = kb0 + kk;
+    const uint32_t koff = (uint32_t)kb * 128;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + 8 * i) * 1024), 16, woff[i], koff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + WB + aq * 1024), 16, aoff, koff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(st + WB + AB), 4, soff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
+#endif
+  };
+  auto stage = [&](int i) -> uint8_t* {
+    switch (i) {
+      case 0: return st0;
+      case 1: return st1;
+      case 2: return st2;
+      case 3: return st3;
+      case 4: return st4;
+      default: return st5;
+    }
+  };
+
+  for (int c = tid; c < nk; c += 512) sws[c] = load_sw<SWF>(p.s_w, (n0 / 128) * KB + kb0 + c);
+
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int r = lane & 15, g = lane >> 4;
+  auto step = [&](int kk, const uint8_t* cur, uint8_t* refill) {
+    // own copies of block kk landed (the younger D-2 blocks' stay in flight), then everyone's:
+    // an execution barrier only (__syncthreads' fence would wait for every copy in flight)
+    __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 2) * OPS>());
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(kk + D - 1, nk - 1), refill);  // into the stage consumed one block ago
+    // The stage's LDS reads are one asm block that also waits for them: after the step guards
+    // below (control-flow joins) the compiler can no longer tell the ring stages apart and would
+    // wait for every copy in flight.
+    const uint32_t b = (uint32_t)(uintptr_t)LPTR(cur);
+    const uint32_t w0 = b + swz(16 * wave + r, 2 * g), w1 = b + swz(16 * wave + r, 2 * g + 1);
+    const uint32_t a0 = b + WB + swz(r, 2 * g), a1 = b + WB + swz(r, 2 * g + 1);
+    const uint32_t sp = b + WB + AB + 4 * r;
+    v4i wl, wh, al[MT], ah[MT];
+    float sa[MT];
+    if constexpr (MT == 2) {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %1, %9\n\t"
+          "ds_read_b128 %2, %10\n\t"
+          "ds_read_b128 %3, %11\n\t"
+          "ds_read_b128 %4, %10 offset:2048\n\t"
+          "ds_read_b128 %5, %11 offset:2048\n\t"
+          "ds_read_b32 %6, %12\n\t"
+          "ds_read_b32 %7, %12 offset:64\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(wl), "=&v"(wh), "=&v"(al[0]), "=&v"(ah[0]), "=&v"(al[1]), "=&v"(ah[1]), "=&v"(sa[0]), "=&v"(sa[1])
+          : "v"(w0), "v"(w1), "v"(a0), "v"(a1), "v"(sp)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %14\n\t"
+          "ds_read_b128 %1, %15\n\t"
+          "ds_read_b128 %2, %16\n\t"
+          "ds_read_b128 %3, %17\n\t"
+          "ds_read_b128 %4, %16 offset:2048\n\t"
+          "ds_read_b128 %5, %17 offset:2048\n\t"
+          "ds_read_b128 %6, %16 offset:4096\n\t"
+          "ds_read_b128 %7, %17 offset:4096\n\t"
+          "ds_read_b128 %8, %16 offset:6144\n\t"
+          "ds_read_b128 %9, %17 offset:6144\n\t"
+          "ds_read_b32 %10, %18\n\t"
+          "ds_read_b32 %11, %18 offset:64\n\t"
+          "ds_read_b32 %12, %18 offset:128\n\t"
+          "ds_read_b32 %13, %18 offset:192\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(wl), "=&v"(wh), "=&v"(al[0]), "=&v"(ah[0]), "=&v"(al[1]), "=&v"(ah[1]), "=&v"(al[2]),
+            "=&v"(ah[2]), "=&v"(al[3]), "=&v"(ah[3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3])
+          : "v"(w0), "v"(w1), "v"(a0), "v"(a1), "v"(sp)
+          : "memory");
+    }
+    v8i wf;
+    wf[0] = wl[0]; wf[1] = wl[1]; wf[2] = wl[2]; wf[3] = wl[3];
+    wf[4] = wh[0]; wf[5] = wh[1]; wf[6] = wh[2]; wf[7] = wh[3];
+    const float sw = sws[kk];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      v8i bf;
+      bf[0] = al[j][0]; bf[1] = al[j][1]; bf[2] = al[j][2]; bf[3] = al[j][3];
+      bf[4] = ah[j][0]; bf[5] = ah[j][1]; bf[6] = ah[j][2]; bf[7] = ah[j][3];
+      acc[j] += mfma_e4m3_16x16x128(wf, bf) * (sa[j] * sw);
+    }
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) issue(min(i, nk - 1), stage(i));
+    for (int kk = 0; kk < nk; kk += D) {
+#pragma unroll
+      for (int i = 0; i < D; ++i)
+        if (kk + i < nk) step(kk + i, stage(i), stage((i + D - 1) % D));
+    }
+  }
+  // the clamped copies past the slice must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+
+  const int64_t n = n0 + 16 * wave + 4 * g;
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int64_t m = 16 * j + r;
+    if (m < M) {
+      if (S == 1) store4<OUT>(p.y, p.ldy, m, n, acc[j]);
+      else gstore<v4f>(ws + ((int64_t)split * M + m) * N + n, acc[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // M <= 16: one workgroup per 16 weight rows and the whole K, its WK waves splitting the K-blocks
 // (contiguous slices) and adding their 16x16 partial tiles through LDS in wave order.  No
 // workspace, one launch; the activation fragments come straight from L2 (the whole activation
@@ -399,26 +451,27 @@ int small_waves(int64_t N, int64_t K) {
 // weights from this size on take the LDS-ring kernel for M <= 16
 constexpr int64_t kRingMinWeightBytes = 48ll << 20;
 
-int mtiles(int64_t M) { return M <= 32 ? 2 : 4; }  // split-K kernel: 16 < M <= 64
+constexpr int MID_D = 4;  // LDS stages of the 16 < M <= 64 kernel (measured: 4 >= 5, 6)
 
-int kb_per_wg(int64_t M, int64_t N, int64_t K) {
+// K-blocks per workgroup of the 16 < M <= 64 kernel.  One slice when the weight blocks alone give
+// 160 or more workgroups; otherwise slices for about 224 workgroups (one per CU, most of the
+// 256), each at least 8 blocks long (shorter slices spend their time filling the ring and their
+// partials cost more than the extra CUs bring; measured on the decode shapes).
+int mid_kpw(int64_t N, int64_t K) {
   const int KB = (int)(K / 128);
-  const int64_t waves_per_split = N / 16;
-  const int64_t target = 2048;  // waves streaming W
-  int S = (int)((target + waves_per_split - 1) / waves_per_split);
-  S = S < 1 ? 1 : (S > KB ? KB : S);
-  int kpw = (KB + S - 1) / S;
-  const int lds_cap = LDS_LIMIT / lds_bytes_per_kb(mtiles(M));
-  if (kpw > lds_cap) kpw = lds_cap;
-  return kpw;
+  const int64_t wgs = N / 128;
+  int S = wgs >= 160 ? 1 : (int)((224 + wgs - 1) / wgs);
+  const int smax = KB / 8 > 1 ? KB / 8 : 1;
+  S = S > smax ? smax : S;
+  return (KB + S - 1) / S;
 }
 
 }  // namespace
 
 int decode_splits(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16) return 1;  // the small-M kernel needs no workspace
+  if (M <= 16) return 1;  // the small-M kernels need no workspace
   const int KB = (int)(K / 128);
-  const int kpw = kb_per_wg(M, N, K);
+  const int kpw = mid_kpw(N, K);
   return (KB + kpw - 1) / kpw;
 }
 
@@ -473,35 +526,35 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
 #undef FGB_SMALL
     return hipGetLastError();
   }
-  const int kpw = kb_per_wg(a.M, a.N, a.K);
-  const int S = decode_splits(a.M, a.N, a.K);
-  const int MT = mtiles(a.M);
-  const size_t lds = (size_t)lds_bytes_per_kb(MT) * kpw;
-  const dim3 grid((unsigned)((a.N / ROWS_PER_WG) * S)), block(THREADS);
-  float* ws = reinterpret_cast<float*>(workspace);
-#define FGB_DEC(MT_, SWF, OUT) \
-  hipLaunchKernelGGL((gemm_decode_kernel<MT_, SWF, OUT>), grid, block, lds, stream, a, kpw, S, ws)
-#define FGB_DEC_MT(SWF, OUT)                 \
-  do {                                       \
-    if (MT == 2) FGB_DEC(2, SWF, OUT);       \
-    else FGB_DEC(4, SWF, OUT);               \
+  {
+    const int kpw = mid_kpw(a.N, a.K);
+    const int S = decode_splits(a.M, a.N, a.K);
+    const dim3 grid((unsigned)((a.N / 128) * S)), block(512);
+    float* ws = reinterpret_cast<float*>(workspace);
+#define FGB_MID(MT_, SWF, OUT) \
+  hipLaunchKernelGGL((gemm_decode_mid_kernel<MT_, MID_D, SWF, OUT>), grid, block, 0, stream, a, kpw, S, ws)
+#define FGB_MID_MT(SWF, OUT)                     \
+  do {                                           \
+    if (a.M <= 32) FGB_MID(2, SWF, OUT);         \
+    else FGB_MID(4, SWF, OUT);                   \
   } while (0)
-  if (a.s_w_fmt == 0) {
-    if (a.y_dtype == 0) FGB_DEC_MT(0, 0); else FGB_DEC_MT(0, 1);
-  } else {
-    if (a.y_dtype == 0) FGB_DEC_MT(1, 0); else FGB_DEC_MT(1, 1);
+    if (a.s_w_fmt == 0) {
+      if (a.y_dtype == 0) FGB_MID_MT(0, 0); else FGB_MID_MT(0, 1);
+    } else {
+      if (a.y_dtype == 0) FGB_MID_MT(1, 0); else FGB_MID_MT(1, 1);
+    }
+#undef FGB_MID_MT
+#undef FGB_MID
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || S == 1) return err;
+    const int64_t total = a.M * (a.N / 4);
+    const dim3 rgrid((unsigned)((total + 255) / 256));
+    if (a.y_dtype == 0)
+      hipLaunchKernelGGL(splitk_reduce_kernel<0>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
+    else
+      hipLaunchKernelGGL(splitk_reduce_kernel<1>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
+    return hipGetLastError();
   }
-#undef FGB_DEC_MT
-#undef FGB_DEC
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || S == 1) return err;
-  const int64_t total = a.M * (a.N / 4);
-  const dim3 rgrid((unsigned)((total + 255) / 256));
-  if (a.y_dtype == 0)
-    hipLaunchKernelGGL(splitk_reduce_kernel<0>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
-  else
-    hipLaunchKernelGGL(splitk_reduce_kernel<1>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
-  return hipGetLastError();
 }
 
 }  // namespace fgb

@@ -106,8 +106,9 @@ size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   s_w   [N/128, K/128] row-major, float32 or UE8M0 bytes per s_w_fmt;
  *   y     [M, ldy] row-major, bf16 bit patterns or float32 per y_dtype.
  * Size limits (FGB_ERR_SHAPE otherwise): K <= 32768; M*lda, N*K and (K/128)*ld_sa*4 below 2^32.
- * M <= 64 selects the split-K streaming path; it needs `workspace` of
- * fgb_gemm_workspace_bytes(M, N, K) bytes (float32 partial sums; contents on entry ignored).
+ * M <= 64 selects the decode (weight-streaming) kernels; for 16 < M <= 64 they may slice K and
+ * then need `workspace` of fgb_gemm_workspace_bytes(M, N, K) bytes (float32 partial sums;
+ * contents on entry ignored; 0 bytes when the shape is not sliced).
  */
 int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
                         const uint8_t* w_q, const void* s_w, int s_w_fmt,

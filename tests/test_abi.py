@@ -84,7 +84,7 @@ def test_gemm_validation(L):
     assert _gemm(L, a_q=FAKE + 8) == ERR["ALIGN"]
     assert _gemm(L, lda=1032) == ERR["ALIGN"]
     assert _gemm(L, ld_sa=258) == ERR["ALIGN"]
-    # the split-K decode path (16 < M <= 64) needs a workspace; M <= 16 and prefill do not
+    # the decode path for 16 < M <= 64 needs a workspace when it slices K; M <= 16 and prefill do not
     need = L.fgb_gemm_workspace_bytes(32, 4096, 4096)
     assert need > 0
     assert _gemm(L, M=32, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=32) == ERR["WORKSPACE"]
@@ -92,6 +92,8 @@ def test_gemm_validation(L):
     assert L.fgb_gemm_workspace_bytes(16, 4096, 4096) == 0
     assert L.fgb_gemm_workspace_bytes(1, 4096, 4096) == 0
     assert L.fgb_gemm_workspace_bytes(128, 4096, 4096) == 0
+    # unsliced 16 < M <= 64 shapes (224 workgroups of 128 weight rows) need none either
+    assert L.fgb_gemm_workspace_bytes(64, 28672, 4096) == 0
 
 
 @pytest.mark.skipif(_has_gpu(), reason="fake pointers must not reach a real device")

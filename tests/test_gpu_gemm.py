@@ -1,4 +1,4 @@
-"""GPU parity: w8a8_block_gemm (prefill and split-K decode paths) against the oracle.
+"""GPU parity: w8a8_block_gemm (prefill and decode paths) against the oracle.
 
 Operands are quantized by the oracle on the CPU and uploaded, so these tests isolate the GEMM;
 the end-to-end tests quantize on the GPU and compare with the oracle run from the same bf16
@@ -129,7 +129,7 @@ def test_rejects_bad_shapes(dev):
 
 
 def test_decode_workspace_reuse_across_shapes(dev):
-    """One workspace buffer serves a sequence of split-K calls of different shapes (its contents
+    """One workspace buffer serves a sequence of K-sliced decode calls of different shapes (its contents
     on entry do not matter)."""
     shapes = [(64, 4096, 4096), (1, 1024, 2048), (33, 4096, 4096), (8, 1536, 14336), (1, 4096, 4096)]
     need = max(fgb.gemm_workspace_bytes(*s) for s in shapes)
@@ -180,3 +180,28 @@ def test_decode_large_weight_ring_kernel(dev, M, fmt):
     check_t1(y32, yref)
     y16 = _run((aq, sa, wq, sw), dev, torch.bfloat16)
     check_t2(bf16_tensor_to_f64(y16), yref)
+
+
+@pytest.mark.parametrize("M", [17, 32, 33, 48, 64])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_decode_mid_rows_kernel(dev, M, fmt):
+    """16 < M <= 64 (the streaming decode kernel with an LDS ring shared by a workgroup's waves):
+    a K slicing with a ragged last slice shorter than the ring (N = 1024, K = 3200: 25 K-blocks in
+    slices of 3), a single slice of two blocks (N = 16384, K = 256), and one of 12 blocks; random
+    finite codes and scales, float32 and bf16 outputs."""
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    for (N, K) in [(1024, 3200), (16384, 256), (2048, 1536)]:
+        rng = np.random.default_rng(3000 + M + N)
+        wq = rng.choice(finite, size=(N, K))
+        if fmt == "f32":
+            sw = (rng.uniform(0.25, 4.0, size=(N // 128, K // 128)) / 448).astype(np.float32)
+        else:
+            sw = rng.integers(112, 124, size=(N // 128, K // 128), dtype=np.uint8)
+        aq = rng.choice(finite, size=(M, K))
+        sa = (rng.uniform(0.25, 4.0, size=(M, K // 128)) / 448).astype(np.float32)
+        yref = gemm.gemm_ref_fast(aq, sa, wq, sw, fmt)
+        y32 = _run((aq, sa, wq, sw), dev, torch.float32).cpu().numpy()
+        check_t1(y32, yref)
+        y16 = _run((aq, sa, wq, sw), dev, torch.bfloat16)
+        check_t2(bf16_tensor_to_f64(y16), yref)
