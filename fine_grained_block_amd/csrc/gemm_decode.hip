@@ -392,7 +392,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
   const int64_t swbase = nb * KB + kb0;
 
   int4 wv[2][CHS][2], av[2][CHS][2];
-  float sav[2][CHS];
+  float sav[2][CHS], swv[2][CHS];
   auto load_chunk = [&](int c, int buf) {
 #pragma unroll
     for (int u = 0; u < CHS; ++u) {
@@ -403,6 +403,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
         av[buf][u][0] = gload_i4(arow + off);
         av[buf][u][1] = gload_i4(arow + off + 16);
         sav[buf][u] = gload<float>(sarow + (int64_t)(c + u) * p.ld_sa);
+        swv[buf][u] = load_sw<SWF>(p.s_w, swbase + c + u);
       }
     }
   };
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
         af[4] = wv[buf][u][1].x; af[5] = wv[buf][u][1].y; af[6] = wv[buf][u][1].z; af[7] = wv[buf][u][1].w;
         bf[0] = av[buf][u][0].x; bf[1] = av[buf][u][0].y; bf[2] = av[buf][u][0].z; bf[3] = av[buf][u][0].w;
         bf[4] = av[buf][u][1].x; bf[5] = av[buf][u][1].y; bf[6] = av[buf][u][1].z; bf[7] = av[buf][u][1].w;
-        const float sc = sav[buf][u] * load_sw<SWF>(p.s_w, swbase + c + u);
+        const float sc = sav[buf][u] * swv[buf][u];
         acc += mfma_e4m3_16x16x128(af, bf) * sc;
       }
     }
