@@ -205,3 +205,49 @@ def test_decode_mid_rows_kernel(dev, M, fmt):
         check_t1(y32, yref)
         y16 = _run((aq, sa, wq, sw), dev, torch.bfloat16)
         check_t2(bf16_tensor_to_f64(y16), yref)
+
+
+def test_repeated_runs_are_bitwise_identical(dev):
+    """Every path sums in a fixed order, so repeated runs must agree bit for bit; a race between
+    the LDS copies and the reads of a stage (or between workgroups) would show up as run-to-run
+    differences.  Each shape runs six times with the caches flushed before every other run:
+    256x256 and 256x128 prefill tiles, the 128x128 tile (N % 256 != 0), the decode ring kernel
+    (M <= 16, 48 MiB of weights), the 16 < M <= 64 kernel with a K slicing and its reduction, and
+    the grouped GEMM."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+
+    def codes(shape):
+        c = torch.randint(0, 256, shape, generator=gen, device=dev, dtype=torch.int32).to(torch.uint8)
+        return torch.where((c & 0x7F) == 0x7F, c ^ 1, c)  # finite E4M3 codes only
+
+    def scales(shape):
+        return torch.rand(shape, generator=gen, device=dev) * (2.0 / 448) + 0.25 / 448
+
+    cases = [(4096, 4096, 2048), (4096, 6144, 4096), (1024, 1152, 1024), (8, 2048, 24576), (48, 1024, 3200)]
+    for (M, N, K) in cases:
+        aq, sa = codes((M, K)), scales((K // 128, M))
+        wq, sw = codes((N, K)), scales((N // 128, K // 128))
+        outs = []
+        for i in range(6):
+            if i % 2:
+                flush.fill_(1)
+            outs.append(fgb.gemm(aq, sa, wq, sw, out_dtype=torch.float32))
+        torch.cuda.synchronize()
+        for o in outs[1:]:
+            assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32)), (M, N, K)
+    E, N, K = 8, 1024, 2048
+    counts = [700, 0, 1, 255, 256, 257, 1500, 63]  # 3032 rows: the scale rows stay 16-byte aligned
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=dev)
+    T = int(sum(counts))
+    aq, sa = codes((T, K)), scales((K // 128, T))
+    wq, sw = codes((E, N, K)), scales((E, N // 128, K // 128))
+    outs = []
+    for i in range(6):
+        if i % 2:
+            flush.fill_(1)
+        outs.append(fgb.grouped_gemm(aq, sa, wq, sw, offsets, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32)), "grouped"
