@@ -4,11 +4,12 @@
 // (Transformers "Fine-grained FP8", "DeepGEMM fast path"; grouped: the expert matmuls of the
 // same section and of "UE8M0 scale format").
 //
-// Workgroup: 512 threads (8 waves, 2 per SIMD) computing a BN x BM tile of y^T (BN output
-// features x BM tokens).  Per K-block the W and A tiles (BN x 128 and BM x 128 bytes) are
-// copied HBM/L2 -> LDS by the direct-to-LDS loads (buffer_load_dwordx4 ... lds: no VGPR staging),
-// together with the tile's activation scales, STAGES deep (three for 256 x 128 tiles, two for 256 x 256): while block kb is multiplied out of
-// one stage, the copies of the next blocks land in the others.
+// Workgroup: 8 waves, 2 per SIMD (the 128 x 128 tile: 4 waves, 2 workgroups per CU), computing a
+// BN x BM tile of y^T (BN output features x BM tokens).  Per K-block the W and A tiles (BN x 128
+// and BM x 128 bytes) and the tile's activation scales are copied HBM/L2 -> LDS by direct-to-LDS
+// loads (buffer_load_dwordx4 ... lds: no VGPR staging), STAGES deep (three for 256 x 128 tiles,
+// two for 256 x 256 and 128 x 128): while block kb is multiplied out of one stage, the copies of
+// the next blocks land in the others.
 // Each stage is its own __shared__ array so the compiler can tell the in-flight copies from the
 // LDS reads of the current stage and does not wait for them.
 //
@@ -31,9 +32,9 @@ namespace fgb {
 namespace {
 
 constexpr int KBYTES = 128;  // one K-block of E4M3 codes per row
-// Waves with four token tiles issue the copies of the next block spread over the first MFMAs of
-// the current one, one every SPACING MFMAs, rather than in a burst after the barrier (+2-5% on
-// the 256 x 256 tiles; later issue leaves the copies too little time).
+// The copies of the next block are issued spread over the first MFMAs of the current one, one
+// every SPACING MFMAs, rather than in a burst after the barrier (+2-5% on the 256 x 256 tiles;
+// later issue leaves the copies too little time).
 constexpr int SPACING = 2;
 
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
@@ -58,6 +59,7 @@ struct Cfg {
   static_assert(SA_LD <= WAVES, "one activation-scale copy per wave at most");
   static_assert(W_LD >= 1 && A_LD >= 1, "every wave loads whole 8-row groups");
   static_assert((BN / WN) % 128 == 0 || 128 % (BN / WN) == 0, "a wave's rows stay in one weight block");
+  static_assert(TM >= 4, "four or more token tiles per wave: the scale-FMAs run one W fragment behind");
 };
 
 // s_waitcnt immediate that waits until at most N vector-memory operations are outstanding
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // direct-load sources: lane i of 8-row group q fetches row 8q + i/8, chunk (i%8) ^ g(row)
   const int lrow = lane >> 3;
   // 32-bit per-lane byte offsets from workgroup-uniform bases (the library checks that every
-  // operand fits in 4 GiB), so the copies use the scalar-base addressing form
+  // operand fits in 4 GiB): the base sits in the buffer descriptor, the offset in one VGPR
   uint32_t woff[C::W_LD], aoff[C::A_LD];
   const uint8_t* wbase = wq + n0 * K;
   const uint8_t* abase = p.a_q;
@@ -201,8 +203,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // count LDS reads and waits for all of them (lgkmcnt(0)) wherever it needs one; with buffer
   // loads it waits only for the reads the next instruction uses.  32-bit offsets; the range check
   // is off (num_records = 2^32 - 1): the library validated every operand's extent.
-  // copy d of block kb: 0 = the activation scales, then the W_LD weight and the
-  // A_LD activation 8-row groups
+  // Copy d of block kb into stage st: 0 = the activation scales, then the W_LD weight and the
+  // A_LD activation 8-row groups.
   constexpr int NPART = 1 + C::W_LD + C::A_LD;
   auto issue_part = [&](int kb, uint8_t* st, float* sas, int d) {
 #if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
@@ -223,21 +225,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 #endif
   };
   auto issue = [&](int kb, uint8_t* st, float* sas) {
-#if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
-    const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, -1, 0x00020000);
-    const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, -1, 0x00020000);
-    const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.s_a, 0, -1, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * sa_grp), 4, saoff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
-    const uint32_t koff = (uint32_t)kb * KBYTES;
 #pragma unroll
-    for (int i = 0; i < C::W_LD; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, woff[i],
-                                               koff, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + C::W_BYTES + (wave + i * C::WAVES) * 8 * KBYTES), 16,
-                                               aoff[i], koff, 0, 0);
-#endif
+    for (int d = 0; d < NPART; ++d) issue_part(kb, st, sas, d);
   };
 
   // this lane's tokens within the tile (one per m-tile)
@@ -266,13 +255,13 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // One K-block of the wave's sub-tile: one MFMA per 16x16 tile gives the partial P, then
   // acc += P * (s_a * s_w).  The MFMAs, the scale-FMAs and the fragment reads are interleaved so
   // that matrix core, VALU and LDS work overlap instead of waiting on each other.
-  // (the copies of block kb_next are issued spread over the MFMAs when SPACING > 0)
+  // The copies of block kb_next go out spread over the first MFMAs, one every SPACING.
   auto compute = [&](const uint8_t* st, const float* sas_cur, const float* swp, int kb_next, uint8_t* refill,
                      float* sas_refill) {
     const uint8_t* ws = st + wn * (C::BN / C::WN) * KBYTES;
     const uint8_t* as = st + C::W_BYTES + wm * (C::BM / C::WM) * KBYTES;
     float sc[C::TM];
-    if constexpr (C::TM >= 4) {
+    {
       // LDS reads in the order of first use (they complete in order, so a wait covers only what
       // the next MFMA needs): the first W fragment and the A fragments, then W fragment i+1 with
       // the first MFMA of W fragment i, the scales with the second MFMA.
@@ -291,7 +280,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       v4f P[LAG + 1];
 #pragma unroll
       for (int t = 0; t < T + LAG; ++t) {
-        if constexpr (SPACING > 0) {
+        {
           // every copy issued within the loop (T + LAG iterations)
           constexpr int SP = (NPART - 1) * SPACING < T + LAG ? SPACING : (T + LAG - 1) / (NPART - 1);
           static_assert(SP >= 1 && (NPART - 1) * SP < T + LAG, "copies fit the MFMA sequence");
@@ -318,30 +307,6 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-      // fewer token tiles per wave: all of the block's A fragments first, two P buffers (the
-      // scale-FMAs of W fragment i-1 follow the MFMAs of fragment i)
-      const float swv = *swp;
-#pragma unroll
-      for (int j = 0; j < C::TM; ++j) sc[j] = sas_cur[tok[j]] * swv;
-      v8i bf[C::TM];
-#pragma unroll
-      for (int j = 0; j < C::TM; ++j) bf[j] = lds_frag(as, j * 16, lane);
-      v8i af[2];
-      af[0] = lds_frag(ws, 0, lane);
-      v4f P[2][C::TM];
-#pragma unroll
-      for (int i = 0; i <= C::TN; ++i) {
-        if (i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
-        if (i < C::TN) {
-#pragma unroll
-          for (int j = 0; j < C::TM; ++j) P[i & 1][j] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
-        }
-        if (i > 0) {
-#pragma unroll
-          for (int j = 0; j < C::TM; ++j) acc[i - 1][j] += P[(i - 1) & 1][j] * sc[j];
-        }
-      }
     }
   };
 
@@ -355,7 +320,6 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<C::STAGES == 3 ? C::NDMA : 0>());
     wg_barrier();
     const int kb_next = min(kb + C::STAGES - 1, KB - 1);
-    if (!(SPACING > 0 && C::TM >= 4)) issue(kb_next, refill, sas_refill);
     compute(cur, sas_cur, sw_lds + kb, kb_next, refill, sas_refill);
   };
 
