@@ -75,6 +75,13 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Barrier after LDS writes that other waves read next: LDS operations of different waves may be
+// served out of order, so the wave's own writes are waited for first.
+__device__ __forceinline__ void wg_barrier_after_lds_writes() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0), vmcnt and expcnt at their maxima
+  wg_barrier();
+}
+
 __host__ __device__ constexpr int swz_g(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * KBYTES + ((chunk ^ swz_g(row)) << 4); }
 
@@ -369,14 +376,15 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
           }
         }
       }
-      wg_barrier();
+      wg_barrier_after_lds_writes();
       for (int c = tid; c < 128 * CPR; c += C::THREADS) {
         const int mr = c / CPR, ch = c - mr * CPR;
         const int64_t m = row0 + r * 128 + mr;
         if (m < row_end) {
           const uint8_t* half = mr < 64 ? stage0 : stage1;
           const v4i v = *reinterpret_cast<const v4i*>(half + (mr & 63) * ROWB + ch * 16);
-          gstore<v4i>(reinterpret_cast<uint16_t*>(p.y) + m * p.ldy + n0 + ch * 8, v);
+          // non-temporal: the output streams past the last-level cache, which keeps the operands
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(p.y) + m * p.ldy + n0 + ch * 8));
         }
       }
     }
@@ -394,6 +402,264 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Persistent variant for 256 x 256 tiles when a launch has several tiles per CU (dense, two
+// stages, an even number of K-blocks): one workgroup per CU walks its tiles (in the order the
+// one-tile-per-workgroup launch runs them), and the work between two tiles is overlapped:
+//   * the next tile's first block and its weight-block scales are copied during the current
+//     tile's last step, into the stage that step frees;
+//   * the output tile is staged through the other stage (free after the last step) in two
+//     rounds of 128 token rows, rows swizzled instead of padded (chunk c of row m at c ^ (m & 15));
+//   * the stores are range-checked buffer stores (rows past M are dropped by the hardware), so
+//     every thread issues the same number of them and the next tile's first wait can leave
+//     exactly those in flight.
+// Per step, the copies and the schedule are those of gemm_prefill_kernel.
+// ---------------------------------------------------------------------------------------------
+template <typename C, int SWF>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(GemmArgs p, int tiles_m,
+                                                                                  int tiles_n) {
+  static_assert(C::STAGES == 2 && C::BM == 256 && C::BN == 256 && C::WN == 2, "two-stage 256 x 256 tiles");
+  static_assert(SWF == 0, "float32 weight-block scales (copied as whole dwords)");
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) float sas0[C::BM];
+  __shared__ __attribute__((aligned(16))) float sas1[C::BM];
+  // weight-block scales of a tile's two block rows, by tile parity
+  __shared__ __attribute__((aligned(16))) float swr0[2 * 256];
+  __shared__ __attribute__((aligned(16))) float swr1[2 * 256];
+
+  const int ntiles = tiles_m * tiles_n;
+  const int64_t K = p.K, M = p.M;
+  const int KB = (int)(K / KBYTES);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  const int lrow = lane >> 3;
+  const int GROUP_M = p.K <= 16 * KBYTES ? 4 : 8;
+  const int sw_q = wave % 8;  // this wave's scale copy: block row sw_q / 4, K-blocks 64 (sw_q % 4) + lane
+
+  // A tile is two uniform values; its copies address through buffer descriptors based at the
+  // tile, so the per-lane offsets below are the same for every tile.  Activation rows past M fall
+  // outside the descriptors' ranges: their copies are dropped (the rows feed only output rows
+  // that are never stored).
+  struct Tile {
+    int64_t row0, n0;
+  };
+  auto make_tile = [&](int v) {
+    Tile t;
+    const int pid = xcd_remap(v, ntiles);
+    const int in_group = GROUP_M * tiles_n;
+    const int first_m = (pid / in_group) * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    t.row0 = (int64_t)(first_m + (pid % in_group) % gsize) * C::BM;
+    t.n0 = (int64_t)((pid % in_group) / gsize) * C::BN;
+    return t;
+  };
+  uint32_t woff[C::W_LD], aoff[C::A_LD];
+#pragma unroll
+  for (int i = 0; i < C::W_LD; ++i) {
+    const int r = 8 * (wave + i * C::WAVES) + lrow;
+    woff[i] = (uint32_t)(r * K + (((lane & 7) ^ swz_g(r)) * 16));
+  }
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) {
+    const int r = 8 * (wave + i * C::WAVES) + lrow;
+    aoff[i] = (uint32_t)(r * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
+  }
+  const uint32_t saoff = (uint32_t)((64 * (wave % C::SA_LD) + lane) * 4);
+  const uint32_t swoff = (uint32_t)(((sw_q >> 2) * KB + min(64 * (sw_q & 3) + lane, KB - 1)) * 4);
+
+  // Copy d of block kb of tile t into stage st: 0 the activation scales, then the weight and
+  // activation 8-row groups, and last the weight-block scales of tile ts into swr (every step
+  // issues it; the copy for the next tile lands in the buffer the current tile does not read).
+  constexpr int NPART = 2 + C::W_LD + C::A_LD;
+  auto issue_part = [&](const Tile t, int kb, uint8_t* st, float* sas, const Tile ts, float* swr, int d) {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
+    const uint32_t koff = (uint32_t)kb * KBYTES;
+    const uint32_t rows = (uint32_t)(M - t.row0);
+    if (d == 0) {
+      // (the K-block goes into the base: the range check then covers exactly the tile's rows)
+      const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.s_a + (int64_t)kb * p.ld_sa + t.row0), 0, (int)(rows * 4), 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * (wave % C::SA_LD)), 4, saoff, 0, 0, 0);
+    } else if (d <= C::W_LD) {
+      const __amdgpu_buffer_rsrc_t w_rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_q + t.n0 * K), 0, -1, 0x00020000);
+      const int i = d - 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, woff[i],
+                                               koff, 0, 0);
+    } else if (d <= C::W_LD + C::A_LD) {
+      const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.a_q + t.row0 * p.lda), 0, (int)(uint32_t)(rows * (uint64_t)p.lda), 0x00020000);
+      const int i = d - 1 - C::W_LD;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + C::W_BYTES + (wave + i * C::WAVES) * 8 * KBYTES), 16,
+                                               aoff[i], koff, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t sw_rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)((const float*)p.s_w + (ts.n0 / 128) * KB), 0, -1, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sw_rs, LPTR(swr + sw_q * 64), 4, swoff, 0, 0, 0);
+    }
+#endif
+  };
+
+  int tok[C::TM];
+#pragma unroll
+  for (int j = 0; j < C::TM; ++j) tok[j] = wm * (C::BM / C::WM) + j * 16 + (lane & 15);
+  const int sw_b = wn;  // this wave's weight block row within the tile (128 rows per wave)
+
+  v4f acc[C::TN][C::TM];
+
+  // One K-block (the schedule of gemm_prefill_kernel); the copies of block kn of tile tn and the
+  // weight-block scales of tile ts go out spread over the first MFMAs.
+  auto compute = [&](const uint8_t* st, const float* sas_cur, const float* swr_cur, int kb, const Tile tn, int kn,
+                     uint8_t* refill, float* sas_refill, const Tile ts, float* swr_next) {
+    const uint8_t* ws = st + wn * (C::BN / C::WN) * KBYTES;
+    const uint8_t* as = st + C::W_BYTES + wm * (C::BM / C::WM) * KBYTES;
+    float sc[C::TM];
+    v8i af[2], bf[C::TM];
+    af[0] = lds_frag(ws, 0, lane);
+#pragma unroll
+    for (int j = 0; j < C::TM; ++j) bf[j] = lds_frag(as, j * 16, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    float sav[C::TM], swv = 0.0f;
+    constexpr int LAG = C::TM;
+    constexpr int T = C::TN * C::TM;
+    v4f P[LAG + 1];
+#pragma unroll
+    for (int t = 0; t < T + LAG; ++t) {
+      {
+        constexpr int SP = (NPART - 1) * SPACING < T + LAG ? SPACING : (T + LAG - 1) / (NPART - 1);
+        static_assert(SP >= 1 && (NPART - 1) * SP < T + LAG, "copies fit the MFMA sequence");
+        if (t % SP == 0 && t / SP < NPART) issue_part(tn, kn, refill, sas_refill, ts, swr_next, t / SP);
+      }
+      if (t < T) {
+        const int i = t / C::TM, j = t % C::TM;
+        P[t % (LAG + 1)] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
+        if (j == 0 && i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
+        if (t == 1) {
+#pragma unroll
+          for (int jj = 0; jj < C::TM; ++jj) sav[jj] = sas_cur[tok[jj]];
+          swv = swr_cur[sw_b * 256 + kb];
+        }
+      }
+      if (t == LAG) {
+#pragma unroll
+        for (int j = 0; j < C::TM; ++j) sc[j] = sav[j] * swv;
+      }
+      if (t >= LAG) {
+        const int u = t - LAG;
+        acc[u / C::TM][u % C::TM] += P[u % (LAG + 1)] * sc[u % C::TM];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // output: y rows past M are out of the descriptor's range and dropped
+  constexpr int ROW = C::BN * 2, CPR = ROW / 16;
+  constexpr int NSTORE = C::BM * CPR / C::THREADS;  // stores per thread per tile
+  auto epilogue = [&](const Tile& t) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // the thread index passes through an empty asm so that the addresses below are computed here
+    // for each tile rather than hoisted out of the tile loop (where they would be spilled)
+    int et = tid;
+    asm volatile("" : "+v"(et));
+    const int el = et & 63;
+    const __amdgpu_buffer_rsrc_t y_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((uint8_t*)p.y + (t.row0 * p.ldy + t.n0) * 2), 0, (int)(uint32_t)((M - t.row0) * p.ldy * 2), 0x00020000);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      wg_barrier();  // the previous round's reads (and, for r = 0, the last block's) are done
+      if (wm / 2 == r) {
+#pragma unroll
+        for (int j = 0; j < C::TM; ++j) {
+          const int mh = (wm % 2) * 64 + j * 16 + (el & 15);
+#pragma unroll
+          for (int i = 0; i < C::TN; ++i) {
+            const int nl = wn * 128 + i * 16 + 4 * (el >> 4);
+            uint2 w;
+            w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][0]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][1]) << 16);
+            w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][2]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][3]) << 16);
+            *reinterpret_cast<uint2*>(stage1 + mh * ROW + (((nl >> 3) ^ (mh & 15)) << 4) + ((nl & 4) << 1)) = w;
+          }
+        }
+      }
+      wg_barrier_after_lds_writes();
+#pragma unroll
+      for (int u = 0; u < NSTORE / 2; ++u) {
+        const int c = et + u * C::THREADS;
+        const int mh = c / CPR, ch = c - mh * CPR;
+        const v4i v = *reinterpret_cast<const v4i*>(stage1 + mh * ROW + ((ch ^ (mh & 15)) << 4));
+        const uint32_t off = (uint32_t)(((r * 128 + mh) * p.ldy + ch * 8) * 2);
+        __builtin_amdgcn_raw_buffer_store_b128(v, y_rs, off, 0, 2);  // 2: non-temporal, as above
+      }
+    }
+#endif
+  };
+
+  // Every step waits for all of its wave's copies except at a tile's first step, which leaves the
+  // previous tile's NSTORE output stores (issued after the copies it needs) in flight.  The
+  // prologue's copies are waited for before the loop, so that the compiler's view of what is in
+  // flight at the loop head is that of the loop's back edge.
+  const int G = (int)gridDim.x;
+  int v = (int)blockIdx.x;
+  Tile tc = make_tile(v);
+#pragma unroll
+  for (int d = 0; d < NPART; ++d) issue_part(tc, 0, stage0, sas0, tc, swr0, d);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  // One tile; the scale buffers alternate by tile and are named directly (the unrolled pair of
+  // calls below), so that the compiler's LDS alias tracking keeps the reads of one free of waits
+  // for the copies into the other.
+  auto run_tile = [&](const Tile tc, const Tile tn, const float* swr_cur, float* swr_nxt) {
+#pragma unroll
+    for (int i = 0; i < C::TN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // blocks 0 and 1
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<NSTORE>());
+    wg_barrier();
+    compute(stage0, sas0, swr_cur, 0, tc, 1, stage1, sas1, tn, swr_nxt);
+    {
+      const bool last = KB == 2;
+      const Tile tt = last ? tn : tc;
+      const int kn = last ? 0 : 2;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+      wg_barrier();
+      compute(stage1, sas1, swr_cur, 1, tt, kn, stage0, sas0, tn, swr_nxt);
+    }
+    // blocks 2 .. KB-1; the last step copies the next tile's block 0
+    for (int kb = 2; kb < KB; kb += 2) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+      wg_barrier();
+      compute(stage0, sas0, swr_cur, kb, tc, kb + 1, stage1, sas1, tn, swr_nxt);
+      const bool last = kb + 2 >= KB;
+      const Tile tt = last ? tn : tc;
+      const int kn = last ? 0 : kb + 2;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+      wg_barrier();
+      compute(stage1, sas1, swr_cur, kb + 1, tt, kn, stage0, sas0, tn, swr_nxt);
+    }
+    epilogue(tc);
+  };
+  // past the last tile the next-tile copies repeat the current tile's (harmless)
+  for (;;) {
+    Tile tn = make_tile(v + G < ntiles ? v + G : v);
+    run_tile(tc, tn, swr0, swr1);
+    v += G;
+    tc = tn;
+    if (v >= ntiles) break;
+    tn = make_tile(v + G < ntiles ? v + G : v);
+    run_tile(tc, tn, swr1, swr0);
+    v += G;
+    tc = tn;
+    if (v >= ntiles) break;
+  }
+  // the clamped copies past the last tile and the stores complete before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
 }
 
 #ifndef FGB_BIG_CFG
@@ -435,6 +701,16 @@ int64_t tiles_for(int64_t M, int64_t N) { return ((M + C::BM - 1) / C::BM) * (N 
 
 double fill(int64_t tiles) { return (double)tiles / (double)(((tiles + 255) / 256) * 256); }
 
+// The persistent form for 256 x 256 tiles with two to four tiles per CU, where it measured 1-6%
+// faster (more per CU measured ~2% slower: the workgroups drift apart over many tiles, unlike the
+// in-order hardware dispatch); an even K-block count of at most 256 (one scale row per wave copy),
+// float32 weight-block scales, bf16 output and 32-bit output offsets.
+bool use_persistent(const GemmArgs& a) {
+  const int64_t KB = a.K / KBYTES, tiles = tiles_for<Big>(a.M, a.N);
+  return tiles > 256 && tiles <= 4 * 256 && KB % 2 == 0 && KB <= 256 && a.s_w_fmt == 0 && a.y_dtype == 0 &&
+         a.M * a.ldy * 2 < (int64_t(1) << 32);
+}
+
 Pick pick_tile(int64_t M, int64_t N, int64_t K) {
   if (N % Big::BN != 0 || N % Half::BN != 0) return Pick::Narrow;
   if (K < 8 * KBYTES) return Pick::Half;
@@ -447,7 +723,14 @@ Pick pick_tile(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
   switch (pick_tile(a.M, a.N, a.K)) {
-    case Pick::Big: return launch_cfg<Big, false>(a, (int)((a.M + Big::BM - 1) / Big::BM), stream);
+    case Pick::Big: {
+      const int tiles_m = (int)((a.M + Big::BM - 1) / Big::BM);
+      if (!use_persistent(a)) return launch_cfg<Big, false>(a, tiles_m, stream);
+      const int tiles_n = (int)(a.N / Big::BN);
+      hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0>), dim3(256), dim3(Big::THREADS), 0, stream, a,
+                         tiles_m, tiles_n);
+      return hipGetLastError();
+    }
     case Pick::Half: return launch_cfg<Half, false>(a, (int)((a.M + Half::BM - 1) / Half::BM), stream);
     default: return launch_cfg<Narrow, false>(a, (int)((a.M + Narrow::BM - 1) / Narrow::BM), stream);
   }

@@ -207,11 +207,32 @@ def test_decode_mid_rows_kernel(dev, M, fmt):
         check_t2(bf16_tensor_to_f64(y16), yref)
 
 
+@pytest.mark.parametrize("M,N,K", [(1000, 32768, 1024), (1700, 16384, 3072), (4096, 8192, 2048), (520, 65536, 1280)])
+def test_persistent_prefill_tiles(dev, M, N, K):
+    """256 x 256 tiles with more tiles than CUs (bf16 output, float32 scales): each workgroup
+    walks several tiles, copying the next tile's first block while it stores the current one.
+    Ragged M, tile counts that are and are not multiples of the grid, 8 to 24 K-blocks.  Every
+    output equals the RNE of the float32-output kernel's (the same sums in the same order), and a
+    sample of rows, including every tile's first and last, matches the oracle."""
+    ops = oracle_operands(M, N, K, key=9)
+    aq, sa, wq, sw = upload(*ops, dev)
+    y16 = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.bfloat16)
+    y32 = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y16 = bf16_tensor_to_f64(y16)
+    assert np.array_equal(y16, gemm.bf16_rne(y32.cpu().numpy().astype(np.float64)))
+    ends = np.arange(0, M, 256)
+    rows = np.unique(np.concatenate([ends, np.minimum(ends + 255, M - 1), [M // 2]]))
+    aq_o, sa_o, wq_o, sw_o = ops
+    check_t2(y16[rows], ref(aq_o[rows], sa_o[rows], wq_o, sw_o))
+
+
 def test_repeated_runs_are_bitwise_identical(dev):
     """Every path sums in a fixed order, so repeated runs must agree bit for bit; a race between
     the LDS copies and the reads of a stage (or between workgroups) would show up as run-to-run
     differences.  Each shape runs six times with the caches flushed before every other run:
-    256x256 and 256x128 prefill tiles, the 128x128 tile (N % 256 != 0), the decode ring kernel
+    256x256 and 256x128 prefill tiles, the persistent 256x256 form (bf16 output, two tiles per
+    workgroup), the 128x128 tile (N % 256 != 0), the decode ring kernel
     (M <= 16, 48 MiB of weights), the 16 < M <= 64 kernel with a K slicing and its reduction, and
     the grouped GEMM."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -237,6 +258,18 @@ def test_repeated_runs_are_bitwise_identical(dev):
         torch.cuda.synchronize()
         for o in outs[1:]:
             assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32)), (M, N, K)
+    # bf16 output with more 256 x 256 tiles than CUs: the persistent form
+    M, N, K = 2048, 16384, 2048
+    aq, sa = codes((M, K)), scales((K // 128, M))
+    wq, sw = codes((N, K)), scales((N // 128, K // 128))
+    outs = []
+    for i in range(6):
+        if i % 2:
+            flush.fill_(1)
+        outs.append(fgb.gemm(aq, sa, wq, sw, out_dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), (M, N, K, "bf16")
     E, N, K = 8, 1024, 2048
     counts = [700, 0, 1, 255, 256, 257, 1500, 63]  # 3032 rows: the scale rows stay 16-byte aligned
     offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=dev)
