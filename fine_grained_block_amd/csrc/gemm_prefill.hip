@@ -108,7 +108,42 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   __shared__ __attribute__((aligned(16))) float sas1[C::BM];
   __shared__ __attribute__((aligned(16))) float sas2[C::STAGES > 2 ? C::BM : 4];
 
-  const int nwg = tiles_m * tiles_n;
+  const int64_t K = p.K, N = p.N;
+  const int KB = (int)(K / KBYTES);
+  const int NBLK = (int)(N / 128);
+
+  // Grouped: tiles are numbered expert by expert, ceil(rows_e / BM) tile-rows each.  The grid is
+  // an upper bound (host side the counts are unknown), so the real tiles are counted first and
+  // split evenly over the XCDs; surplus workgroups exit.  (Numbering over the bound instead left
+  // the padding on the last XCDs: for MoE down one XCD idle and 17.5 waves of tiles instead of
+  // 15.75.)  63 experts per wave pass: lane l holds offsets[e0 + l], the tile-row counts are
+  // prefix-summed across the wave; with at most 63 experts the one pass also finds the expert.
+  const int lane0 = threadIdx.x & 63;
+  auto expert_chunk = [&](int e0, int& off, int& nxt, int& mt, int& inc) {
+    const int idx = e0 + lane0;
+    off = idx <= p.E ? gload<int>(p.offsets + idx) : 0;
+    nxt = __shfl_down(off, 1);
+    mt = lane0 < 63 && idx < p.E ? (nxt - off + C::BM - 1) / C::BM : 0;
+    inc = mt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(inc, d);
+      if (lane0 >= d) inc += t;
+    }
+  };
+  int c_off = 0, c_nxt = 0, c_mt = 0, c_inc = 0;  // the first chunk, kept for the lookup
+  int real_tiles_m = tiles_m;
+  if constexpr (GROUPED) {
+    real_tiles_m = 0;
+    for (int e0 = 0; e0 < p.E; e0 += 63) {
+      int off, nxt, mt, inc;
+      expert_chunk(e0, off, nxt, mt, inc);
+      if (e0 == 0) { c_off = off; c_nxt = nxt; c_mt = mt; c_inc = inc; }
+      real_tiles_m += __shfl(inc, 62);
+    }
+  }
+  const int nwg = real_tiles_m * tiles_n;
+  if (GROUPED && (int)blockIdx.x / 8 >= nwg / 8 + ((int)blockIdx.x % 8 < nwg % 8)) return;
   const int pid = xcd_remap((int)blockIdx.x, nwg);
   // grouped ordering: bands of GROUP_M tile-rows share W tiles in L2 (narrower bands for short K,
   // where a tile's operands are in L2 only briefly)
@@ -116,39 +151,23 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   const int in_group = GROUP_M * tiles_n;
   const int group_id = pid / in_group;
   const int first_m = group_id * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int gsize = min(real_tiles_m - first_m, GROUP_M);
   const int pid_m = first_m + (pid % in_group) % gsize;
   const int pid_n = (pid % in_group) / gsize;
-
-  const int64_t K = p.K, N = p.N;
-  const int KB = (int)(K / KBYTES);
-  const int NBLK = (int)(N / 128);
 
   int64_t row0, row_end;
   const uint8_t* wq = p.w_q;
   int64_t sw_base = 0;
   if constexpr (GROUPED) {
-    // Expert of this tile: tiles are numbered expert by expert, ceil(rows_e / BM) each.  63
-    // experts per pass: lane l holds offsets[e0 + l], the tile counts are prefix-summed across
-    // the wave and a ballot finds the first expert whose tiles reach past pid_m.
-    const int lane0 = threadIdx.x & 63;
-    int cum = 0, e = -1, first = 0;
+    // expert of tile-row pid_m: a ballot finds the first expert whose tile-rows reach past it
+    int cum = 0, e = -1;
     int r0 = 0, r1 = 0;
     for (int e0 = 0; e0 < p.E; e0 += 63) {
-      const int idx = e0 + lane0;
-      const int off = idx <= p.E ? gload<int>(p.offsets + idx) : 0;
-      const int nxt = __shfl_down(off, 1);
-      const bool real = lane0 < 63 && idx < p.E;
-      const int mt = real ? (nxt - off + C::BM - 1) / C::BM : 0;
-      int inc = mt;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(inc, d);
-        if (lane0 >= d) inc += t;
-      }
-      const unsigned long long hit = __ballot(real && cum + inc > pid_m);
+      int off = c_off, nxt = c_nxt, mt = c_mt, inc = c_inc;
+      if (e0 > 0) expert_chunk(e0, off, nxt, mt, inc);
+      const unsigned long long hit = __ballot(mt > 0 && cum + inc > pid_m);
       if (hit) {
-        first = __ffsll((long long)hit) - 1;
+        const int first = __ffsll((long long)hit) - 1;
         e = e0 + first;
         r0 = __shfl(off, first);
         r1 = __shfl(nxt, first);
@@ -157,7 +176,6 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       }
       cum += __shfl(inc, 62);
     }
-    if (e < 0) return;  // padding tile beyond the real tile count
     row0 = (int64_t)r0 + (int64_t)(pid_m - cum) * C::BM;
     row_end = r1;
     wq += (int64_t)e * N * K;
@@ -675,7 +693,9 @@ using Narrow = Cfg<128, 128, 2, 2, 2, 2>;  // N % 256 != 0: 4 waves, wave tile 6
 template <typename C, bool GROUPED>
 hipError_t launch_cfg(const GemmArgs& a, int tiles_m, hipStream_t stream) {
   const int tiles_n = (int)(a.N / C::BN);
-  const int nwg = tiles_m * tiles_n;
+  // grouped: tiles_m is an upper bound; a multiple of 8 workgroups gives every XCD at least its
+  // share of the real tiles
+  const int nwg = GROUPED ? (tiles_m * tiles_n + 7) / 8 * 8 : tiles_m * tiles_n;
   dim3 grid(nwg), block(C::THREADS);
 #define FGB_LAUNCH(SWF, OUT)                                                                  \
   hipLaunchKernelGGL((gemm_prefill_kernel<C, SWF, OUT, GROUPED>), grid, block, 0, stream, a, \

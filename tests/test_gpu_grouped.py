@@ -44,6 +44,24 @@ def test_grouped_parity(dev, counts, fmt, K):
     check_t2(bf16_tensor_to_f64(y16), yref)
 
 
+@pytest.mark.parametrize("K", [512, 1024])  # 256 x 128 and 256 x 256 tiles
+def test_grouped_many_experts(dev, K):
+    """130 experts: the tile-row counts and the expert lookup run over three 63-expert wave
+    passes; empty experts sit at the pass edges and the last pass holds rows."""
+    rng = np.random.default_rng(130)
+    counts = rng.integers(0, 160, 130)
+    counts[[0, 62, 63, 64, 125, 126]] = 0
+    counts[[61, 127, 129]] = [257, 1, 300]
+    offsets = workloads.offsets_from_counts(counts)
+    T, E, N = int(offsets[-1]), 130, 256
+    x = workloads.activations(T, K, key=(0, 34, 0, T))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, key=34)
+    yref = gemm.grouped_ref(aq, sa, wq, sw, offsets)
+    y16 = _run(aq, sa, wq, sw, offsets, dev, torch.bfloat16)
+    check_t2(bf16_tensor_to_f64(y16), yref)
+
+
 @pytest.mark.parametrize("N,K", [(384, 1024), (512, 4096)])
 def test_single_expert_equals_dense(dev, N, K):
     """E = 1 equals the dense GEMM bit for bit (at (512, 4096) the grouped launch uses 256 x 256
