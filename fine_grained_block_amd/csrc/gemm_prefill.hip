@@ -708,18 +708,8 @@ hipError_t launch_cfg(const GemmArgs& a, int tiles_m, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile choice: 256 x 256 (8 waves of 128 x 64, two stages) when K has at least 8 blocks and its
-// workgroups fill the 256 CUs about as well as the 256 x 128 tile's (three stages, 8 waves of
-// 64 x 64: four token tiles per wave, so the pinned MFMA/FMA pipeline applies, and 20% fewer LDS
-// reads than 128 x 32 waves; +5-7% measured); otherwise 256 x 128.  128 x 128 tiles with 2 stages when N % 256 != 0.  (Measured:
-// 256 x 256 +11-18% at K = 1024-3072, +2% at 1536 with UE8M0 scales; at equal fill it is ~20%
-// faster than 256 x 128, hence the 1.15 fill margin.)
-enum class Pick { Big, Half, Narrow };
-
 template <typename C>
 int64_t tiles_for(int64_t M, int64_t N) { return ((M + C::BM - 1) / C::BM) * (N / C::BN); }
-
-double fill(int64_t tiles) { return (double)tiles / (double)(((tiles + 255) / 256) * 256); }
 
 // The persistent form for 256 x 256 tiles with two to four tiles per CU, where it measured 1-6%
 // faster (more per CU measured ~2% slower: the workgroups drift apart over many tiles, unlike the
@@ -731,29 +721,69 @@ bool use_persistent(const GemmArgs& a) {
          a.M * a.ldy * 2 < (int64_t(1) << 32);
 }
 
-Pick pick_tile(int64_t M, int64_t N, int64_t K) {
-  if (N % Big::BN != 0 || N % Half::BN != 0) return Pick::Narrow;
-  if (K < 8 * KBYTES) return Pick::Half;
-  const double eff_big = fill(tiles_for<Big>(M, N));
-  const double eff_half = fill(tiles_for<Half>(M, N));
-  return eff_half > eff_big * 1.15 ? Pick::Half : Pick::Big;
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    cached[dev] =
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cached[dev];
+}
+
+// Tile choice (N % 256 == 0; otherwise 128 x 128 tiles with 2 stages).  256 x 256 tiles (8 waves
+// of 128 x 64, two stages) need K of at least 8 blocks; 256 x 128 tiles (three stages, 8 waves of
+// 64 x 64: four token tiles per wave, so the pinned MFMA/FMA pipeline applies) take ~0.6 of a
+// 256 x 256 tile's time (~20% slower per flop, measured at equal fill).  The output columns are
+// split: the first n_big run as 256 x 256 tiles, the rest as 256 x 128 tiles, each part in its
+// own launch, with n_big chosen to minimize the waves of tiles over the CUs (one tile per CU at
+// a time), weighted 1 and 0.6.  Whole waves of big tiles plus one wave of half tiles can beat
+// either tile alone: QKV at M = 4096 (384 big tiles) runs 256 big + 256 half tiles.
+int64_t big_columns(int64_t M, int64_t N, int64_t K) {
+  if (K < 8 * KBYTES) return 0;
+  const int64_t cus = cu_count(), nc = N / Big::BN;
+  const int64_t tm_big = (M + Big::BM - 1) / Big::BM, tm_half = (M + Half::BM - 1) / Half::BM;
+  auto waves = [&](int64_t tiles) { return (tiles + cus - 1) / cus; };
+  int64_t best_c = nc;
+  double best = 1e30;
+  for (int64_t c = nc; c >= 0; --c) {  // on a tie the most big tiles
+    const double t = (double)waves(tm_big * c) + 0.6 * (double)waves(tm_half * (nc - c));
+    if (t < best - 1e-9) { best = t; best_c = c; }
+  }
+  return best_c * Big::BN;
 }
 
 }  // namespace
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
-  switch (pick_tile(a.M, a.N, a.K)) {
-    case Pick::Big: {
-      const int tiles_m = (int)((a.M + Big::BM - 1) / Big::BM);
-      if (!use_persistent(a)) return launch_cfg<Big, false>(a, tiles_m, stream);
-      const int tiles_n = (int)(a.N / Big::BN);
-      hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0>), dim3(256), dim3(Big::THREADS), 0, stream, a,
-                         tiles_m, tiles_n);
-      return hipGetLastError();
+  if (a.N % Big::BN != 0 || a.N % Half::BN != 0)
+    return launch_cfg<Narrow, false>(a, (int)((a.M + Narrow::BM - 1) / Narrow::BM), stream);
+  const int64_t n_big = big_columns(a.M, a.N, a.K);
+  if (n_big > 0) {
+    GemmArgs b = a;
+    b.N = n_big;
+    const int tiles_m = (int)((b.M + Big::BM - 1) / Big::BM);
+    if (use_persistent(b)) {
+      hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0>), dim3(256), dim3(Big::THREADS), 0, stream, b,
+                         tiles_m, (int)(b.N / Big::BN));
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else {
+      const hipError_t e = launch_cfg<Big, false>(b, tiles_m, stream);
+      if (e != hipSuccess) return e;
     }
-    case Pick::Half: return launch_cfg<Half, false>(a, (int)((a.M + Half::BM - 1) / Half::BM), stream);
-    default: return launch_cfg<Narrow, false>(a, (int)((a.M + Narrow::BM - 1) / Narrow::BM), stream);
   }
+  if (n_big == a.N) return hipSuccess;
+  // the remaining output columns: their weight rows, block-scale rows and output columns
+  GemmArgs h = a;
+  h.N = a.N - n_big;
+  h.w_q = a.w_q + n_big * a.K;
+  h.s_w = (const uint8_t*)a.s_w + (n_big / 128) * (a.K / KBYTES) * (a.s_w_fmt == 0 ? 4 : 1);
+  h.y = (uint8_t*)a.y + n_big * (a.y_dtype == 0 ? 2 : 4);
+  return launch_cfg<Half, false>(h, (int)((h.M + Half::BM - 1) / Half::BM), stream);
 }
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t stream) {

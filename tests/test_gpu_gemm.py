@@ -227,6 +227,27 @@ def test_persistent_prefill_tiles(dev, M, N, K):
     check_t2(y16[rows], ref(aq_o[rows], sa_o[rows], wq_o, sw_o))
 
 
+@pytest.mark.parametrize("M", [4096, 4000])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_split_columns_big_and_half_tiles(dev, M, fmt):
+    """N = 6144 at M ~ 4096: the first 4096 output columns run as 256 x 256 tiles and the last
+    2048 as 256 x 128 tiles (two launches on offset weight rows, scale rows and output
+    columns).  Rows across the tile-rows (and the ragged last one) are checked against the
+    oracle over all columns, so both parts and their boundary are covered; bf16 output is the
+    RNE of the float32 output."""
+    N, K = 6144, 1024
+    ops = oracle_operands(M, N, K, key=12, fmt=fmt)
+    aq, sa, wq, sw = upload(*ops, dev)
+    y32 = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.float32)
+    y16 = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y32 = y32.cpu().numpy().astype(np.float64)
+    assert np.array_equal(bf16_tensor_to_f64(y16), gemm.bf16_rne(y32))
+    rows = np.unique(np.concatenate([np.arange(0, M, 256), np.arange(127, M, 256), [M - 1]]))
+    aq_o, sa_o, wq_o, sw_o = ops
+    check_t1(y32[rows], ref(aq_o[rows], sa_o[rows], wq_o, sw_o, fmt=fmt))
+
+
 def test_repeated_runs_are_bitwise_identical(dev):
     """Every path sums in a fixed order, so repeated runs must agree bit for bit; a race between
     the LDS copies and the reads of a stage (or between workgroups) would show up as run-to-run
