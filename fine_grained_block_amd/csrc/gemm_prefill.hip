@@ -439,12 +439,12 @@ template <typename C, int SWF>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(GemmArgs p, int tiles_m,
                                                                                   int tiles_n) {
   static_assert(C::STAGES == 2 && C::BM == 256 && C::BN == 256 && C::WN == 2, "two-stage 256 x 256 tiles");
-  static_assert(SWF == 0, "float32 weight-block scales (copied as whole dwords)");
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE];
   __shared__ __attribute__((aligned(16))) float sas0[C::BM];
   __shared__ __attribute__((aligned(16))) float sas1[C::BM];
-  // weight-block scales of a tile's two block rows, by tile parity
+  // weight-block scales of a tile's two block rows, by tile parity: float32 [2][256], or UE8M0
+  // bytes [2][256] in the first 512 bytes
   __shared__ __attribute__((aligned(16))) float swr0[2 * 256];
   __shared__ __attribute__((aligned(16))) float swr1[2 * 256];
 
@@ -457,7 +457,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
   const int wn = wave % C::WN, wm = wave / C::WN;
   const int lrow = lane >> 3;
   const int GROUP_M = p.K <= 16 * KBYTES ? 4 : 8;
-  const int sw_q = wave % 8;  // this wave's scale copy: block row sw_q / 4, K-blocks 64 (sw_q % 4) + lane
+  // this wave's scale copy: float32, block row sw_q / 4, K-block 64 (sw_q % 4) + lane; UE8M0 (K
+  // a multiple of 4 blocks), block row sw_q % 2, K-blocks 4 lane .. 4 lane + 3 in one dword
+  const int sw_q = wave % 8;
 
   // A tile is two uniform values; its copies address through buffer descriptors based at the
   // tile, so the per-lane offsets below are the same for every tile.  Activation rows past M fall
@@ -488,7 +490,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
     aoff[i] = (uint32_t)(r * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
   }
   const uint32_t saoff = (uint32_t)((64 * (wave % C::SA_LD) + lane) * 4);
-  const uint32_t swoff = (uint32_t)(((sw_q >> 2) * KB + min(64 * (sw_q & 3) + lane, KB - 1)) * 4);
+  const uint32_t swoff = SWF == 0 ? (uint32_t)(((sw_q >> 2) * KB + min(64 * (sw_q & 3) + lane, KB - 1)) * 4)
+                                  : (uint32_t)((sw_q & 1) * KB + 4 * min(lane, KB / 4 - 1));
 
   // Copy d of block kb of tile t into stage st: 0 the activation scales, then the weight and
   // activation 8-row groups, and last the weight-block scales of tile ts into swr (every step
@@ -516,9 +519,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + C::W_BYTES + (wave + i * C::WAVES) * 8 * KBYTES), 16,
                                                aoff[i], koff, 0, 0);
     } else {
-      const __amdgpu_buffer_rsrc_t sw_rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)((const float*)p.s_w + (ts.n0 / 128) * KB), 0, -1, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sw_rs, LPTR(swr + sw_q * 64), 4, swoff, 0, 0, 0);
+      const __amdgpu_buffer_rsrc_t sw_rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const uint8_t*)p.s_w + (ts.n0 / 128) * KB * (SWF == 0 ? 4 : 1)), 0, -1, 0x00020000);
+      uint8_t* const dst = (uint8_t*)swr + (SWF == 0 ? sw_q * 256 : (sw_q & 1) * 256);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sw_rs, LPTR(dst), 4, swoff, 0, 0, 0);
     }
 #endif
   };
@@ -530,10 +534,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
 
   v4f acc[C::TN][C::TM];
 
-  // One K-block (the schedule of gemm_prefill_kernel); the copies of block kn of tile tn and the
-  // weight-block scales of tile ts go out spread over the first MFMAs.
-  auto compute = [&](const uint8_t* st, const float* sas_cur, const float* swr_cur, int kb, const Tile tn, int kn,
-                     uint8_t* refill, float* sas_refill, const Tile ts, float* swr_next) {
+  // One K-block (the schedule of gemm_prefill_kernel); the copies of block kn of tile tn, and in
+  // a tile's first step (WithSw) the weight-block scales of tile ts, go out spread over the first
+  // MFMAs.
+  auto compute = [&](auto WithSw, const uint8_t* st, const float* sas_cur, const float* swr_cur, int kb,
+                     const Tile tn, int kn, uint8_t* refill, float* sas_refill, const Tile ts, float* swr_next) {
+    constexpr int NP = decltype(WithSw)::value ? NPART : NPART - 1;
     const uint8_t* ws = st + wn * (C::BN / C::WN) * KBYTES;
     const uint8_t* as = st + C::W_BYTES + wm * (C::BM / C::WM) * KBYTES;
     float sc[C::TM];
@@ -549,9 +555,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
 #pragma unroll
     for (int t = 0; t < T + LAG; ++t) {
       {
-        constexpr int SP = (NPART - 1) * SPACING < T + LAG ? SPACING : (T + LAG - 1) / (NPART - 1);
-        static_assert(SP >= 1 && (NPART - 1) * SP < T + LAG, "copies fit the MFMA sequence");
-        if (t % SP == 0 && t / SP < NPART) issue_part(tn, kn, refill, sas_refill, ts, swr_next, t / SP);
+        constexpr int SP = (NP - 1) * SPACING < T + LAG ? SPACING : (T + LAG - 1) / (NP - 1);
+        static_assert(SP >= 1 && (NP - 1) * SP < T + LAG, "copies fit the MFMA sequence");
+        if (t % SP == 0 && t / SP < NP) issue_part(tn, kn, refill, sas_refill, ts, swr_next, t / SP);
       }
       if (t < T) {
         const int i = t / C::TM, j = t % C::TM;
@@ -560,7 +566,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
         if (t == 1) {
 #pragma unroll
           for (int jj = 0; jj < C::TM; ++jj) sav[jj] = sas_cur[tok[jj]];
-          swv = swr_cur[sw_b * 256 + kb];
+          if constexpr (SWF == 0) swv = swr_cur[sw_b * 256 + kb];
+          else swv = dec_ue8m0(reinterpret_cast<const uint8_t*>(swr_cur)[sw_b * 256 + kb]);
         }
       }
       if (t == LAG) {
@@ -640,26 +647,26 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
     // blocks 0 and 1
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<NSTORE>());
     wg_barrier();
-    compute(stage0, sas0, swr_cur, 0, tc, 1, stage1, sas1, tn, swr_nxt);
+    compute(std::true_type{}, stage0, sas0, swr_cur, 0, tc, 1, stage1, sas1, tn, swr_nxt);
     {
       const bool last = KB == 2;
       const Tile tt = last ? tn : tc;
       const int kn = last ? 0 : 2;
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
       wg_barrier();
-      compute(stage1, sas1, swr_cur, 1, tt, kn, stage0, sas0, tn, swr_nxt);
+      compute(std::false_type{}, stage1, sas1, swr_cur, 1, tt, kn, stage0, sas0, tn, swr_nxt);
     }
     // blocks 2 .. KB-1; the last step copies the next tile's block 0
     for (int kb = 2; kb < KB; kb += 2) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
       wg_barrier();
-      compute(stage0, sas0, swr_cur, kb, tc, kb + 1, stage1, sas1, tn, swr_nxt);
+      compute(std::false_type{}, stage0, sas0, swr_cur, kb, tc, kb + 1, stage1, sas1, tn, swr_nxt);
       const bool last = kb + 2 >= KB;
       const Tile tt = last ? tn : tc;
       const int kn = last ? 0 : kb + 2;
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
       wg_barrier();
-      compute(stage1, sas1, swr_cur, kb + 1, tt, kn, stage0, sas0, tn, swr_nxt);
+      compute(std::false_type{}, stage1, sas1, swr_cur, kb + 1, tt, kn, stage0, sas0, tn, swr_nxt);
     }
     epilogue(tc);
   };
@@ -708,19 +715,6 @@ hipError_t launch_cfg(const GemmArgs& a, int tiles_m, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename C>
-int64_t tiles_for(int64_t M, int64_t N) { return ((M + C::BM - 1) / C::BM) * (N / C::BN); }
-
-// The persistent form for 256 x 256 tiles with two to four tiles per CU, where it measured 1-6%
-// faster (more per CU measured ~2% slower: the workgroups drift apart over many tiles, unlike the
-// in-order hardware dispatch); an even K-block count of at most 256 (one scale row per wave copy),
-// float32 weight-block scales, bf16 output and 32-bit output offsets.
-bool use_persistent(const GemmArgs& a) {
-  const int64_t KB = a.K / KBYTES, tiles = tiles_for<Big>(a.M, a.N);
-  return tiles > 256 && tiles <= 4 * 256 && KB % 2 == 0 && KB <= 256 && a.s_w_fmt == 0 && a.y_dtype == 0 &&
-         a.M * a.ldy * 2 < (int64_t(1) << 32);
-}
-
 // Compute units of the current device (cached per device).
 int cu_count() {
   static int cached[64] = {};
@@ -733,6 +727,21 @@ int cu_count() {
   }
   return cached[dev];
 }
+
+template <typename C>
+int64_t tiles_for(int64_t M, int64_t N) { return ((M + C::BM - 1) / C::BM) * (N / C::BN); }
+
+// The persistent form for more 256 x 256 tiles than CUs when K has at most 16 blocks, where the
+// work between tiles weighs most: measured +4-7% at 12-16 blocks; at 32 (gate+up) +2% alone but
+// 0.5% slower inside the Llama step, and 0.2-1.5% slower at 56-144 blocks.  An even K-block count
+// (a multiple of 4 with UE8M0 scales, copied four to a dword), bf16 output and 32-bit output
+// offsets.
+bool use_persistent(const GemmArgs& a) {
+  const int64_t KB = a.K / KBYTES, tiles = tiles_for<Big>(a.M, a.N);
+  return tiles > cu_count() && KB <= 16 && KB % 2 == 0 && (a.s_w_fmt == 0 || KB % 4 == 0) && a.y_dtype == 0 &&
+         a.M * a.ldy * 2 < (int64_t(1) << 32);
+}
+
 
 // Tile choice (N % 256 == 0; otherwise 128 x 128 tiles with 2 stages).  256 x 256 tiles (8 waves
 // of 128 x 64, two stages) need K of at least 8 blocks; 256 x 128 tiles (three stages, 8 waves of
@@ -767,8 +776,14 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
     b.N = n_big;
     const int tiles_m = (int)((b.M + Big::BM - 1) / Big::BM);
     if (use_persistent(b)) {
-      hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0>), dim3(256), dim3(Big::THREADS), 0, stream, b,
-                         tiles_m, (int)(b.N / Big::BN));
+      // one workgroup per CU (a multiple of 8, as the XCD mapping of tiles assumes)
+      const dim3 grid(cu_count() / 8 * 8);
+      if (b.s_w_fmt == 0)
+        hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0>), grid, dim3(Big::THREADS), 0, stream, b, tiles_m,
+                           (int)(b.N / Big::BN));
+      else
+        hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 1>), grid, dim3(Big::THREADS), 0, stream, b, tiles_m,
+                           (int)(b.N / Big::BN));
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     } else {

@@ -207,14 +207,16 @@ def test_decode_mid_rows_kernel(dev, M, fmt):
         check_t2(bf16_tensor_to_f64(y16), yref)
 
 
-@pytest.mark.parametrize("M,N,K", [(1000, 32768, 1024), (1700, 16384, 3072), (4096, 8192, 2048), (520, 65536, 1280)])
-def test_persistent_prefill_tiles(dev, M, N, K):
-    """256 x 256 tiles with more tiles than CUs (bf16 output, float32 scales): each workgroup
-    walks several tiles, copying the next tile's first block while it stores the current one.
-    Ragged M, tile counts that are and are not multiples of the grid, 8 to 24 K-blocks.  Every
-    output equals the RNE of the float32-output kernel's (the same sums in the same order), and a
-    sample of rows, including every tile's first and last, matches the oracle."""
-    ops = oracle_operands(M, N, K, key=9)
+@pytest.mark.parametrize("M,N,K", [(1000, 32768, 1024), (1700, 16384, 2048), (4096, 8192, 2048), (520, 65536, 1280)])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_persistent_prefill_tiles(dev, M, N, K, fmt):
+    """256 x 256 tiles with more tiles than CUs and K of at most 16 blocks (bf16 output): each
+    workgroup walks several tiles, copying the next tile's first block while it stores the
+    current one.  Ragged M, tile counts that are and are not multiples of the grid, 8 to 16
+    K-blocks, both scale formats (UE8M0 with 10 K-blocks takes the one-tile launch).  Every output
+    equals the RNE of the float32-output kernel's (the same sums in the same order), and a sample
+    of rows, including every tile's first and last, matches the oracle."""
+    ops = oracle_operands(M, N, K, key=9, fmt=fmt)
     aq, sa, wq, sw = upload(*ops, dev)
     y16 = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.bfloat16)
     y32 = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.float32)
@@ -224,7 +226,7 @@ def test_persistent_prefill_tiles(dev, M, N, K):
     ends = np.arange(0, M, 256)
     rows = np.unique(np.concatenate([ends, np.minimum(ends + 255, M - 1), [M // 2]]))
     aq_o, sa_o, wq_o, sw_o = ops
-    check_t2(y16[rows], ref(aq_o[rows], sa_o[rows], wq_o, sw_o))
+    check_t2(y16[rows], ref(aq_o[rows], sa_o[rows], wq_o, sw_o, fmt=fmt))
 
 
 @pytest.mark.parametrize("M", [4096, 4000])
