@@ -435,7 +435,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 //     exactly those in flight.
 // Per step, the copies and the schedule are those of gemm_prefill_kernel.
 // ---------------------------------------------------------------------------------------------
-template <typename C, int SWF>
+template <typename C, int SWF, bool GROUPED>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(GemmArgs p, int tiles_m,
                                                                                   int tiles_n) {
   static_assert(C::STAGES == 2 && C::BM == 256 && C::BN == 256 && C::WN == 2, "two-stage 256 x 256 tiles");
@@ -448,11 +448,28 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
   __shared__ __attribute__((aligned(16))) float swr0[2 * 256];
   __shared__ __attribute__((aligned(16))) float swr1[2 * 256];
 
-  const int ntiles = tiles_m * tiles_n;
   const int64_t K = p.K, M = p.M;
   const int KB = (int)(K / KBYTES);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // Grouped (at most 63 experts): lane l holds offsets[l] and the inclusive prefix sum over
+  // experts 0..l of their tile-row counts; tiles are numbered expert by expert, and tiles_m (an
+  // upper bound) is replaced by the real count.
+  int c_off = 0, c_inc = 0;
+  int real_tiles_m = tiles_m;
+  if constexpr (GROUPED) {
+    c_off = lane <= p.E ? gload<int>(p.offsets + lane) : 0;
+    const int nxt = __shfl_down(c_off, 1);
+    c_inc = lane < p.E ? (nxt - c_off + C::BM - 1) / C::BM : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(c_inc, d);
+      if (lane >= d) c_inc += t;
+    }
+    real_tiles_m = __builtin_amdgcn_readfirstlane(__shfl(c_inc, 62));
+  }
+  const int ntiles = real_tiles_m * tiles_n;
+  if ((int)blockIdx.x >= ntiles) return;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % C::WN, wm = wave / C::WN;
   const int lrow = lane >> 3;
@@ -461,21 +478,36 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
   // a multiple of 4 blocks), block row sw_q % 2, K-blocks 4 lane .. 4 lane + 3 in one dword
   const int sw_q = wave % 8;
 
-  // A tile is two uniform values; its copies address through buffer descriptors based at the
-  // tile, so the per-lane offsets below are the same for every tile.  Activation rows past M fall
-  // outside the descriptors' ranges: their copies are dropped (the rows feed only output rows
-  // that are never stored).
+  // A tile is a few uniform values (rows row0 .. row_end-1 of the activations, for grouped those
+  // of expert e); its copies address through buffer descriptors based at the tile, so the
+  // per-lane offsets below are the same for every tile.  Activation rows past row_end fall outside
+  // the descriptors' ranges: their copies are dropped (the rows feed only output rows that are
+  // never stored).
   struct Tile {
-    int64_t row0, n0;
+    int64_t row0, n0, row_end;
+    int e;
   };
   auto make_tile = [&](int v) {
     Tile t;
     const int pid = xcd_remap(v, ntiles);
     const int in_group = GROUP_M * tiles_n;
     const int first_m = (pid / in_group) * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    t.row0 = (int64_t)(first_m + (pid % in_group) % gsize) * C::BM;
+    const int gsize = min(real_tiles_m - first_m, GROUP_M);
+    const int pid_m = first_m + (pid % in_group) % gsize;
     t.n0 = (int64_t)((pid % in_group) / gsize) * C::BN;
+    if constexpr (GROUPED) {
+      // the first expert whose tile-rows reach past pid_m (an empty expert's prefix equals the
+      // one before it, so the first lane past pid_m has tiles)
+      const int first = __builtin_amdgcn_readfirstlane(__ffsll((long long)__ballot(c_inc > pid_m)) - 1);
+      const int before = first > 0 ? __builtin_amdgcn_readlane(c_inc, first - 1) : 0;
+      t.e = first;
+      t.row0 = (int64_t)__builtin_amdgcn_readlane(c_off, first) + (int64_t)(pid_m - before) * C::BM;
+      t.row_end = __builtin_amdgcn_readlane(c_off, first + 1);
+    } else {
+      t.e = 0;
+      t.row0 = (int64_t)pid_m * C::BM;
+      t.row_end = M;
+    }
     return t;
   };
   uint32_t woff[C::W_LD], aoff[C::A_LD];
@@ -500,7 +532,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
   auto issue_part = [&](const Tile t, int kb, uint8_t* st, float* sas, const Tile ts, float* swr, int d) {
 #if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
     const uint32_t koff = (uint32_t)kb * KBYTES;
-    const uint32_t rows = (uint32_t)(M - t.row0);
+    const uint32_t rows = (uint32_t)(t.row_end - t.row0);
     if (d == 0) {
       // (the K-block goes into the base: the range check then covers exactly the tile's rows)
       const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -508,7 +540,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * (wave % C::SA_LD)), 4, saoff, 0, 0, 0);
     } else if (d <= C::W_LD) {
       const __amdgpu_buffer_rsrc_t w_rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_q + t.n0 * K), 0, -1, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_q + ((int64_t)t.e * p.N + t.n0) * K), 0, -1, 0x00020000);
       const int i = d - 1;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, woff[i],
                                                koff, 0, 0);
@@ -520,7 +552,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
                                                aoff[i], koff, 0, 0);
     } else {
       const __amdgpu_buffer_rsrc_t sw_rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const uint8_t*)p.s_w + (ts.n0 / 128) * KB * (SWF == 0 ? 4 : 1)), 0, -1, 0x00020000);
+          (void*)((const uint8_t*)p.s_w + ((int64_t)ts.e * (p.N / 128) + ts.n0 / 128) * KB * (SWF == 0 ? 4 : 1)), 0,
+          -1, 0x00020000);
       uint8_t* const dst = (uint8_t*)swr + (SWF == 0 ? sw_q * 256 : (sw_q & 1) * 256);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sw_rs, LPTR(dst), 4, swoff, 0, 0, 0);
     }
@@ -593,7 +626,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
     asm volatile("" : "+v"(et));
     const int el = et & 63;
     const __amdgpu_buffer_rsrc_t y_rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((uint8_t*)p.y + (t.row0 * p.ldy + t.n0) * 2), 0, (int)(uint32_t)((M - t.row0) * p.ldy * 2), 0x00020000);
+        (void*)((uint8_t*)p.y + (t.row0 * p.ldy + t.n0) * 2), 0, (int)(uint32_t)((t.row_end - t.row0) * p.ldy * 2), 0x00020000);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       wg_barrier();  // the previous round's reads (and, for r = 0, the last block's) are done
@@ -779,11 +812,11 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
       // one workgroup per CU (a multiple of 8, as the XCD mapping of tiles assumes)
       const dim3 grid(cu_count() / 8 * 8);
       if (b.s_w_fmt == 0)
-        hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0>), grid, dim3(Big::THREADS), 0, stream, b, tiles_m,
-                           (int)(b.N / Big::BN));
+        hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0, false>), grid, dim3(Big::THREADS), 0, stream, b,
+                           tiles_m, (int)(b.N / Big::BN));
       else
-        hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 1>), grid, dim3(Big::THREADS), 0, stream, b, tiles_m,
-                           (int)(b.N / Big::BN));
+        hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 1, false>), grid, dim3(Big::THREADS), 0, stream, b,
+                           tiles_m, (int)(b.N / Big::BN));
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     } else {
@@ -804,8 +837,22 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t stream) {
   // upper bound on the per-expert tile count: sum_e ceil(M_e/BM) <= ceil(total_M/BM) + E
   // (256 x 256 tiles from 8 K-blocks, as for the dense GEMM; MoE down, K = 2048: +15% over 256 x 128)
-  if (a.N % Big::BN == 0 && a.K >= 8 * KBYTES)
-    return launch_cfg<Big, true>(a, (int)((a.M + Big::BM - 1) / Big::BM) + a.E, stream);
+  if (a.N % Big::BN == 0 && a.K >= 8 * KBYTES) {
+    const int tiles_m = (int)((a.M + Big::BM - 1) / Big::BM) + a.E;
+    // the persistent form under the dense rule (K of at most 16 blocks; the real tile count is
+    // known only on the device, the bound decides), with at most 63 experts (one wave pass)
+    if (a.E <= 63 && use_persistent(a)) {
+      const dim3 grid(cu_count() / 8 * 8);
+      if (a.s_w_fmt == 0)
+        hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0, true>), grid, dim3(Big::THREADS), 0, stream, a,
+                           tiles_m, (int)(a.N / Big::BN));
+      else
+        hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 1, true>), grid, dim3(Big::THREADS), 0, stream, a,
+                           tiles_m, (int)(a.N / Big::BN));
+      return hipGetLastError();
+    }
+    return launch_cfg<Big, true>(a, tiles_m, stream);
+  }
   if (a.N % Half::BN == 0)
     return launch_cfg<Half, true>(a, (int)((a.M + Half::BM - 1) / Half::BM) + a.E, stream);
   return launch_cfg<Narrow, true>(a, (int)((a.M + Narrow::BM - 1) / Narrow::BM) + a.E, stream);

@@ -62,6 +62,32 @@ def test_grouped_many_experts(dev, K):
     check_t2(bf16_tensor_to_f64(y16), yref)
 
 
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+@pytest.mark.parametrize("K", [1024, 2048])
+def test_grouped_persistent(dev, fmt, K):
+    """More 256 x 256 tiles than CUs with K of at most 16 blocks: the persistent form, experts
+    looked up per tile from one wave's prefix sums, rows past an expert's end dropped by the copy
+    and store ranges.  bf16 output equals the RNE of the float32 output (the one-tile launch: the
+    same sums in the same order); the first, a middle and the last row of every expert match the
+    oracle."""
+    counts = [3000, 0, 257, 4100, 1, 2555, 0, 6200, 700]
+    E, N = len(counts), 1536
+    offsets = workloads.offsets_from_counts(counts)
+    T = int(offsets[-1])
+    x = workloads.activations(T, K, key=(0, 35, 0, T))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, key=35, fmt=fmt)
+    y32 = _run(aq, sa, wq, sw, offsets, dev, torch.float32).cpu().numpy().astype(np.float64)
+    y16 = bf16_tensor_to_f64(_run(aq, sa, wq, sw, offsets, dev, torch.bfloat16))
+    assert np.array_equal(y16, gemm.bf16_rne(y32))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows = np.unique([lo, (lo + hi) // 2, hi - 1])
+        check_t1(y32[rows], gemm.gemm_ref(aq[rows], sa[rows], wq[e], sw[e], fmt))
+
+
 @pytest.mark.parametrize("N,K", [(384, 1024), (512, 4096)])
 def test_single_expert_equals_dense(dev, N, K):
     """E = 1 equals the dense GEMM bit for bit (at (512, 4096) the grouped launch uses 256 x 256
