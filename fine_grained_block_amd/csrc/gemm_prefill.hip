@@ -423,16 +423,18 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 }
 
 // ---------------------------------------------------------------------------------------------
-// Persistent variant for 256 x 256 tiles when a launch has several tiles per CU (dense, two
-// stages, an even number of K-blocks): one workgroup per CU walks its tiles (in the order the
-// one-tile-per-workgroup launch runs them), and the work between two tiles is overlapped:
-//   * the next tile's first block and its weight-block scales are copied during the current
-//     tile's last step, into the stage that step frees;
+// Persistent variant for 256 x 256 tiles when a launch has several tiles per CU (dense or
+// grouped, two stages, an even number of K-blocks, bf16 output): one workgroup per CU walks its
+// tiles (in the order the one-tile-per-workgroup launch runs them), and the work between two
+// tiles is overlapped:
+//   * the next tile's first block is copied during the current tile's last step, into the stage
+//     that step frees, and its weight-block scales during the current tile's first step, into
+//     the scale buffer the current tile does not read;
 //   * the output tile is staged through the other stage (free after the last step) in two
 //     rounds of 128 token rows, rows swizzled instead of padded (chunk c of row m at c ^ (m & 15));
-//   * the stores are range-checked buffer stores (rows past M are dropped by the hardware), so
-//     every thread issues the same number of them and the next tile's first wait can leave
-//     exactly those in flight.
+//   * the stores are range-checked buffer stores (rows past the tile's last row are dropped by
+//     the hardware), so every thread issues the same number of them and the next tile's first
+//     wait can leave exactly those in flight.
 // Per step, the copies and the schedule are those of gemm_prefill_kernel.
 // ---------------------------------------------------------------------------------------------
 template <typename C, int SWF, bool GROUPED>
@@ -526,8 +528,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
                                   : (uint32_t)((sw_q & 1) * KB + 4 * min(lane, KB / 4 - 1));
 
   // Copy d of block kb of tile t into stage st: 0 the activation scales, then the weight and
-  // activation 8-row groups, and last the weight-block scales of tile ts into swr (every step
-  // issues it; the copy for the next tile lands in the buffer the current tile does not read).
+  // activation 8-row groups, and last (a tile's first step only) the weight-block scales of tile
+  // ts into swr, the buffer the current tile does not read.
   constexpr int NPART = 2 + C::W_LD + C::A_LD;
   auto issue_part = [&](const Tile t, int kb, uint8_t* st, float* sas, const Tile ts, float* swr, int d) {
 #if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
