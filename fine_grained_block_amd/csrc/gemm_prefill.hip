@@ -277,12 +277,23 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   }
   const float* sw_lds = sws + (int)(nb - n0 / 128) * 256;
 
+  // A wave whose token rows all lie past the tile's last row (the last tile of an expert or of
+  // M) only issues its copies: its outputs are never stored, and on a SIMD left with one working
+  // wave that wave runs alone.  (Two-stage tiles only: with three stages the branch made the
+  // compiler wait for the younger copies that the pipeline leaves in flight.)
+  const bool active = C::STAGES != 2 || wm * (C::BM / C::WM) < row_end - row0;
+
   // One K-block of the wave's sub-tile: one MFMA per 16x16 tile gives the partial P, then
   // acc += P * (s_a * s_w).  The MFMAs, the scale-FMAs and the fragment reads are interleaved so
   // that matrix core, VALU and LDS work overlap instead of waiting on each other.
   // The copies of block kb_next go out spread over the first MFMAs, one every SPACING.
   auto compute = [&](const uint8_t* st, const float* sas_cur, const float* swp, int kb_next, uint8_t* refill,
                      float* sas_refill) {
+    if (!active) {
+#pragma unroll
+      for (int d = 0; d < NPART; ++d) issue_part(kb_next, refill, sas_refill, d);
+      return;
+    }
     const uint8_t* ws = st + wn * (C::BN / C::WN) * KBYTES;
     const uint8_t* as = st + C::W_BYTES + wm * (C::BM / C::WM) * KBYTES;
     float sc[C::TM];

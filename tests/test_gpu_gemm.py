@@ -229,14 +229,15 @@ def test_persistent_prefill_tiles(dev, M, N, K, fmt):
     check_t2(y16[rows], ref(aq_o[rows], sa_o[rows], wq_o, sw_o, fmt=fmt))
 
 
-@pytest.mark.parametrize("M", [4096, 4000])
+@pytest.mark.parametrize("M", [4096, 4000, 3900])
 @pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
 def test_split_columns_big_and_half_tiles(dev, M, fmt):
     """N = 6144 at M ~ 4096: the first 4096 output columns run as 256 x 256 tiles and the last
     2048 as 256 x 128 tiles (two launches on offset weight rows, scale rows and output
-    columns).  Rows across the tile-rows (and the ragged last one) are checked against the
-    oracle over all columns, so both parts and their boundary are covered; bf16 output is the
-    RNE of the float32 output."""
+    columns).  Rows across the tile-rows (and the ragged last one: 160 or 60 rows, where the
+    waves of the empty 64-row quarters skip their MFMAs) are checked against the oracle over
+    all columns, so both parts and their boundary are covered; bf16 output is the RNE of the
+    float32 output."""
     N, K = 6144, 1024
     ops = oracle_operands(M, N, K, key=12, fmt=fmt)
     aq, sa, wq, sw = upload(*ops, dev)
