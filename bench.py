@@ -59,25 +59,28 @@ def kernel_source_hash() -> str:
 
 
 def derive_traffic(pmc_dir: str) -> dict:
-    """HBM bytes per prefill-GEMM launch from two rocprofv3 counter runs.
+    """HBM bytes per prefill-GEMM call of the Llama step from two rocprofv3 counter runs.
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by 1 GiB over what the same
-    counter read for the 1 GiB device copy (__amd_rocclr_copyBuffer) of the same run; the result
-    is the mean over the GEMM dispatches of one step, weighting each projection once.
+    counter read for the 1 GiB device copy (__amd_rocclr_copyBuffer) of the same run.  A
+    projection's GEMM call is every GEMM dispatch between its act_quant dispatch and the next one
+    (QKV runs as two dispatches); the projections repeat in step order.
     """
     import collections
     import csv
+
+    names = ("qkv", "o", "gate_up", "down")
 
     def load(counter):
         per = collections.OrderedDict()
         with open(os.path.join(pmc_dir, counter, "run_counter_collection.csv")) as fh:
             for r in csv.DictReader(fh):
-                k = (int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]))
+                k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
                 per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
         return per
 
-    out = {"kernel_source_hash": kernel_source_hash(), "per_grid": {}}
-    per_launch = 0.0
+    out = {"kernel_source_hash": kernel_source_hash(), "per_projection": {}}
+    per_call = 0.0
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         d = load(counter)
         copy_kib = [v for k, v in d.items() if "copyBuffer" in k[1]]
@@ -85,22 +88,29 @@ def derive_traffic(pmc_dir: str) -> dict:
             raise SystemExit(f"{counter}: expected one 1 GiB copy dispatch, found {len(copy_kib)}")
         factor = (1 << 20) / copy_kib[0]
         out[counter.lower() + "_copy_factor"] = round(factor, 5)
-        grids = collections.defaultdict(list)
-        for k, v in d.items():
-            if "gemm_prefill_kernel" in k[1]:
-                grids[k[2]].append(v * 1024 * factor)
-        for g, vals in grids.items():
-            out["per_grid"].setdefault(str(g), {})[counter.lower() + "_bytes"] = round(sum(vals) / len(vals))
-        allv = [v for vals in grids.values() for v in vals]
-        per_launch += sum(allv) / len(allv)
-    out["gemm_prefill_hbm_bytes_per_launch"] = round(per_launch)
-    out["note"] = ("calibrated HBM fetch + write bytes per prefill-GEMM dispatch, mean over every "
-                   "GEMM dispatch of the run (each step launches the four projections once); "
-                   "per_grid splits it by launch grid (O and down share one grid)")
+        calls, disp = [], []
+        for (did, name), v in sorted(d.items()):
+            if "act_quant" in name:
+                calls.append(0.0)
+                disp.append(0)
+            elif "gemm_prefill" in name and calls:
+                calls[-1] += v * 1024 * factor
+                disp[-1] += 1
+        if not calls or len(calls) % 4:
+            raise SystemExit(f"{counter}: {len(calls)} projection calls, expected whole steps of 4")
+        for i, nm in enumerate(names):
+            vals = calls[i::4]
+            e = out["per_projection"].setdefault(nm, {})
+            e[counter.lower() + "_bytes"] = round(sum(vals) / len(vals))
+            e["dispatches"] = disp[i]
+        per_call += sum(calls) / len(calls)
+    out["gemm_prefill_hbm_bytes_per_call"] = round(per_call)
+    out["note"] = ("calibrated HBM fetch + write bytes per prefill-GEMM call of the Llama step, mean "
+                   "over the four projections' calls (QKV's call is two dispatches: 256x256 and "
+                   "256x128 tiles)")
     return out
 
 
-# ---------------------------------------------------------------------------------------------
 def headline_step(args, torch, fgb, workloads, np):
     dev = torch.device("cuda:0")
     M = workloads.LLAMA3_8B_PREFILL_M
@@ -348,7 +358,7 @@ def main():
         with open(tfile) as fh:
             t = json.load(fh)
         if t.get("kernel_source_hash") == extra["kernel_source_hash"]:
-            traffic = t.get("gemm_prefill_hbm_bytes_per_launch")
+            traffic = t.get("gemm_prefill_hbm_bytes_per_call")
     if args.suite == "all":
         extra.update(extra_suites(torch, fgb, workloads, np))
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, workloads, np)
