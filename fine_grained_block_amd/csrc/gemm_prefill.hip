@@ -141,6 +141,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       if (e0 == 0) { c_off = off; c_nxt = nxt; c_mt = mt; c_inc = inc; }
       real_tiles_m += __shfl(inc, 62);
     }
+    real_tiles_m = min(real_tiles_m, tiles_m);  // (valid offsets never exceed the host's bound)
   }
   const int nwg = real_tiles_m * tiles_n;
   if (GROUPED && (int)blockIdx.x / 8 >= nwg / 8 + ((int)blockIdx.x % 8 < nwg % 8)) return;
@@ -479,7 +480,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
       const int t = __shfl_up(c_inc, d);
       if (lane >= d) c_inc += t;
     }
-    real_tiles_m = __builtin_amdgcn_readfirstlane(__shfl(c_inc, 62));
+    // (never above the host's bound, which valid offsets cannot exceed)
+    real_tiles_m = min(__builtin_amdgcn_readfirstlane(__shfl(c_inc, 62)), tiles_m);
   }
   const int ntiles = real_tiles_m * tiles_n;
   if ((int)blockIdx.x >= ntiles) return;
