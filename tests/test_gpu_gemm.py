@@ -251,6 +251,23 @@ def test_split_columns_big_and_half_tiles(dev, M, fmt):
     check_t1(y32[rows], ref(aq_o[rows], sa_o[rows], wq_o, sw_o, fmt=fmt))
 
 
+@pytest.mark.parametrize("M,N,K", [(1000, 32768, 1024), (3900, 6144, 1024)])
+def test_persistent_and_split_paths_respect_strides(dev, M, N, K):
+    """The persistent launch (range-checked stores based at each tile) and the split-column
+    launches (offset output columns) write exactly the [M, N] window of a wider output buffer
+    (ldy > N): the guard rows and columns keep their pattern, and the window equals the result
+    written to a dense output."""
+    ops = oracle_operands(M, N, K, key=13)
+    aq, sa, wq, sw = upload(*ops, dev)
+    dense = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.bfloat16)
+    buf = torch.full((M + 2, N + 64), -7.0, dtype=torch.bfloat16, device=dev)
+    fgb.gemm(aq, sa, wq, sw, out=buf[1:M + 1, 8:N + 8])
+    torch.cuda.synchronize()
+    assert torch.equal(buf[1:M + 1, 8:N + 8], dense)
+    assert bool((buf[0] == -7).all()) and bool((buf[M + 1] == -7).all())
+    assert bool((buf[:, :8] == -7).all()) and bool((buf[:, N + 8:] == -7).all())
+
+
 def test_repeated_runs_are_bitwise_identical(dev):
     """Every path sums in a fixed order, so repeated runs must agree bit for bit; a race between
     the LDS copies and the reads of a stage (or between workgroups) would show up as run-to-run
