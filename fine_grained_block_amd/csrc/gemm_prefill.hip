@@ -779,14 +779,16 @@ int cu_count() {
 template <typename C>
 int64_t tiles_for(int64_t M, int64_t N) { return ((M + C::BM - 1) / C::BM) * (N / C::BN); }
 
-// The persistent form for more 256 x 256 tiles than CUs when K has at most 16 blocks, where the
-// work between tiles weighs most: measured +4-7% at 12-16 blocks; at 32 (gate+up) +2% alone but
-// 0.5% slower inside the Llama step, and 0.2-1.5% slower at 56-144 blocks.  An even K-block count
-// (a multiple of 4 with UE8M0 scales, copied four to a dword), bf16 output and 32-bit output
-// offsets.
-bool use_persistent(const GemmArgs& a) {
+// The persistent form for more 256 x 256 tiles than CUs when K has at most max_kb blocks.  Dense
+// (16 blocks), where the work between tiles weighs most: measured +4-7% at 12-16 blocks; at 32
+// (gate+up) +2% alone but 0.5% slower inside the Llama step, and 0.2-1.5% slower at 56-144
+// blocks.  Grouped (64 blocks): a one-tile launch also looks up each tile's expert when it
+// starts, which the persistent form does from registers; MoE gate+up (56 blocks) +2-4%.  An even
+// K-block count (a multiple of 4 with UE8M0 scales, copied four to a dword), bf16 output and
+// 32-bit output offsets.
+bool use_persistent(const GemmArgs& a, int64_t max_kb) {
   const int64_t KB = a.K / KBYTES, tiles = tiles_for<Big>(a.M, a.N);
-  return tiles > cu_count() && KB <= 16 && KB % 2 == 0 && (a.s_w_fmt == 0 || KB % 4 == 0) && a.y_dtype == 0 &&
+  return tiles > cu_count() && KB <= max_kb && KB % 2 == 0 && (a.s_w_fmt == 0 || KB % 4 == 0) && a.y_dtype == 0 &&
          a.M * a.ldy * 2 < (int64_t(1) << 32);
 }
 
@@ -823,7 +825,7 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
     GemmArgs b = a;
     b.N = n_big;
     const int tiles_m = (int)((b.M + Big::BM - 1) / Big::BM);
-    if (use_persistent(b)) {
+    if (use_persistent(b, 16)) {
       // one workgroup per CU (a multiple of 8, as the XCD mapping of tiles assumes)
       const dim3 grid(cu_count() / 8 * 8);
       if (b.s_w_fmt == 0)
@@ -854,9 +856,9 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t stream) {
   // (256 x 256 tiles from 8 K-blocks, as for the dense GEMM; MoE down, K = 2048: +15% over 256 x 128)
   if (a.N % Big::BN == 0 && a.K >= 8 * KBYTES) {
     const int tiles_m = (int)((a.M + Big::BM - 1) / Big::BM) + a.E;
-    // the persistent form under the dense rule (K of at most 16 blocks; the real tile count is
-    // known only on the device, the bound decides), with at most 63 experts (one wave pass)
-    if (a.E <= 63 && use_persistent(a)) {
+    // the persistent form (the real tile count is known only on the device, the bound decides),
+    // with at most 63 experts (one wave pass)
+    if (a.E <= 63 && use_persistent(a, 64)) {
       const dim3 grid(cu_count() / 8 * 8);
       if (a.s_w_fmt == 0)
         hipLaunchKernelGGL((gemm_prefill_persistent_kernel<Big, 0, true>), grid, dim3(Big::THREADS), 0, stream, a,

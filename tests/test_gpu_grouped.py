@@ -63,9 +63,9 @@ def test_grouped_many_experts(dev, K):
 
 
 @pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
-@pytest.mark.parametrize("K", [1024, 2048])
+@pytest.mark.parametrize("K", [1024, 2048, 7168])
 def test_grouped_persistent(dev, fmt, K):
-    """More 256 x 256 tiles than CUs with K of at most 16 blocks: the persistent form, experts
+    """More 256 x 256 tiles than CUs with K of at most 64 blocks: the persistent form, experts
     looked up per tile from one wave's prefix sums, rows past an expert's end dropped by the copy
     and store ranges.  bf16 output equals the RNE of the float32 output (the one-tile launch: the
     same sums in the same order); the first, a middle and the last row of every expert match the
