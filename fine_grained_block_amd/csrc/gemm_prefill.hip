@@ -23,7 +23,12 @@
 //
 // Each wave owns a (BN/WN) x (BM/WM) sub-tile = TN x TM MFMA tiles of 16x16.  For every K-block
 // one MFMA per tile yields the exact-product float32 partial P, and acc += P * (s_a * s_w).
-// bf16 output tiles are staged through LDS so that the stores write whole lines.
+// bf16 output tiles are staged through LDS so that the (non-temporal) stores write whole lines.
+//
+// Launches (host code at the end): a dense GEMM splits its output columns between 256 x 256 and
+// 256 x 128 tiles so that the tiles fill whole waves of CUs; with more 256 x 256 tiles than CUs
+// and a short K (grouped: up to 64 K-blocks) one workgroup per CU walks the tiles
+// (gemm_prefill_persistent_kernel) and overlaps the work between consecutive tiles.
 #include "gemm_common.hpp"
 #include "internal.h"
 
