@@ -30,6 +30,7 @@ from .ops import (  # noqa: F401
     quantize_weight,
     gemm,
     grouped_gemm,
+    check_offsets,
     gemm_workspace_bytes,
     fp8_encode,
     fp8_decode,

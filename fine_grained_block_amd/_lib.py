@@ -25,6 +25,7 @@ _SIGS = {
     "fgb_grouped_w8a8_block_gemm": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _vp, _vp, ctypes.c_int, _vp,
                                                    ctypes.c_int32, _c_i64, _vp, ctypes.c_int, _c_i64, _c_i64,
                                                    _c_i64, _vp, ctypes.c_size_t, _vp]),
+    "fgb_check_expert_offsets": (ctypes.c_int, [_vp, ctypes.c_int32, _c_i64, _vp, _vp]),
     "fgb_fp8_encode": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp]),
     "fgb_fp8_decode": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp]),
     "fgb_selftest_quotients": (ctypes.c_int, [_vp, _vp]),

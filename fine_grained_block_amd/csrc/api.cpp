@@ -159,6 +159,16 @@ int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
   return launch_status(fgb::launch_gemm_grouped(a, (hipStream_t)stream));
 }
 
+int fgb_check_expert_offsets(const int32_t* expert_offsets, int32_t E, int64_t total_M, int32_t* result,
+                             void* stream) {
+  if (E <= 0 || E > 65536 || total_M < 0) return FGB_ERR_SHAPE;
+  if (!expert_offsets || !result) return FGB_ERR_NULL;
+  if (((uintptr_t)expert_offsets & 3u) || ((uintptr_t)result & 3u)) return FGB_ERR_ALIGN;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_check_offsets(expert_offsets, E, total_M, result, (hipStream_t)stream));
+}
+
 int fgb_fp8_encode(const float* in, uint8_t* out, int64_t n, int fmt, int saturate, void* stream) {
   if (n < 0) return FGB_ERR_SHAPE;
   if (fmt < FGB_FP8_E4M3 || fmt > FGB_FP8_E4M3_INT) return FGB_ERR_ENUM;

@@ -36,6 +36,8 @@ struct GemmArgs {
 // Prefill (M > 64) dense GEMM and the grouped variant.
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_check_offsets(const int32_t* offsets, int32_t E, int64_t total_M, int32_t* result,
+                                hipStream_t stream);
 
 // Split-K decode path (M <= 64).
 int decode_splits(int64_t M, int64_t N, int64_t K);

@@ -130,6 +130,17 @@ def grouped_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: t
     return out
 
 
+def check_offsets(offsets: torch.Tensor, total_M: int) -> int:
+    """Check the grouped GEMM's expert offsets on the device (synchronizes): 0 when they start at
+    0, never decrease and end at total_M, else 1 + the first index that breaks that."""
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous 1-D int32 tensor")
+    result = torch.empty(1, dtype=torch.int32, device=offsets.device)
+    st = lib().fgb_check_expert_offsets(_ptr(offsets), offsets.numel() - 1, total_M, _ptr(result), _stream())
+    check("fgb_check_expert_offsets", st)
+    return int(result.item())
+
+
 def linear(x: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
     """One fine-grained FP8 linear: dynamic activation quantization, then the block GEMM."""
     q, s_a = quantize(x)

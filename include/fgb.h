@@ -140,6 +140,17 @@ int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Debugging aid for the grouped GEMM's precondition (the expert layout of Transformers
+ * "Fine-grained FP8": rows sorted by expert, expert e owning rows offsets[e] .. offsets[e+1]-1).
+ * Writes to `result` (DEVICE int32, 4-byte aligned; read it after synchronizing the stream) 0
+ * when expert_offsets[0] == 0, the offsets are nondecreasing and expert_offsets[E] == total_M,
+ * otherwise 1 + the first index i in 0..E whose entry breaks that.  Reads the E+1 offsets only.
+ * FGB_ERR_SHAPE for E outside 1..65536 or total_M < 0, FGB_ERR_NULL, FGB_ERR_ALIGN as usual.
+ */
+int fgb_check_expert_offsets(const int32_t* expert_offsets, int32_t E, int64_t total_M, int32_t* result,
+                             void* stream);
+
+/*
  * Element-wise codecs (vLLM "FP8 W8A8", "Two FP8 representations"; UE8M0 per Transformers
  * "Fine-grained FP8", "UE8M0 scale format").
  *   encode: float32 in[n] -> u8 out[n].  E4M3: RNE, saturating to +-448 (`saturate` ignored).

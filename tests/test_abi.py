@@ -96,6 +96,17 @@ def test_gemm_validation(L):
     assert L.fgb_gemm_workspace_bytes(64, 28672, 4096) == 0
 
 
+def test_check_expert_offsets_validation(L):
+    """The offsets check validates its arguments before any device work."""
+    assert L.fgb_check_expert_offsets(FAKE, 0, 10, FAKE, None) == ERR["SHAPE"]
+    assert L.fgb_check_expert_offsets(FAKE, 65537, 10, FAKE, None) == ERR["SHAPE"]
+    assert L.fgb_check_expert_offsets(FAKE, 4, -1, FAKE, None) == ERR["SHAPE"]
+    assert L.fgb_check_expert_offsets(None, 4, 10, FAKE, None) == ERR["NULL"]
+    assert L.fgb_check_expert_offsets(FAKE, 4, 10, None, None) == ERR["NULL"]
+    assert L.fgb_check_expert_offsets(FAKE + 2, 4, 10, FAKE, None) == ERR["ALIGN"]
+    assert L.fgb_check_expert_offsets(FAKE, 4, 10, FAKE + 1, None) == ERR["ALIGN"]
+
+
 @pytest.mark.skipif(_has_gpu(), reason="fake pointers must not reach a real device")
 def test_valid_arguments_stop_at_device_check(L):
     assert _gemm(L) == ERR["DEVICE"]

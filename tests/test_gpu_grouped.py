@@ -88,6 +88,22 @@ def test_grouped_persistent(dev, fmt, K):
         check_t1(y32[rows], gemm.gemm_ref(aq[rows], sa[rows], wq[e], sw[e], fmt))
 
 
+def test_check_offsets(dev):
+    """The device check of the grouped GEMM's precondition: 0 for valid offsets (empty experts
+    included), else 1 + the first index that breaks it."""
+    def chk(vals, total):
+        return fgb.check_offsets(torch.tensor(vals, dtype=torch.int32, device=dev), total)
+    assert chk([0, 3, 3, 10], 10) == 0
+    assert chk([0, 0], 0) == 0
+    assert chk([1, 3, 3, 10], 10) == 1          # nonzero start
+    assert chk([0, 5, 4, 10], 10) == 3          # offsets[2] < offsets[1]
+    assert chk([0, 3, 3, 9], 10) == 4           # ends short of total_M
+    many = list(range(0, 700, 10))              # 70 experts: several entries per thread
+    assert chk(many, 690) == 0
+    many[65] = many[64] - 1
+    assert chk(many, 690) == 66
+
+
 @pytest.mark.parametrize("N,K", [(384, 1024), (512, 4096)])
 def test_single_expert_equals_dense(dev, N, K):
     """E = 1 equals the dense GEMM bit for bit (at (512, 4096) the grouped launch uses 256 x 256
