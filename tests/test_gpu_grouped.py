@@ -88,6 +88,31 @@ def test_grouped_persistent(dev, fmt, K):
         check_t1(y32[rows], gemm.gemm_ref(aq[rows], sa[rows], wq[e], sw[e], fmt))
 
 
+@pytest.mark.parametrize("E", [63, 64])
+def test_grouped_expert_count_edge(dev, E):
+    """63 experts fill one wave pass of the persistent form's expert table (lane 63 holds the
+    final offset); 64 take the one-tile launch's multi-pass lookup.  More tiles than CUs, empty
+    and one-row experts included; bf16 equals the RNE of the float32 output and the first and
+    last row of every expert match the oracle."""
+    rng = np.random.default_rng(E)
+    counts = rng.integers(150, 450, E)
+    counts[[0, 17, E - 1]] = [0, 1, 0]
+    N, K = 1536, 1024
+    offsets = workloads.offsets_from_counts(counts)
+    T = int(offsets[-1])
+    x = workloads.activations(T, K, key=(0, 36, 0, T))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, key=36)
+    y32 = _run(aq, sa, wq, sw, offsets, dev, torch.float32).cpu().numpy().astype(np.float64)
+    y16 = bf16_tensor_to_f64(_run(aq, sa, wq, sw, offsets, dev, torch.bfloat16))
+    assert np.array_equal(y16, gemm.bf16_rne(y32))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            rows = np.unique([lo, hi - 1])
+            check_t1(y32[rows], gemm.gemm_ref(aq[rows], sa[rows], wq[e], sw[e]))
+
+
 def test_check_offsets(dev):
     """The device check of the grouped GEMM's precondition: 0 for valid offsets (empty experts
     included), else 1 + the first index that breaks it."""
