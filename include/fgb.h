@@ -18,8 +18,9 @@
  *     (An explicitly requested backend that the hardware cannot run is an error, not a silent
  *     fallback: vLLM "FP8 W8A8", "GEMM kernel selection"; an unsupported scale format raises:
  *     Transformers "Fine-grained FP8", "UE8M0 scale format".)
- *   - Sizes and leading dimensions are in ELEMENTS.  Base pointers must be 16-byte aligned and
- *     every row pitch in bytes a multiple of 16, else FGB_ERR_ALIGN.
+ *   - Sizes and leading dimensions are in ELEMENTS.  Matrix and scale base pointers must be
+ *     16-byte aligned and every row pitch in bytes a multiple of 16 (int32 expert offsets and
+ *     status words: 4-byte aligned), else FGB_ERR_ALIGN.
  *   - M == 0 (or total_M == 0) is a valid no-op returning FGB_OK.
  *   - N and K must be multiples of 128 (the block edge), else FGB_ERR_SHAPE.
  *   - Inputs must be finite and codes must not be NaN (0x7F/0xFF); otherwise results are
