@@ -93,9 +93,3 @@ def weight_quant(w, fmt: str = "f32", block: int = GROUP):
     q = q.transpose(0, 2, 1, 3).reshape(NB * block, KB * block)[:N, :K]
     return np.ascontiguousarray(q), s
 
-
-def dequant_act(q, s, group: int = GROUP) -> np.ndarray:
-    """float64 dequantization dec(q) * s of an activation tensor (for error bounds)."""
-    M, K = q.shape
-    sx = np.repeat(np.asarray(s, dtype=np.float64), group, axis=1)[:, :K]
-    return fp8.dec_e4m3(q) * sx

@@ -108,6 +108,3 @@ def bf16_rne(y) -> np.ndarray:
     out = np.where(out > 3.3895313892515355e38, np.inf, out)
     return np.copysign(out, y)
 
-
-def bf16_bits_to_f64(b) -> np.ndarray:
-    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
