@@ -1,8 +1,12 @@
 """torch-tensor wrappers over the C-ABI (argument marshalling only).
 
 Tensors must live on the current HIP device; outputs are allocated with torch and the calls
-are enqueued on torch's current stream.  Shapes, strides and enums are validated by the
-library itself, which returns a status that is turned into FGBError (a ValueError).
+are enqueued on torch's current stream.  The C-ABI sees only base pointers and sizes, so it
+cannot tell how large a buffer is: this layer checks every tensor's dtype, device, layout and
+extent against the problem sizes before it calls the library, and raises ValueError on any
+mismatch (a transposed or sliced weight would otherwise be read out of bounds by the kernels).
+The library then validates what it can see (divisibility, leading dimensions, alignment) and
+returns a status that is turned into FGBError (also a ValueError).
 """
 from __future__ import annotations
 
@@ -31,20 +35,72 @@ def _ceil4(n: int) -> int:
     return (n + 3) // 4 * 4
 
 
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _matrix(t: torch.Tensor, name: str, dtype, rows: int | None = None, cols: int | None = None,
+            min_cols: int | None = None) -> None:
+    """t is a 2-D `dtype` tensor with unit inner stride, a row pitch of at least its width, and
+    the given row count and width (or at least `min_cols` columns)."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.dim() == 2, f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    _need(t.stride(1) == 1 and t.stride(0) >= t.shape[1], f"{name} needs unit inner stride and row pitch >= width")
+    if rows is not None:
+        _need(t.shape[0] == rows, f"{name} must have {rows} rows, got {t.shape[0]}")
+    if cols is not None:
+        _need(t.shape[1] == cols, f"{name} must have {cols} columns, got {t.shape[1]}")
+    if min_cols is not None:
+        _need(t.shape[1] >= min_cols, f"{name} must have at least {min_cols} columns, got {t.shape[1]}")
+
+
+def _dense(t: torch.Tensor, name: str, dtypes, shape: tuple) -> None:
+    """t is a contiguous tensor of exactly `shape` with one of `dtypes`."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _need(t.dtype in dtypes, f"{name} must be one of {dtypes}, got {t.dtype}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _on_device(*named) -> None:
+    """Every tensor lives on the current HIP device (checked after the shapes, so that shape
+    errors are reported without touching the device)."""
+    cur = None
+    for name, t in named:
+        if t is None:
+            continue
+        _need(t.is_cuda, f"{name} must be on the GPU, got {t.device}")
+        if cur is None:
+            cur = torch.cuda.current_device()
+        _need(t.device.index == cur, f"{name} is on {t.device}, the current device is cuda:{cur}")
+
+
+def _blocks(n: int, what: str) -> int:
+    _need(n % BLOCK == 0, f"{what} = {n} must be a multiple of {BLOCK}")
+    return n // BLOCK
+
+
 def quantize(x: torch.Tensor, out: tuple | None = None):
     """Dynamic per-token 1x128-group E4M3 quantization of bf16 activations.
 
     Returns (q uint8 [M, K], s_a float32 [K/128, ld_sa]) with ld_sa = M rounded up to 4;
-    s_a[:, :M].t() is the logical [M, K/128] scale matrix.
+    s_a[:, :M].t() is the logical [M, K/128] scale matrix.  `out` = (q, s_a) writes into given
+    buffers: q uint8 [M, K] and s_a float32 [K/128, >= M], both with unit inner stride.
     """
-    if x.dtype != torch.bfloat16:
-        raise ValueError("quantize expects bf16 activations")
+    _matrix(x, "x", torch.bfloat16)
     M, K = x.shape
+    KB = _blocks(K, "K")
     if out is None:
+        _on_device(("x", x))
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-        s_a = torch.empty((K // BLOCK if K % BLOCK == 0 else 0, max(_ceil4(M), 4)), dtype=torch.float32, device=x.device)
+        s_a = torch.empty((KB, max(_ceil4(M), 4)), dtype=torch.float32, device=x.device)
     else:
         q, s_a = out
+        _matrix(q, "q", torch.uint8, rows=M, cols=K)
+        _matrix(s_a, "s_a", torch.float32, rows=KB, min_cols=M)
+        _on_device(("x", x), ("q", q), ("s_a", s_a))
     st = lib().fgb_act_quant_group128(_ptr(x), M, K, _row_ld(x), _ptr(q), _row_ld(q), _ptr(s_a),
                                       s_a.stride(0), _stream())
     check("fgb_act_quant_group128", st)
@@ -56,15 +112,17 @@ def quantize_weight(w: torch.Tensor, scale_fmt: str = "float"):
 
     scale_fmt "float" -> s_w float32 [N/128, K/128]; "ue8m0" -> s_w uint8 UE8M0 codes.
     """
-    if w.dtype != torch.bfloat16 or not w.is_contiguous():
-        raise ValueError("quantize_weight expects a contiguous bf16 [N, K] tensor")
+    _need(isinstance(w, torch.Tensor) and w.dim() == 2, "quantize_weight expects a 2-D tensor")
+    _dense(w, "w", (torch.bfloat16,), tuple(w.shape))
     N, K = w.shape
+    NB, KB = _blocks(N, "N"), _blocks(K, "K")
     fmt = {"float": SCALE_F32, "ue8m0": SCALE_UE8M0}.get(scale_fmt)
     if fmt is None:
         raise ValueError("scale_fmt must be 'float' or 'ue8m0'")
+    _on_device(("w", w))
     w_q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     sdt = torch.float32 if fmt == SCALE_F32 else torch.uint8
-    s_w = torch.empty((max(N // BLOCK, 1), max(K // BLOCK, 1)), dtype=sdt, device=w.device)
+    s_w = torch.empty((max(NB, 1), max(KB, 1)), dtype=sdt, device=w.device)
     st = lib().fgb_weight_quant_block128(_ptr(w), N, K, _ptr(w_q), _ptr(s_w), fmt, _stream())
     check("fgb_weight_quant_block128", st)
     return w_q, s_w
@@ -90,12 +148,37 @@ def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().fgb_gemm_workspace_bytes(M, N, K))
 
 
+def _check_gemm_operands(a_q, s_a, w_q, s_w, out, E: int | None):
+    """Shapes of the GEMM operands against M (rows of a_q), N, K (and E for grouped)."""
+    _matrix(a_q, "a_q", torch.uint8)
+    M, K = a_q.shape
+    KB = _blocks(K, "K")
+    _need(isinstance(w_q, torch.Tensor), "w_q must be a torch.Tensor")
+    N = w_q.shape[-2] if w_q.dim() >= 2 else -1
+    _need(w_q.dim() == (2 if E is None else 3), f"w_q must be {'[N, K]' if E is None else '[E, N, K]'}")
+    NB = _blocks(N, "N")
+    lead = () if E is None else (E,)
+    _dense(w_q, "w_q", (torch.uint8,), lead + (N, K))
+    _dense(s_w, "s_w", (torch.float32, torch.uint8), lead + (NB, KB))
+    _matrix(s_a, "s_a", torch.float32, rows=KB, min_cols=M)
+    if out is not None:
+        _need(out.dtype in (torch.bfloat16, torch.float32), "out must be bf16 or float32")
+        _matrix(out, "out", out.dtype, rows=M, cols=N)
+    return M, N, K
+
+
 def gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor,
          out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
          workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y = block-scaled (A_q . W_q^T) with 1x128 activation and 128x128 weight scales."""
-    M, K = a_q.shape
-    N = w_q.shape[0]
+    """y = block-scaled (A_q . W_q^T) with 1x128 activation and 128x128 weight scales.
+
+    a_q uint8 [M, K] (unit inner stride); s_a float32 [K/128, >= M]; w_q uint8 [N, K] and s_w
+    [N/128, K/128] (float32 or UE8M0 bytes), both contiguous; out [M, N] bf16 or float32.
+    """
+    M, N, K = _check_gemm_operands(a_q, s_a, w_q, s_w, out, None)
+    if workspace is not None:
+        _need(workspace.is_contiguous(), "workspace must be contiguous")
+    _on_device(("a_q", a_q), ("s_a", s_a), ("w_q", w_q), ("s_w", s_w), ("out", out), ("workspace", workspace))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
     need = gemm_workspace_bytes(M, N, K)
@@ -114,12 +197,14 @@ def grouped_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: t
                  out: torch.Tensor | None = None) -> torch.Tensor:
     """MoE grouped GEMM: rows offsets[e]..offsets[e+1]-1 use expert e's weights and scales.
 
-    offsets: int32 device tensor [E+1] (0, nondecreasing, ends at a_q.shape[0]).
+    w_q uint8 [E, N, K], s_w [E, N/128, K/128] contiguous; offsets: contiguous int32 device
+    tensor [E+1] (0, nondecreasing, ends at a_q.shape[0]).
     """
-    total_M, K = a_q.shape
-    E, N, _ = w_q.shape
-    if offsets.dtype != torch.int32 or offsets.numel() != E + 1:
-        raise ValueError("offsets must be an int32 tensor with E+1 entries")
+    _need(isinstance(w_q, torch.Tensor) and w_q.dim() == 3, "w_q must be [E, N, K]")
+    E = w_q.shape[0]
+    total_M, N, K = _check_gemm_operands(a_q, s_a, w_q, s_w, out, E)
+    _dense(offsets, "offsets", (torch.int32,), (E + 1,))
+    _on_device(("a_q", a_q), ("s_a", s_a), ("w_q", w_q), ("s_w", s_w), ("offsets", offsets), ("out", out))
     if out is None:
         out = torch.empty((total_M, N), dtype=out_dtype, device=a_q.device)
     st = lib().fgb_grouped_w8a8_block_gemm(_ptr(a_q), _row_ld(a_q), _ptr(s_a), s_a.stride(0), _ptr(w_q),
@@ -133,8 +218,9 @@ def grouped_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: t
 def check_offsets(offsets: torch.Tensor, total_M: int) -> int:
     """Check the grouped GEMM's expert offsets on the device (synchronizes): 0 when they start at
     0, never decrease and end at total_M, else 1 + the first index that breaks that."""
-    if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
-        raise ValueError("offsets must be a contiguous 1-D int32 tensor")
+    _need(isinstance(offsets, torch.Tensor) and offsets.dim() == 1, "offsets must be 1-D")
+    _dense(offsets, "offsets", (torch.int32,), tuple(offsets.shape))
+    _on_device(("offsets", offsets))
     result = torch.empty(1, dtype=torch.int32, device=offsets.device)
     st = lib().fgb_check_expert_offsets(_ptr(offsets), offsets.numel() - 1, total_M, _ptr(result), _stream())
     check("fgb_check_expert_offsets", st)
@@ -150,6 +236,7 @@ def linear(x: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor, out_dtype=torc
 def fp8_encode(x: torch.Tensor, fmt: int = FP8_E4M3, saturate: bool = True) -> torch.Tensor:
     if x.dtype != torch.float32 or not x.is_contiguous():
         raise ValueError("fp8_encode expects a contiguous float32 tensor")
+    _on_device(("x", x))
     out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     check("fgb_fp8_encode", lib().fgb_fp8_encode(_ptr(x), _ptr(out), x.numel(), fmt, int(saturate), _stream()))
     return out
@@ -158,6 +245,7 @@ def fp8_encode(x: torch.Tensor, fmt: int = FP8_E4M3, saturate: bool = True) -> t
 def fp8_decode(c: torch.Tensor, fmt: int = FP8_E4M3) -> torch.Tensor:
     if c.dtype != torch.uint8 or not c.is_contiguous():
         raise ValueError("fp8_decode expects a contiguous uint8 tensor")
+    _on_device(("c", c))
     out = torch.empty(c.shape, dtype=torch.float32, device=c.device)
     check("fgb_fp8_decode", lib().fgb_fp8_decode(_ptr(c), _ptr(out), c.numel(), fmt, _stream()))
     return out
