@@ -126,9 +126,11 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   const int lane0 = threadIdx.x & 63;
   auto expert_chunk = [&](int e0, int& off, int& nxt, int& mt, int& inc) {
     const int idx = e0 + lane0;
-    off = idx <= p.E ? gload<int>(p.offsets + idx) : 0;
+    // offsets are a precondition; clamped to 0..M, and an expert whose end lies before its start
+    // gets no tiles, so that bad offsets cannot move a tile's rows outside 0..M-1
+    off = idx <= p.E ? min(max(gload<int>(p.offsets + idx), 0), (int)p.M) : 0;
     nxt = __shfl_down(off, 1);
-    mt = lane0 < 63 && idx < p.E ? (nxt - off + C::BM - 1) / C::BM : 0;
+    mt = lane0 < 63 && idx < p.E && nxt > off ? (nxt - off + C::BM - 1) / C::BM : 0;
     inc = mt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -182,6 +184,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       }
       cum += __shfl(inc, 62);
     }
+    if (e < 0) return;  // (cannot happen: the real tile count is the prefix sum searched here)
     row0 = (int64_t)r0 + (int64_t)(pid_m - cum) * C::BM;
     row_end = r1;
     wq += (int64_t)e * N * K;
@@ -477,9 +480,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
   int c_off = 0, c_inc = 0;
   int real_tiles_m = tiles_m;
   if constexpr (GROUPED) {
-    c_off = lane <= p.E ? gload<int>(p.offsets + lane) : 0;
+    // clamped to 0..M, and no tiles for an expert whose end lies before its start (bad offsets
+    // then cannot move a tile's rows outside 0..M-1)
+    c_off = lane <= p.E ? min(max(gload<int>(p.offsets + lane), 0), (int)M) : 0;
     const int nxt = __shfl_down(c_off, 1);
-    c_inc = lane < p.E ? (nxt - c_off + C::BM - 1) / C::BM : 0;
+    c_inc = lane < p.E && nxt > c_off ? (nxt - c_off + C::BM - 1) / C::BM : 0;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int t = __shfl_up(c_inc, d);

@@ -251,12 +251,13 @@ def fp8_decode(c: torch.Tensor, fmt: int = FP8_E4M3) -> torch.Tensor:
     return out
 
 
-def selftest_quotients() -> tuple[int, int]:
+def selftest_quotients() -> tuple[int, int, int]:
     """Exhaustive device check of the quantizers' fast quotient (see include/fgb.h).
 
-    Returns (pairs with differing E4M3 codes, pairs with differing float32 quotients).
+    Returns (pairs with differing E4M3 codes, pairs with differing float32 quotients, pairs with
+    differing quotients of magnitude >= 2^-13).
     """
-    counts = torch.zeros(2, dtype=torch.int64, device=torch.device("cuda", torch.cuda.current_device()))
+    counts = torch.zeros(3, dtype=torch.int64, device=torch.device("cuda", torch.cuda.current_device()))
     check("fgb_selftest_quotients", lib().fgb_selftest_quotients(_ptr(counts), _stream()))
     c = counts.cpu().tolist()
-    return int(c[0]), int(c[1])
+    return int(c[0]), int(c[1]), int(c[2])

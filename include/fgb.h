@@ -165,11 +165,13 @@ int fgb_fp8_decode(const uint8_t* in, float* out, int64_t n, int fmt, void* stre
 /*
  * Self-test of the quantizers' division.  The codes are defined with the IEEE float32 quotient
  * x / s; the kernels form it as a correctly rounded reciprocal of s plus one FMA correction per
- * element.  This call checks, for every positive finite bf16 amax and every bf16 x with
- * |x| <= amax (both signs; about 1.07e9 pairs), s = fl32(amax/448) and both quotients, and
- * ADDS to the device counters: counts[0] += pairs whose E4M3 codes differ, counts[1] += pairs
- * whose float32 quotients differ in any bit.  counts: device, 2 x uint64, 8-byte aligned; the
- * caller zeroes them.
+ * element, which is the IEEE quotient except where the FMA residual leaves the float32 normal
+ * range (tiny x only; the quotient is then below 2^-13 and encodes as +-0 either way).  This
+ * call checks, for every positive finite bf16 amax and every bf16 x with |x| <= amax (both
+ * signs; about 1.07e9 pairs), s = fl32(amax/448) and both quotients, and ADDS to the device
+ * counters: counts[0] += pairs whose E4M3 codes differ, counts[1] += pairs whose float32
+ * quotients differ in any bit, counts[2] += those of them whose IEEE quotient has magnitude
+ * >= 2^-13.  counts: device, 3 x uint64, 8-byte aligned; the caller zeroes them.
  */
 int fgb_selftest_quotients(unsigned long long* counts, void* stream);
 

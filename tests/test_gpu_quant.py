@@ -118,6 +118,9 @@ def test_weight_quant(dev, fmt):
 def test_fast_quotient_selftest(dev):
     """The quantizers' reciprocal-and-correct quotient gives the IEEE quotient's E4M3 code for
     every positive finite bf16 amax and every bf16 |x| <= amax, both signs (~1.07e9 pairs)."""
-    code_bad, quot_bad = fgb.selftest_quotients()
+    code_bad, quot_bad, quot_bad_big = fgb.selftest_quotients()
     assert code_bad == 0
-    print(f"float32 quotient mismatches (codes equal): {quot_bad}")
+    # the last-bit differences come only from residuals below the float32 normal range, i.e.
+    # tiny quotients, which encode as +-0 whichever way they round
+    assert quot_bad_big == 0
+    print(f"float32 quotient mismatches (codes equal, all below 2^-13): {quot_bad}")
