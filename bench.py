@@ -1,17 +1,18 @@
 """Benchmark: fine-grained FP8 W8A8 linears on one MI355X.
 
-A step is one pass of the hot path over the Llama-3-8B-shaped prefill batch (M = 4096 tokens):
-for each of the four projections (QKV 6144x4096, O 4096x4096, gate+up 28672x4096, down
-4096x14336) the bf16 activations are quantized dynamically (1x128 groups) and the block-scaled
-FP8 GEMM produces bf16 outputs.  Weights are quantized once beforehand (offline, untimed);
-activations are resident in HBM when the timed region starts.
+A step is one pass of the hot path over the DeepSeek-V3-shaped prefill batch (M = 8192 tokens,
+the largest single-GPU configuration): for each of the four projections (q_b 24576x1536,
+o 7168x16384, gate+up 36864x7168, down 7168x18432) the bf16 activations are quantized
+dynamically (1x128 groups, float32 scales) and the block-scaled FP8 GEMM with UE8M0 (power-of-two)
+128x128 weight scales produces bf16 outputs.  Weights are quantized once beforehand (offline,
+untimed); activations are resident in HBM when the timed region starts.
 
 Prints ONE JSON line.  `value` is the whole step's useful GEMM throughput (2*M*N*K summed over
 the four projections, divided by the step time, quantization included).  `roofline` is for the
-dominant kernel (the prefill GEMM), from HIP events recorded around every GEMM launch on the
+dominant kernel (the prefill GEMM), from HIP events recorded around every GEMM call on the
 launch stream inside the timed region.  `cpu_baseline` times the CPU oracle on a bounded sample
-of the same workload.  `extra` carries the other rows of the hot path (decode, UE8M0 prefill,
-grouped MoE, quantization bandwidth), each timed on its own.
+of the same workload.  `extra` carries the other rows of the hot path (the Llama-3-8B prefill
+step, decode, grouped MoE, quantization bandwidth), each timed on its own.
 """
 from __future__ import annotations
 
@@ -36,10 +37,11 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--suite", choices=["step", "all"], default="all",
-                   help="'step': only the headline step; 'all': also decode, UE8M0 prefill, MoE, quant")
+                   help="'step': only the headline step; 'all': also the Llama-3-8B step, decode, cold UE8M0 "
+                        "prefill calls, MoE, quant")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=4096, help="tokens in the oracle sample")
-    p.add_argument("--cpu-cols", type=int, default=4096, help="output features per projection in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="tokens in the oracle sample")
+    p.add_argument("--cpu-cols", type=int, default=1024, help="output features per projection in the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     p.add_argument("--derive-traffic", metavar="PMC_DIR",
@@ -58,18 +60,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def derive_traffic(pmc_dir: str) -> dict:
-    """HBM bytes per prefill-GEMM call of the Llama step from two rocprofv3 counter runs.
+def derive_traffic(pmc_dir: str, names=None) -> dict:
+    """HBM bytes per prefill-GEMM call of the headline step from two rocprofv3 counter runs.
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by 1 GiB over what the same
     counter read for the 1 GiB device copy (__amd_rocclr_copyBuffer) of the same run.  A
     projection's GEMM call is every GEMM dispatch between its act_quant dispatch and the next one
-    (QKV runs as two dispatches); the projections repeat in step order.
+    (a call can be two dispatches: 256x256 and 256x128 tiles); the projections repeat in step
+    order.
     """
     import collections
     import csv
 
-    names = ("qkv", "o", "gate_up", "down")
+    if names is None:
+        import workloads
+        names = tuple(n for n, _, _ in workloads.DEEPSEEK_V3_LINEARS)
+    P = len(names)
 
     def load(counter):
         per = collections.OrderedDict()
@@ -96,36 +102,45 @@ def derive_traffic(pmc_dir: str) -> dict:
             elif "gemm_prefill" in name and calls:
                 calls[-1] += v * 1024 * factor
                 disp[-1] += 1
-        if not calls or len(calls) % 4:
-            raise SystemExit(f"{counter}: {len(calls)} projection calls, expected whole steps of 4")
+        if not calls or len(calls) % P:
+            raise SystemExit(f"{counter}: {len(calls)} projection calls, expected whole steps of {P}")
         for i, nm in enumerate(names):
-            vals = calls[i::4]
+            vals = calls[i::P]
             e = out["per_projection"].setdefault(nm, {})
             e[counter.lower() + "_bytes"] = round(sum(vals) / len(vals))
             e["dispatches"] = disp[i]
         per_call += sum(calls) / len(calls)
     out["gemm_prefill_hbm_bytes_per_call"] = round(per_call)
-    out["note"] = ("calibrated HBM fetch + write bytes per prefill-GEMM call of the Llama step, mean "
-                   "over the four projections' calls (QKV's call is two dispatches: 256x256 and "
-                   "256x128 tiles)")
+    out["note"] = ("calibrated HBM fetch + write bytes per prefill-GEMM call of the headline step, mean "
+                   "over its projections' calls")
     return out
 
 
-def headline_step(args, torch, fgb, workloads, np):
-    dev = torch.device("cuda:0")
-    M = workloads.LLAMA3_8B_PREFILL_M
-    layers = []
-    for i, (name, N, K) in enumerate(workloads.LLAMA3_8B_LINEARS):
-        x = torch.from_numpy(workloads.activations(M, K, key=(0, 1, 0, i)).view(np.int16)).to(dev).view(torch.bfloat16)
-        w = torch.from_numpy(workloads.weights(N, K, key=(0, 1, 1, i)).view(np.int16)).to(dev).view(torch.bfloat16)
-        wq, sw = fgb.quantize_weight(w)  # offline
+def _dev_inputs(torch, fgb, workloads, linears, M, scale_fmt, seed0, dev, host_rows=0, host_cols=0):
+    """Per projection: bf16 activations [M, K] and quantized weights (offline), drawn on the device
+    with seeded generators; optionally the first host_rows activation rows and host_cols weight rows
+    copied back as bf16 bit patterns (for the CPU baseline's sample)."""
+    import numpy as np
+    layers, host = [], []
+    for i, (name, N, K) in enumerate(linears):
+        w = workloads.device_bf16((N, K), seed0 + 2 * i + 1, dev, outliers=False, std=0.02)
+        wq, sw = fgb.quantize_weight(w, scale_fmt)  # offline
+        x = workloads.device_bf16((M, K), seed0 + 2 * i, dev)
+        if host_rows:
+            host.append((x[:host_rows].view(torch.int16).cpu().numpy().view(np.uint16),
+                         w[:host_cols].view(torch.int16).cpu().numpy().view(np.uint16)))
         del w
         q = torch.empty((M, K), dtype=torch.uint8, device=dev)
         sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         layers.append(dict(name=name, N=N, K=K, x=x, wq=wq, sw=sw, q=q, sa=sa, y=y))
     torch.cuda.synchronize()
+    return layers, host
 
+
+def run_step(torch, fgb, layers, M, steps, warmup):
+    """Time `steps` back-to-back steps (act_quant + GEMM per projection) after `warmup` untimed
+    ones; HIP events around every call on the launch stream give the per-call times."""
     def step(ev=None):
         for j, L in enumerate(layers):
             if ev is not None:
@@ -137,30 +152,59 @@ def headline_step(args, torch, fgb, workloads, np):
             if ev is not None:
                 ev[j][2].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(args.steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
-    for s in range(args.steps):
+    for s in range(steps):
         step(evs[s])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    gemm_ms = [sum(evs[s][j][1].elapsed_time(evs[s][j][2]) for s in range(args.steps)) / args.steps for j in range(len(layers))]
-    quant_ms = [sum(evs[s][j][0].elapsed_time(evs[s][j][1]) for s in range(args.steps)) / args.steps for j in range(len(layers))]
+    ms_step = e0.elapsed_time(e1) / steps
+    gemm_ms = [sum(evs[s][j][1].elapsed_time(evs[s][j][2]) for s in range(steps)) / steps for j in range(len(layers))]
+    quant_ms = [sum(evs[s][j][0].elapsed_time(evs[s][j][1]) for s in range(steps)) / steps for j in range(len(layers))]
     flops = [2.0 * M * L["N"] * L["K"] for L in layers]
     qbytes = [3.03125 * M * L["K"] for L in layers]
     per = {}
     for L, g, q, f, b in zip(layers, gemm_ms, quant_ms, flops, qbytes):
         per[L["name"]] = dict(N=L["N"], K=L["K"], gemm_us=round(g * 1e3, 1), gemm_tflops=round(f / g / 1e9, 1),
+                              frac_mfma=round(f / g / 1e9 / PEAK_FP8_TFLOPS, 3),
                               quant_us=round(q * 1e3, 1), quant_gbs=round(b / q / 1e6, 1))
     return dict(M=M, ms_step=ms_step, wall_s=wall, gemm_ms=gemm_ms, quant_ms=quant_ms, flops=flops,
                 qbytes=qbytes, per=per)
+
+
+def headline_step(args, torch, fgb, workloads):
+    """The DeepSeek-V3-shaped step (M = 8192, UE8M0 weight scales)."""
+    dev = torch.device("cuda:0")
+    M = workloads.DEEPSEEK_V3_PREFILL_M
+    want_host = not args.no_cpu_baseline
+    layers, host = _dev_inputs(torch, fgb, workloads, workloads.DEEPSEEK_V3_LINEARS, M, "ue8m0", 4000, dev,
+                               args.cpu_rows if want_host else 0, args.cpu_cols if want_host else 0)
+    res = run_step(torch, fgb, layers, M, args.steps, args.warmup)
+    del layers
+    torch.cuda.empty_cache()
+    res["host_sample"] = host
+    return res
+
+
+def llama_step(args, torch, fgb, workloads):
+    """The Llama-3-8B-shaped step (M = 4096, float32 weight scales), reported in `extra`."""
+    dev = torch.device("cuda:0")
+    M = workloads.LLAMA3_8B_PREFILL_M
+    layers, _ = _dev_inputs(torch, fgb, workloads, workloads.LLAMA3_8B_LINEARS, M, "float", 3000, dev)
+    res = run_step(torch, fgb, layers, M, args.steps, args.warmup)
+    del layers
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=round(res["ms_step"], 4),
+                tflops=round(sum(res["flops"]) / (res["ms_step"] * 1e-3) / 1e12, 1),
+                gemm_frac_mfma=round(sum(res["flops"]) / (sum(res["gemm_ms"]) * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                per_projection=res["per"])
 
 
 # ---------------------------------------------------------------------------------------------
@@ -211,10 +255,12 @@ def extra_suites(torch, fgb, workloads, np):
         return next(seeds)
 
     out = {}
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # read-only cache flush: a sum over 512 MB of other data (twice the 256 MB MALL) evicts the
+    # operands without leaving dirty lines that would drain during the next timed call
+    flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
 
     def flush():
-        flush_buf.fill_(1)
+        flush_buf.sum()
 
     # decode — hipGraph loop over rotating weight copies (> 2x MALL in total)
     dec = {}
@@ -236,7 +282,8 @@ def extra_suites(torch, fgb, workloads, np):
         del wqs, wq0
     out["decode"] = dec
 
-    # DeepSeek-V3-shaped prefill with UE8M0 weight scales (M = 8192), flushed between calls
+    # DeepSeek-V3-shaped prefill with UE8M0 weight scales (M = 8192), each call alone with cold
+    # caches (the headline step runs the same calls back to back)
     ds = {}
     M = workloads.DEEPSEEK_V3_PREFILL_M
     for (name, N, K) in workloads.DEEPSEEK_V3_LINEARS:
@@ -250,7 +297,7 @@ def extra_suites(torch, fgb, workloads, np):
         f = 2.0 * M * N * K
         ds[f"{name}_{N}x{K}"] = dict(us=round(us, 1), tflops=round(f / us / 1e6, 1), frac_mfma=round(f / us / 1e6 / PEAK_FP8_TFLOPS, 3))
         del wq, x, q, y
-    out["prefill_ue8m0_m8192"] = ds
+    out["prefill_ue8m0_m8192_cold"] = ds
 
     # MoE grouped GEMM: 32 experts, 4096 tokens top-8 Zipf(1.1)
     moe = {}
@@ -291,23 +338,22 @@ def extra_suites(torch, fgb, workloads, np):
 
 
 # ---------------------------------------------------------------------------------------------
-def cpu_baseline(args, workloads, np):
-    """The CPU oracle (as it is) on a bounded sample of the step: the first `cpu_rows` tokens and
-    the first `cpu_cols` output features of each projection, full K; act_quant + gemm_ref.
+def cpu_baseline(args, host_sample, workloads, np):
+    """The CPU oracle (as it is) on a bounded sample of the headline step: the first `cpu_rows`
+    tokens and the first `cpu_cols` output features of each projection, full K; act_quant +
+    gemm_ref with UE8M0 weight scales.  The sample's bf16 bytes are those the GPU step used.
     Weight quantization of the sampled rows is offline (untimed), as on the GPU."""
     from oracle import blockquant, gemm
     R, C = args.cpu_rows, args.cpu_cols
     prepared = []
-    for i, (name, N, K) in enumerate(workloads.LLAMA3_8B_LINEARS):
-        x = workloads.activations(workloads.LLAMA3_8B_PREFILL_M, K, key=(0, 1, 0, i))[:R]
-        w = workloads.weights(N, K, key=(0, 1, 1, i))[:C]
-        wq, sw = blockquant.weight_quant(w)
+    for (x, w), (name, N, K) in zip(host_sample, workloads.DEEPSEEK_V3_LINEARS):
+        wq, sw = blockquant.weight_quant(w, "ue8m0")
         prepared.append((x, wq, sw, K))
     t0 = time.perf_counter()
     flops = 0.0
     for x, wq, sw, K in prepared:
         aq, sa = blockquant.act_quant(x)
-        gemm.gemm_ref(aq, sa, wq, sw)
+        gemm.gemm_ref(aq, sa, wq, sw, "ue8m0")
         flops += 2.0 * R * C * K
     dt = time.perf_counter() - t0
     try:
@@ -316,8 +362,9 @@ def cpu_baseline(args, workloads, np):
         cores = os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=min(cores, threads), kind="oracle",
-                sample=f"first {R} tokens x first {C} output features of each of the 4 projections, full K "
-                       f"(act_quant + exact-partial float64 gemm_ref); {flops / 1e9:.2f} GFLOP in {dt:.1f} s")
+                sample=f"first {R} tokens x first {C} output features of each of the 4 DeepSeek-V3-shaped "
+                       f"projections at M = 8192, full K, UE8M0 weight scales (act_quant + exact-partial "
+                       f"float64 gemm_ref); {flops / 1e9:.2f} GFLOP in {dt:.1f} s")
 
 
 def main():
@@ -347,7 +394,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    res = headline_step(args, torch, fgb, workloads, np)
+    res = headline_step(args, torch, fgb, workloads)
     total_flops = sum(res["flops"])
     gemm_total_ms = sum(res["gemm_ms"])
     achieved = total_flops / (gemm_total_ms * 1e-3) / 1e12  # TFLOP/s over the GEMM launches
@@ -360,8 +407,9 @@ def main():
         if t.get("kernel_source_hash") == extra["kernel_source_hash"]:
             traffic = t.get("gemm_prefill_hbm_bytes_per_call")
     if args.suite == "all":
+        extra["llama3_8b_prefill_m4096_step"] = llama_step(args, torch, fgb, workloads)
         extra.update(extra_suites(torch, fgb, workloads, np))
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args, workloads, np)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, res["host_sample"], workloads, np)
     line = {
         "metric": "block-FP8 GEMM TFLOPS (% of FP8 MFMA peak); quant/decode GB/s (% HBM)",
         "value": round(total_flops / (res["ms_step"] * 1e-3) / 1e12, 2),
@@ -374,10 +422,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
-        "data": "synthetic (seeded: x ~ N(0,1) with 1% x20 outliers, W ~ N(0,0.02), bf16)",
-        "config": {"workload": "llama3_8b_prefill_m4096: act_quant_group128 + w8a8_block_gemm for "
-                               "qkv 6144x4096, o 4096x4096, gate_up 28672x4096, down 4096x14336; "
-                               "fp32 128x128 weight scales, bf16 out",
+        "data": "synthetic (seeded on the device: x ~ N(0,1) with 1% x20 outliers, W ~ N(0,0.02), bf16)",
+        "config": {"workload": "deepseek_v3_prefill_m8192_ue8m0: act_quant_group128 + w8a8_block_gemm for "
+                               "q_b 24576x1536, o 7168x16384, gate_up 36864x7168, down 7168x18432; "
+                               "UE8M0 128x128 weight scales, float32 1x128 activation scales, bf16 out",
                    "M": res["M"], "parallelism": "single_gpu"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic},

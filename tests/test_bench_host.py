@@ -35,7 +35,7 @@ def _step_rows(scale):
 def test_derive_traffic_groups_dispatches_into_projection_calls(tmp_path):
     _write_pass(str(tmp_path), "FETCH_SIZE", _step_rows(1))
     _write_pass(str(tmp_path), "WRITE_SIZE", _step_rows(2))
-    t = bench.derive_traffic(str(tmp_path))
+    t = bench.derive_traffic(str(tmp_path), names=("qkv", "o", "gate_up", "down"))
     assert t["fetch_size_copy_factor"] == pytest.approx(2.0)
     # WRITE_SIZE's copy dispatch reads the same 2^19 KiB, so its factor is also 2
     kib = 1024 * 2.0
@@ -55,4 +55,4 @@ def test_derive_traffic_rejects_a_partial_step(tmp_path):
     _write_pass(str(tmp_path), "FETCH_SIZE", rows)
     _write_pass(str(tmp_path), "WRITE_SIZE", rows)
     with pytest.raises(SystemExit):
-        bench.derive_traffic(str(tmp_path))
+        bench.derive_traffic(str(tmp_path), names=("qkv", "o", "gate_up", "down"))
