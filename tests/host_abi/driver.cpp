@@ -1,0 +1,137 @@
+// Calls every entry point of include/fgb.h with invalid and valid arguments against the host
+// stand-ins of stub.cpp; built with AddressSanitizer and UBSan by tests/test_abi_sanitized.py.
+// Exits nonzero on the first unexpected status (and the sanitizers abort on any memory error
+// or undefined behaviour in the validation code).
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/fgb.h"
+#include "stub.h"
+
+static int failures = 0;
+#define EXPECT(call, want)                                                                    \
+  do {                                                                                        \
+    int got_ = (call);                                                                        \
+    if (got_ != (want)) {                                                                     \
+      fprintf(stderr, "%s:%d: %s returned %d, expected %d\n", __FILE__, __LINE__, #call, got_, \
+              (int)(want));                                                                   \
+      failures++;                                                                             \
+    }                                                                                         \
+  } while (0)
+
+static void* P(uintptr_t v) { return (void*)v; }
+static const uintptr_t F = 0x10000;  // a 16-byte aligned address that is never dereferenced
+
+static int gemm(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ld_sa, int64_t ldy, int fmt = 0, int ydt = 0,
+                uintptr_t a = F, uintptr_t ws = 0, size_t wsb = 0) {
+  return fgb_w8a8_block_gemm((const uint8_t*)P(a), lda, (const float*)P(F), ld_sa, (const uint8_t*)P(F), P(F), fmt,
+                             P(F), ydt, ldy, M, N, K, P(ws), wsb, nullptr);
+}
+
+int main() {
+  // status strings and version
+  for (int s = 0; s >= -8; --s)
+    if (!fgb_status_string(s) || strncmp(fgb_status_string(s), "FGB_", 4) != 0) failures++;
+  if (strcmp(fgb_status_string(77), "unknown fgb status") != 0) failures++;
+  EXPECT(fgb_abi_version(), FGB_ABI_VERSION);
+
+  // GEMM validation
+  EXPECT(gemm(256, 512, 1000, 1008, 256, 512), FGB_ERR_SHAPE);
+  EXPECT(gemm(256, 500, 1024, 1024, 256, 512), FGB_ERR_SHAPE);
+  EXPECT(gemm(-1, 512, 1024, 1024, 256, 512), FGB_ERR_SHAPE);
+  EXPECT(gemm((int64_t)1 << 40, 512, 1024, 1024, 256, 512), FGB_ERR_SHAPE);
+  EXPECT(gemm(0, 512, 1024, 1024, 256, 512), FGB_OK);
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512, 2), FGB_ERR_ENUM);
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512, 0, 5), FGB_ERR_ENUM);
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512, 0, 0, 0), FGB_ERR_NULL);
+  EXPECT(gemm(256, 512, 1024, 512, 256, 512), FGB_ERR_STRIDE);
+  EXPECT(gemm(256, 512, 1024, 1024, 100, 512), FGB_ERR_STRIDE);
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 256), FGB_ERR_STRIDE);
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512, 0, 0, F + 8), FGB_ERR_ALIGN);
+  EXPECT(gemm(256, 512, 1024, 1032, 256, 512), FGB_ERR_ALIGN);
+  EXPECT(gemm(256, 512, 1024, 1024, 258, 512), FGB_ERR_ALIGN);
+  EXPECT(gemm(256, 512, 65536, 65536, 256, 512), FGB_ERR_SHAPE);       // K above 32768
+  EXPECT(gemm(65536, 512, 1024, 65536, 65536, 512), FGB_ERR_SHAPE);    // A beyond 32-bit offsets
+  // valid prefill call reaches the prefill launcher with the sizes given
+  g_stub.launches = 0;
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512), FGB_OK);
+  if (g_stub.launches != 1 || strcmp(g_stub.last, "gemm_prefill") || g_stub.M != 256 || g_stub.N != 512 ||
+      g_stub.K != 1024)
+    failures++;
+  // decode: M <= 64; a workspace is required when the plan asks for one
+  EXPECT(gemm(32, 4096, 4096, 4096, 32, 4096), FGB_ERR_WORKSPACE);
+  EXPECT(gemm(32, 4096, 4096, 4096, 32, 4096, 0, 0, F, F, (1u << 20) - 1), FGB_ERR_WORKSPACE);
+  EXPECT(gemm(32, 4096, 4096, 4096, 32, 4096, 0, 0, F, F + 4, 1u << 20), FGB_ERR_ALIGN);
+  EXPECT(gemm(32, 4096, 4096, 4096, 32, 4096, 0, 0, F, F, 1u << 20), FGB_OK);
+  if (strcmp(g_stub.last, "gemm_decode") || g_stub.workspace != P(F)) failures++;
+  EXPECT(gemm(8, 4096, 4096, 4096, 8, 4096), FGB_OK);
+  EXPECT(fgb_gemm_workspace_bytes(65, 4096, 4096), 0);
+  EXPECT(fgb_gemm_workspace_bytes(32, 4096, 4096) > 0, 1);
+  // launch failure and device checks
+  g_stub.launch_error = 1;
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512), FGB_ERR_LAUNCH);
+  g_stub.launch_error = 0;
+  g_stub.get_device_fails = 1;
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512), FGB_ERR_DEVICE);
+  g_stub.get_device_fails = 0;
+  g_stub.device = 1;
+  g_stub.arch = "gfx942:sramecc+:xnack-";
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512), FGB_ERR_DEVICE);
+  g_stub.device = 70;  // beyond the library's device table
+  EXPECT(gemm(256, 512, 1024, 1024, 256, 512), FGB_ERR_DEVICE);
+  g_stub.device = 0;
+  g_stub.arch = "gfx950:sramecc+:xnack-";
+
+  // grouped GEMM
+  auto grouped = [](int32_t E, int64_t tM, uintptr_t off, int64_t N = 512) {
+    return fgb_grouped_w8a8_block_gemm((const uint8_t*)P(F), 1024, (const float*)P(F), 256, (const uint8_t*)P(F),
+                                       P(F), 0, (const int32_t*)P(off), E, tM, P(F), 0, 512, N, 1024, nullptr, 0,
+                                       nullptr);
+  };
+  EXPECT(grouped(0, 256, F), FGB_ERR_SHAPE);
+  EXPECT(grouped(65537, 256, F), FGB_ERR_SHAPE);
+  EXPECT(grouped(4, 256, 0), FGB_ERR_NULL);
+  EXPECT(grouped(4, 256, F + 2), FGB_ERR_ALIGN);
+  EXPECT(grouped(4, 0, F), FGB_OK);
+  EXPECT(grouped(4, 256, F, 100), FGB_ERR_SHAPE);
+  EXPECT(grouped(4, 256, F), FGB_OK);
+  if (strcmp(g_stub.last, "gemm_grouped") || g_stub.E != 4 || g_stub.M != 256) failures++;
+  EXPECT(fgb_grouped_gemm_workspace_bytes(256, 512, 1024, 4), 0);
+
+  // quantizers and codecs
+  EXPECT(fgb_act_quant_group128((const uint16_t*)P(F), 64, 1000, 1000, (uint8_t*)P(F), 1008, (float*)P(F), 64,
+                                nullptr), FGB_ERR_SHAPE);
+  EXPECT(fgb_act_quant_group128(nullptr, 64, 1024, 1024, (uint8_t*)P(F), 1024, (float*)P(F), 64, nullptr),
+         FGB_ERR_NULL);
+  EXPECT(fgb_act_quant_group128((const uint16_t*)P(F), 64, 1024, 1024, (uint8_t*)P(F), 1024, (float*)P(F), 32,
+                                nullptr), FGB_ERR_STRIDE);
+  EXPECT(fgb_act_quant_group128((const uint16_t*)P(F), 64, 1024, 1028, (uint8_t*)P(F), 1024, (float*)P(F), 64,
+                                nullptr), FGB_ERR_ALIGN);
+  EXPECT(fgb_act_quant_group128((const uint16_t*)P(F), 64, 1024, 1024, (uint8_t*)P(F), 1024, (float*)P(F), 64,
+                                nullptr), FGB_OK);
+  EXPECT(fgb_weight_quant_block128((const uint16_t*)P(F), 130, 128, (uint8_t*)P(F), P(F), 0, nullptr), FGB_ERR_SHAPE);
+  EXPECT(fgb_weight_quant_block128((const uint16_t*)P(F), 128, 128, (uint8_t*)P(F), P(F), 9, nullptr), FGB_ERR_ENUM);
+  EXPECT(fgb_weight_quant_block128((const uint16_t*)P(F), 128, 128, (uint8_t*)P(F), P(F + 1), 0, nullptr),
+         FGB_ERR_ALIGN);
+  EXPECT(fgb_weight_quant_block128((const uint16_t*)P(F), 128, 128, (uint8_t*)P(F), P(F + 1), 1, nullptr), FGB_OK);
+  EXPECT(fgb_fp8_encode((const float*)P(F), (uint8_t*)P(F), 16, 9, 1, nullptr), FGB_ERR_ENUM);
+  EXPECT(fgb_fp8_encode((const float*)P(F), (uint8_t*)P(F), -1, 0, 1, nullptr), FGB_ERR_SHAPE);
+  EXPECT(fgb_fp8_encode((const float*)P(F), (uint8_t*)P(F), 16, 0, 1, nullptr), FGB_OK);
+  EXPECT(fgb_fp8_decode((const uint8_t*)P(F), (float*)P(F + 1), 16, 0, nullptr), FGB_ERR_ALIGN);
+  EXPECT(fgb_fp8_decode((const uint8_t*)P(F), (float*)P(F), 16, 3, nullptr), FGB_ERR_ENUM);
+  EXPECT(fgb_fp8_decode((const uint8_t*)P(F), (float*)P(F), 16, 2, nullptr), FGB_OK);
+  EXPECT(fgb_check_expert_offsets((const int32_t*)P(F), 0, 10, (int32_t*)P(F), nullptr), FGB_ERR_SHAPE);
+  EXPECT(fgb_check_expert_offsets((const int32_t*)P(F), 4, 10, (int32_t*)P(F + 1), nullptr), FGB_ERR_ALIGN);
+  EXPECT(fgb_check_expert_offsets((const int32_t*)P(F), 4, 10, (int32_t*)P(F), nullptr), FGB_OK);
+  EXPECT(fgb_selftest_quotients(nullptr, nullptr), FGB_ERR_NULL);
+  EXPECT(fgb_selftest_quotients((unsigned long long*)P(F + 4), nullptr), FGB_ERR_ALIGN);
+  EXPECT(fgb_selftest_quotients((unsigned long long*)P(F), nullptr), FGB_OK);
+
+  if (failures) {
+    fprintf(stderr, "%d failures\n", failures);
+    return 1;
+  }
+  printf("host ABI checks passed\n");
+  return 0;
+}

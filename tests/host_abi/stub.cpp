@@ -1,0 +1,70 @@
+// Stand-ins for the HIP runtime and the kernel launchers (see stub.h).
+#include <hip/hip_runtime_api.h>
+#include <string.h>
+
+#include "../../fine_grained_block_amd/csrc/internal.h"
+#include "stub.h"
+
+StubState g_stub = {0, 0, "gfx950:sramecc+:xnack-", 0, 0, "", 0, 0, 0, 0, nullptr, 1u << 20};
+
+hipError_t hipGetDevice(int* d) {
+  if (g_stub.get_device_fails) return hipErrorNoDevice;
+  *d = g_stub.device;
+  return hipSuccess;
+}
+
+hipError_t hipGetDeviceProperties(hipDeviceProp_t* p, int dev) {
+  (void)dev;
+  memset(p, 0, sizeof(*p));
+  strncpy(p->gcnArchName, g_stub.arch, sizeof(p->gcnArchName) - 1);
+  return hipSuccess;
+}
+
+hipError_t hipGetLastError(void) { return hipSuccess; }
+
+namespace fgb {
+
+static hipError_t launched(const char* name) {
+  g_stub.launches++;
+  g_stub.last = name;
+  return g_stub.launch_error ? hipErrorInvalidValue : hipSuccess;
+}
+
+static void record(const GemmArgs& a) {
+  g_stub.M = a.M;
+  g_stub.N = a.N;
+  g_stub.K = a.K;
+  g_stub.E = a.E;
+}
+
+hipError_t launch_act_quant(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, int64_t, float*, int64_t,
+                            hipStream_t) {
+  return launched("act_quant");
+}
+hipError_t launch_weight_quant(const uint16_t*, int64_t, int64_t, uint8_t*, void*, int, hipStream_t) {
+  return launched("weight_quant");
+}
+hipError_t launch_encode(const float*, uint8_t*, int64_t, int, int, hipStream_t) { return launched("encode"); }
+hipError_t launch_decode(const uint8_t*, float*, int64_t, int, hipStream_t) { return launched("decode"); }
+hipError_t launch_selftest_quotients(unsigned long long*, hipStream_t) { return launched("selftest"); }
+hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t) {
+  record(a);
+  return launched("gemm_prefill");
+}
+hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t) {
+  record(a);
+  return launched("gemm_grouped");
+}
+hipError_t launch_check_offsets(const int32_t*, int32_t, int64_t, int32_t*, hipStream_t) {
+  return launched("check_offsets");
+}
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return (M == 32 && N == 4096 && K == 4096) ? (size_t)g_stub.ws_bytes_query : 0;
+}
+hipError_t launch_gemm_decode(const GemmArgs& a, void* ws, hipStream_t) {
+  record(a);
+  g_stub.workspace = ws;
+  return launched("gemm_decode");
+}
+
+}  // namespace fgb
