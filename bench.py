@@ -40,8 +40,8 @@ def parse():
                    help="'step': only the headline step; 'all': also the Llama-3-8B step, decode, cold UE8M0 "
                         "prefill calls, MoE, quant")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=1024, help="tokens in the oracle sample")
-    p.add_argument("--cpu-cols", type=int, default=1024, help="output features per projection in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=2048, help="tokens in the oracle sample")
+    p.add_argument("--cpu-cols", type=int, default=2048, help="output features per projection in the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     p.add_argument("--derive-traffic", metavar="PMC_DIR",
