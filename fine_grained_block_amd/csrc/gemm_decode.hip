@@ -6,7 +6,9 @@
 //   * M <= 16: one workgroup per 16 weight rows and the whole K, its waves splitting the
 //     K-blocks; weights >= 48 MiB stream through per-wave LDS rings with whole-line direct
 //     copies, smaller ones load the MFMA operand layout straight into registers.  One launch.
-//   * 16 < M <= 64: a workgroup of 8 waves per 128-row weight block over a K slice, weights,
+//   * 16 < M <= 64, weights of at most 16 MiB: the per-wave ring kernel with 32 or 64 activation
+//     rows, one launch.
+//   * 16 < M <= 64, larger weights: a workgroup of 8 waves per 128-row weight block over a K slice, weights,
 //     activations and their scales streamed through a 4-stage LDS ring shared by the waves; K is
 //     sliced only to occupy the CUs, and sliced shapes add their float32 partials [S][M][N] in a
 //     second, ordered launch.  (A reduction inside the same launch would need device-scope
@@ -60,20 +62,25 @@ constexpr int vmcnt_only() { return (V & 0xF) | ((V >> 4) << 14) | (0x7 << 4) | 
 __device__ __forceinline__ int swz_g(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // ---------------------------------------------------------------------------------------------
-// M <= 16, large weights: same work split as the kernel below, but each wave streams its 16
-// weight rows (and the <= MR activation rows of its K-slice, and their scales) through a private
-// LDS ring of D stages with direct copies.  A copy instruction reads 8 whole 128-byte lines,
-// where loading the MFMA operand layout straight into registers touches 16 half-used lines per
-// instruction, which costs about four times as much address-unit time per byte on gfx950 and
-// limits the weight stream below the HBM rate.  No barrier is needed until the partial tiles are
-// added.  For small weights the extra LDS round trip costs more than it saves.
+// Weight-streaming kernel with per-wave LDS rings.  A workgroup owns 16 weight rows and the whole
+// K; its WK waves split the K-blocks into contiguous slices and add their partial tiles through
+// LDS at the end (one launch, no workspace).  Each wave streams its 16 weight rows, the MR
+// activation rows of its slice (rows >= M repeat row M-1; their results are dropped) and their
+// scales through a private ring of D LDS stages with whole-line direct copies.  A copy instruction
+// reads 8 whole 128-byte lines, where loading the MFMA operand layout straight into registers
+// touches 16 half-used lines per instruction, which costs about four times as much address-unit
+// time per byte on gfx950.  No barrier is needed until the partial tiles are added.  MR = 32 or
+// 64 gives each wave MR/16 token tiles, all multiplied by the same weight fragment.
 template <int WK, int MR, int D, int SWF, int OUT>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
+  constexpr int MT = MR >= 16 ? MR / 16 : 1;  // token tiles per wave
   constexpr int WST = 16 * 128, AST = MR * 128, SST = 64 * 4;
   constexpr int STAGE = WST + AST + SST;
   constexpr int OPS = 2 + MR / 8 + 1;  // direct copies per stage
+  static_assert(MR == 8 || MR == 16 || MR == 32 || MR == 64, "8, 16, 32 or 64 activation rows");
+  static_assert((D - 1) * OPS <= 63, "copies in flight fit the vmcnt counter");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[WK * D * STAGE];
-  __shared__ v4f red[WK > 1 ? WK - 1 : 1][64];
+  __shared__ v4f red[WK > 1 ? WK - 1 : 1][MT][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t K = p.K, M = p.M;
@@ -98,7 +105,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
     const int64_t m = r < M ? r : M - 1;
     aoff[q] = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
   }
-  const uint32_t soff = (uint32_t)(((lane & 15) < M ? (lane & 15) : M - 1) * 4);
+  const uint32_t soff = (uint32_t)((lane < M ? lane : M - 1) * 4);
   const uint8_t* wbase = p.w_q + n0 * K;
 
   auto issue = [&](int kk) {
@@ -146,7 +153,9 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
     return __int_as_float((t & 2) ? hi : lo);
   };
 
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   if (nk > 0) {
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) issue(min(i, nk - 1));
@@ -162,36 +171,88 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
       const int ra = r & (MR - 1);
       const uint32_t aa0 = st + WST + swz(ra, 2 * g), aa1 = st + WST + swz(ra, 2 * g + 1);
       const uint32_t as = st + WST + AST + 4 * r;
-      v4i w0, w1, a0, a1;
-      float sa;
-      asm volatile(
-          "ds_read_b128 %0, %5\n\t"
-          "ds_read_b128 %1, %6\n\t"
-          "ds_read_b128 %2, %7\n\t"
-          "ds_read_b128 %3, %8\n\t"
-          "ds_read_b32 %4, %9\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(w0), "=&v"(w1), "=&v"(a0), "=&v"(a1), "=&v"(sa)
-          : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
-          : "memory");
-      v8i wf, af;
+      v4i w0, w1, a0[MT], a1[MT];
+      float sa[MT];
+      if constexpr (MT == 1) {
+        asm volatile(
+            "ds_read_b128 %0, %5\n\t"
+            "ds_read_b128 %1, %6\n\t"
+            "ds_read_b128 %2, %7\n\t"
+            "ds_read_b128 %3, %8\n\t"
+            "ds_read_b32 %4, %9\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(sa[0])
+            : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
+            : "memory");
+      } else if constexpr (MT == 2) {
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %9\n\t"
+            "ds_read_b128 %2, %10\n\t"
+            "ds_read_b128 %3, %11\n\t"
+            "ds_read_b128 %4, %10 offset:2048\n\t"
+            "ds_read_b128 %5, %11 offset:2048\n\t"
+            "ds_read_b32 %6, %12\n\t"
+            "ds_read_b32 %7, %12 offset:64\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(a0[1]), "=&v"(a1[1]), "=&v"(sa[0]),
+              "=&v"(sa[1])
+            : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
+            : "memory");
+      } else {
+        asm volatile(
+            "ds_read_b128 %0, %14\n\t"
+            "ds_read_b128 %1, %15\n\t"
+            "ds_read_b128 %2, %16\n\t"
+            "ds_read_b128 %3, %17\n\t"
+            "ds_read_b128 %4, %16 offset:2048\n\t"
+            "ds_read_b128 %5, %17 offset:2048\n\t"
+            "ds_read_b128 %6, %16 offset:4096\n\t"
+            "ds_read_b128 %7, %17 offset:4096\n\t"
+            "ds_read_b128 %8, %16 offset:6144\n\t"
+            "ds_read_b128 %9, %17 offset:6144\n\t"
+            "ds_read_b32 %10, %18\n\t"
+            "ds_read_b32 %11, %18 offset:64\n\t"
+            "ds_read_b32 %12, %18 offset:128\n\t"
+            "ds_read_b32 %13, %18 offset:192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(a0[1]), "=&v"(a1[1]), "=&v"(a0[2]),
+              "=&v"(a1[2]), "=&v"(a0[3]), "=&v"(a1[3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3])
+            : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
+            : "memory");
+      }
+      v8i wf;
       wf[0] = w0[0]; wf[1] = w0[1]; wf[2] = w0[2]; wf[3] = w0[3];
       wf[4] = w1[0]; wf[5] = w1[1]; wf[6] = w1[2]; wf[7] = w1[3];
-      af[0] = a0[0]; af[1] = a0[1]; af[2] = a0[2]; af[3] = a0[3];
-      af[4] = a1[0]; af[5] = a1[1]; af[6] = a1[2]; af[7] = a1[3];
-      acc += mfma_e4m3_16x16x128(wf, af) * (sa * sw_at(kk));
+      const float sw = sw_at(kk);
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        v8i af;
+        af[0] = a0[j][0]; af[1] = a0[j][1]; af[2] = a0[j][2]; af[3] = a0[j][3];
+        af[4] = a1[j][0]; af[5] = a1[j][1]; af[6] = a1[j][2]; af[7] = a1[j][3];
+        acc[j] += mfma_e4m3_16x16x128(wf, af) * (sa[j] * sw);
+      }
     }
   }
   // the clamped copies past the slice must land before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
   if constexpr (WK > 1) {
-    if (wave > 0) red[wave - 1][lane] = acc;
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j) red[wave - 1][j][lane] = acc[j];
+    }
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
-    for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
+    for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+      for (int j = 0; j < MT; ++j) acc[j] += red[w][j][lane];
   }
-  if ((lane & 15) < M) store4<OUT>(p.y, p.ldy, lane & 15, n0 + 4 * (lane >> 4), acc);
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int m = 16 * j + (lane & 15);
+    if (m < M) store4<OUT>(p.y, p.ldy, m, n0 + 4 * (lane >> 4), acc[j]);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -452,6 +513,13 @@ int small_waves(int64_t N, int64_t K) {
 // weights from this size on take the LDS-ring kernel for M <= 16
 constexpr int64_t kRingMinWeightBytes = 48ll << 20;
 
+// 16 < M <= 64 with weights of at most 16 MiB (the 4096 x 4096 projection): the per-wave ring
+// kernel (16 weight rows and the whole K per workgroup, 4 waves, 32 or 64 activation rows), one
+// launch.  Measured against the shared-ring kernel below, whose K slicing needs a second launch
+// at these sizes: 4096 x 4096 at M = 32 7.1 vs 10.0 us, M = 64 8.9 vs 11.5 us.  For larger
+// weights the per-wave copies of all activation rows cost more than the second launch.
+bool ring_mid_rows(int64_t N, int64_t K) { return N * K <= (16ll << 20); }
+
 constexpr int MID_D = 4;  // LDS stages of the 16 < M <= 64 kernel (measured: 4 >= 5, 6)
 
 // K-blocks per workgroup of the 16 < M <= 64 kernel.  One slice when the weight blocks alone give
@@ -470,7 +538,7 @@ int mid_kpw(int64_t N, int64_t K) {
 }  // namespace
 
 int decode_splits(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16) return 1;  // the small-M kernels need no workspace
+  if (M <= 16 || ring_mid_rows(N, K)) return 1;  // these kernels need no workspace
   const int KB = (int)(K / 128);
   const int kpw = mid_kpw(N, K);
   return (KB + kpw - 1) / kpw;
@@ -504,6 +572,21 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
     }
 #undef FGB_RING_WK
 #undef FGB_RING
+    return hipGetLastError();
+  }
+  if (a.M > 16 && ring_mid_rows(a.N, a.K)) {
+    const dim3 grid((unsigned)(a.N / 16));
+#define FGB_RING_MID(SWF, OUT)                                                                                   \
+  do {                                                                                                           \
+    if (a.M <= 32) hipLaunchKernelGGL((gemm_decode_ring_kernel<4, 32, 3, SWF, OUT>), grid, dim3(256), 0, stream, a); \
+    else hipLaunchKernelGGL((gemm_decode_ring_kernel<4, 64, 2, SWF, OUT>), grid, dim3(256), 0, stream, a);           \
+  } while (0)
+    if (a.s_w_fmt == 0) {
+      if (a.y_dtype == 0) FGB_RING_MID(0, 0); else FGB_RING_MID(0, 1);
+    } else {
+      if (a.y_dtype == 0) FGB_RING_MID(1, 0); else FGB_RING_MID(1, 1);
+    }
+#undef FGB_RING_MID
     return hipGetLastError();
   }
   if (a.M <= 16) {
