@@ -29,6 +29,7 @@ from .ops import (  # noqa: F401
     quantize,
     quantize_weight,
     gemm,
+    gemm_noalloc,
     grouped_gemm,
     check_offsets,
     gemm_workspace_bytes,

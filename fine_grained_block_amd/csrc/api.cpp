@@ -134,6 +134,26 @@ int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64
   return launch_status(fgb::launch_gemm_prefill(a, (hipStream_t)stream));
 }
 
+int fgb_w8a8_block_gemm_noalloc(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                                const uint8_t* w_q, const void* s_w, int s_w_fmt, void* y, int y_dtype,
+                                int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K);
+  if (st != FGB_OK || M == 0) return st;
+  const bool decode = M <= 64;
+  const size_t need = decode ? fgb::decode_workspace_bytes(M, N, K) : 0;
+  if (need > fgb::kDecodeScratchBytes) return FGB_ERR_WORKSPACE;
+  st = check_device();
+  if (st != FGB_OK) return st;
+  fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K, nullptr, 1};
+  if (!decode) return launch_status(fgb::launch_gemm_prefill(a, (hipStream_t)stream));
+  void* ws = nullptr;
+  if (need > 0 && fgb::decode_scratch(&ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return FGB_ERR_DEVICE;
+  }
+  return launch_status(fgb::launch_gemm_decode(a, ws, (hipStream_t)stream));
+}
+
 size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, int32_t E) {
   (void)total_M; (void)N; (void)K; (void)E;
   return 0;

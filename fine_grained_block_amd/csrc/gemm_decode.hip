@@ -14,6 +14,8 @@
 //     second, ordered launch.  (A reduction inside the same launch would need device-scope
 //     release fences, which on this multi-XCD part write back the L2 and cost more than the
 //     second launch.)
+#include <mutex>
+
 #include "gemm_common.hpp"
 #include "internal.h"
 
@@ -639,6 +641,32 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
       hipLaunchKernelGGL(splitk_reduce_kernel<1>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
     return hipGetLastError();
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Library-owned scratch for callers that cannot allocate (the no-allocation GEMM entry point).
+// One array per GPU, in the code object's device memory for as long as the library is loaded.
+// Host code never uses the array's name as an address: hipGetSymbolAddress gives each device's
+// own copy, looked up once per device and kept.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = ptr;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 }  // namespace fgb

@@ -44,4 +44,10 @@ int decode_splits(int64_t M, int64_t N, int64_t K);
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream);
 
+// Scratch that the library owns for callers that cannot allocate: kDecodeScratchBytes per GPU
+// (covers every decode workspace: at most 64 x 49024 float32 partials, 12.25 MiB).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+// The current device's scratch address (looked up once per device).
+hipError_t decode_scratch(void** out);
+
 }  // namespace fgb

@@ -192,6 +192,21 @@ def gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: torch.Ten
     return out
 
 
+def gemm_noalloc(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor,
+                 out: torch.Tensor) -> torch.Tensor:
+    """gemm() through the entry point that allocates nothing: the caller passes the output, and
+    the decode calls that need a workspace use the library's own per-GPU scratch.  Calls that
+    may overlap on one GPU must not be issued (they share that scratch)."""
+    _need(out is not None, "gemm_noalloc writes into a given output tensor")
+    M, N, K = _check_gemm_operands(a_q, s_a, w_q, s_w, out, None)
+    _on_device(("a_q", a_q), ("s_a", s_a), ("w_q", w_q), ("s_w", s_w), ("out", out))
+    st = lib().fgb_w8a8_block_gemm_noalloc(_ptr(a_q), _row_ld(a_q), _ptr(s_a), s_a.stride(0), _ptr(w_q),
+                                           _ptr(s_w), _scale_fmt(s_w), _ptr(out), _out_code(out.dtype),
+                                           _row_ld(out), M, N, K, _stream())
+    check("fgb_w8a8_block_gemm_noalloc", st)
+    return out
+
+
 def grouped_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor,
                  offsets: torch.Tensor, out_dtype=torch.bfloat16,
                  out: torch.Tensor | None = None) -> torch.Tensor:

@@ -117,6 +117,21 @@ int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64
                         int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fgb_w8a8_block_gemm without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, kernels and results as fgb_w8a8_block_gemm; the decode calls that need a
+ * workspace use a scratch array that the library owns instead: 16 MiB per GPU, held until the
+ * process ends (every decode workspace fits: at most 12.25 MiB; a shape needing more returns
+ * FGB_ERR_WORKSPACE).  Allocates nothing.  All calls on one GPU share that GPU's scratch, so
+ * calls that may overlap on one GPU (different streams without ordering) race and must not be
+ * issued; calls ordered on one stream are fine.  The scratch needs no initial contents.
+ */
+int fgb_w8a8_block_gemm_noalloc(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                                const uint8_t* w_q, const void* s_w, int s_w_fmt,
+                                void* y, int y_dtype, int64_t ldy,
+                                int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Host query: workspace bytes fgb_grouped_w8a8_block_gemm needs (0 if none). */
 size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, int32_t E);
 
