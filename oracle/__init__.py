@@ -11,6 +11,8 @@ Modules
 fp8        E4M3 / E5M2 / UE8M0 decode and encode from the bit fields (float64, exact)
 blockquant act_quant (dynamic 1x128 groups), weight_quant (128x128 blocks, float32 or UE8M0)
 gemm       gemm_ref (exact per-block partials, float64), gemm_ref_fast, grouped_ref, bf16_rne
+schemes    per-token / per-channel (FP8_DYNAMIC) and static per-tensor quantization, E5M2 codes,
+           and the GEMM under those scales (scaled_gemm_ref)
 
 Pins (see tests/test_oracle_*.py): exhaustive code tables against the formats' printed maxima
 and NaN/inf sets and against torch's float8 dtypes; brute-force nearest-code searches for the
@@ -18,7 +20,7 @@ encoders; closed forms for UE8M0; quantization invariants; hand-worked golden fi
 float64 brute force and an exact-integer special case for the GEMM.  Parity unpinned: none of
 the functions above; the GEMM's float32 summation order on the GPU is judged by tolerance.
 """
-from . import fp8, blockquant, gemm  # noqa: F401
+from . import fp8, blockquant, gemm, schemes  # noqa: F401
 from .fp8 import dec_e4m3, dec_e5m2, dec_ue8m0, enc_e4m3_sat, enc_e5m2, ue8m0_from_amax  # noqa: F401
 from .blockquant import act_quant, weight_quant  # noqa: F401
 from .gemm import gemm_ref, gemm_ref_fast, grouped_ref, bf16_rne  # noqa: F401

@@ -33,23 +33,37 @@ def _as_f32(x) -> np.ndarray:
     return x
 
 
-def _quantize_groups(xg: np.ndarray, s: np.ndarray) -> np.ndarray:
+# the largest finite value of each code format (vLLM "FP8 W8A8", "Two FP8 representations")
+CODE_MAX = {"e4m3": np.float32(448.0), "e5m2": np.float32(57344.0)}
+
+
+def encode(r, code: str = "e4m3") -> np.ndarray:
+    """Round-to-nearest-even, saturating encoder of the chosen format."""
+    if code == "e4m3":
+        return fp8.enc_e4m3_sat(r)
+    if code == "e5m2":
+        return fp8.enc_e5m2(r, saturate=True)
+    raise ValueError("code must be 'e4m3' or 'e5m2'")
+
+
+def _quantize_groups(xg: np.ndarray, s: np.ndarray, code: str = "e4m3") -> np.ndarray:
     """xg float32 [..., G, L]; s float32 [..., G] -> u8 codes [..., G, L]."""
     with np.errstate(divide="ignore", invalid="ignore"):
         r = xg / s[..., None]  # float32 / float32: IEEE correctly rounded
     zero = (s == 0)[..., None] & np.ones(xg.shape, dtype=bool)
     r = np.where(zero, 0.0, r)
-    q = fp8.enc_e4m3_sat(r)
+    q = encode(r, code)
     # amax == 0: every element is +-0; keep its sign (enc saw +0 after the where above)
     signs = (np.signbit(xg).astype(np.uint8) << 7)
     return np.where(zero, signs, q).astype(np.uint8)
 
 
-def act_quant(x, group: int = GROUP):
+def act_quant(x, group: int = GROUP, code: str = "e4m3"):
     """Dynamic per-token, per-group activation quantization.
 
     x: bf16 bits uint16 [M, K] (or float32 holding bf16-exact values), finite.
     Returns (q uint8 [M, K], s float32 [M, ceil(K/group)]).  The last group may be partial.
+    s = fl32(amax / max) with max = 448 for E4M3 codes, 57344 for E5M2 codes.
     """
     xf = _as_f32(x)
     if not np.all(np.isfinite(xf)):
@@ -60,18 +74,21 @@ def act_quant(x, group: int = GROUP):
     xp = np.pad(xf, ((0, 0), (0, pad))) if pad else xf
     xg = xp.reshape(M, G, group)
     amax = np.max(np.abs(xg), axis=2)                 # exact
-    s = (amax / np.float32(448.0)).astype(np.float32)  # one IEEE float32 division
-    q = _quantize_groups(xg, s).reshape(M, G * group)[:, :K]
+    s = (amax / CODE_MAX[code]).astype(np.float32)     # one IEEE float32 division
+    q = _quantize_groups(xg, s, code).reshape(M, G * group)[:, :K]
     return np.ascontiguousarray(q), s
 
 
-def weight_quant(w, fmt: str = "f32", block: int = GROUP):
+def weight_quant(w, fmt: str = "f32", block: int = GROUP, code: str = "e4m3"):
     """Per 128x128 block weight quantization.
 
     w: bf16 bits uint16 [N, K] (or float32).  fmt: "f32" -> s float32 [ceil(N/128), ceil(K/128)];
-    "ue8m0" -> s uint8 UE8M0 codes of the same shape.
+    "ue8m0" -> s uint8 UE8M0 codes of the same shape (E4M3 codes only).  code: "e4m3" or
+    "e5m2" (float32 scales amax / 57344).
     Returns (q uint8 [N, K], s).
     """
+    if fmt == "ue8m0" and code != "e4m3":
+        raise ValueError("UE8M0 weight scales go with E4M3 codes")
     wf = _as_f32(w)
     if not np.all(np.isfinite(wf)):
         raise ValueError("weight_quant: non-finite input is outside the contract")
@@ -81,7 +98,7 @@ def weight_quant(w, fmt: str = "f32", block: int = GROUP):
     blocks = wp.reshape(NB, block, KB, block).transpose(0, 2, 1, 3)  # [NB, KB, b, b]
     amax = np.max(np.abs(blocks), axis=(2, 3))
     if fmt == "f32":
-        s = (amax / np.float32(448.0)).astype(np.float32)
+        s = (amax / CODE_MAX[code]).astype(np.float32)
         s_used = s
     elif fmt == "ue8m0":
         s = fp8.ue8m0_from_amax(amax)
@@ -89,7 +106,7 @@ def weight_quant(w, fmt: str = "f32", block: int = GROUP):
     else:
         raise ValueError("fmt must be 'f32' or 'ue8m0'")
     flat = blocks.reshape(NB, KB, block * block)
-    q = _quantize_groups(flat, s_used).reshape(NB, KB, block, block)
+    q = _quantize_groups(flat, s_used, code).reshape(NB, KB, block, block)
     q = q.transpose(0, 2, 1, 3).reshape(NB * block, KB * block)[:N, :K]
     return np.ascontiguousarray(q), s
 

@@ -7,10 +7,11 @@ floor instead of ceil); the listed pin must then fail.
 import numpy as np
 import pytest
 
-from oracle import blockquant, fp8, gemm
+from oracle import blockquant, fp8, gemm, schemes
 import tests.test_oracle_fp8 as T8
 import tests.test_oracle_gemm as TG
 import tests.test_oracle_quant as TQ
+import tests.test_oracle_schemes as TS
 
 _orig_dec = fp8.dec_e4m3
 _orig_enc = fp8.enc_e4m3_sat
@@ -81,6 +82,39 @@ def _ue8m0_floor(amax):
 
 _orig_ue = fp8.ue8m0_from_amax
 
+_orig_token = schemes.token_quant
+_orig_static = schemes.static_quant
+_orig_scaled = schemes.scaled_gemm_ref
+
+
+def _token_quant_column_amax(x, code="e4m3"):
+    """per-channel of x instead of per-token: the scale of column k applied to row k's place"""
+    q, s = _orig_token(np.ascontiguousarray(np.asarray(x).T), code)
+    return np.ascontiguousarray(q.T), s[: np.asarray(x).shape[0]]
+
+
+def _static_reciprocal(x, s, code="e4m3"):
+    xf = np.asarray(x)
+    if xf.dtype == np.uint16:
+        xf = (xf.astype(np.uint32) << 16).view(np.float32)
+    inv = np.float32(1.0) / np.float32(s)
+    return blockquant.encode((xf * inv).astype(np.float32), code)
+
+
+def _scaled_channel_by_row(a_q, a_scale, w_q, w_scale, **kw):
+    if kw.get("weight") == "channel":
+        y = _orig_scaled(a_q, a_scale, w_q, np.ones(w_q.shape[0], np.float32), **kw)
+        ws = np.resize(np.asarray(w_scale, np.float64), a_q.shape[0])
+        return y * ws[:, None]
+    return _orig_scaled(a_q, a_scale, w_q, w_scale, **kw)
+
+
+def _scaled_tensor_scale_dropped(a_q, a_scale, w_q, w_scale, **kw):
+    if kw.get("act") == "tensor":
+        return _orig_scaled(a_q, np.float32(1.0), w_q, w_scale, **kw)
+    return _orig_scaled(a_q, a_scale, w_q, w_scale, **kw)
+
+
 MUTANTS = [
     ("decode bias 8", fp8, "dec_e4m3", _dec_bias8, [T8.test_e4m3_printed_facts, T8.test_e4m3_matches_torch_table]),
     ("ties away from zero", fp8, "enc_e4m3_sat", _enc_ties_away, [T8.test_enc_e4m3_bruteforce, TQ.test_golden_handworked_groups]),
@@ -90,7 +124,22 @@ MUTANTS = [
     ("transposed weight-scale index", gemm, "gemm_ref", _gemm_transposed_sw, [lambda: TG.test_blockwise_equals_dense_bruteforce("f32")]),
     ("dropped last K-block", gemm, "gemm_ref", _gemm_drop_last_block, [lambda: TG.test_blockwise_equals_dense_bruteforce("f32"), TG.test_exact_integer_special_case]),
     ("UE8M0 floor instead of ceil", fp8, "ue8m0_from_amax", _ue8m0_floor, [TQ.test_golden_ue8m0_scale_choice]),
+    ("per-token scale over columns", schemes, "token_quant", _token_quant_column_amax,
+     [lambda: TS.test_token_quant_rational_definition("e4m3"), TS.test_token_quant_reduces_to_group_quant_at_k128]),
+    ("static quant by reciprocal", schemes, "static_quant", _static_reciprocal,
+     [TS.test_static_quant_divides_by_the_scale]),
+    ("channel scale on rows", schemes, "scaled_gemm_ref", _scaled_channel_by_row,
+     [TS.test_token_channel_gemm_reduces_to_block_gemm]),
+    ("static scale dropped", schemes, "scaled_gemm_ref", _scaled_tensor_scale_dropped,
+     [lambda: TS.test_tensor_block_gemm_reduces_to_block_gemm("f32")]),
 ]
+
+
+def test_pin_catches_e5m2_maximum_448(monkeypatch):
+    monkeypatch.setitem(blockquant.CODE_MAX, "e5m2", np.float32(448.0))
+    for pin in (TS.test_e5m2_max_element_reaches_57344, TS.test_e5m2_group_quant_rational_definition):
+        with pytest.raises(AssertionError):
+            pin()
 
 
 @pytest.mark.parametrize("name,mod,attr,mutant,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
