@@ -21,6 +21,10 @@ from ._lib import (  # noqa: F401
     FP8_E5M2,
     UE8M0,
     FP8_E4M3_INT,
+    ACT_SCALE_TOKEN,
+    ACT_SCALE_TENSOR,
+    W_SCALE_BLOCK128,
+    W_SCALE_CHANNEL,
     lib,
     lib_path,
     status_string,
@@ -28,6 +32,10 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     quantize,
     quantize_weight,
+    quantize_per_token,
+    quantize_weight_per_channel,
+    quantize_static,
+    scaled_gemm,
     gemm,
     gemm_noalloc,
     grouped_gemm,

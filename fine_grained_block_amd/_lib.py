@@ -8,6 +8,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libfgb.so")
 
 SCALE_F32, SCALE_UE8M0 = 0, 1
+ACT_SCALE_GROUP128, ACT_SCALE_TOKEN, ACT_SCALE_TENSOR = 0, 1, 2
+W_SCALE_BLOCK128, W_SCALE_CHANNEL = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 FP8_E4M3, FP8_E5M2, UE8M0, FP8_E4M3_INT = 0, 1, 2, 3
 
@@ -28,6 +30,12 @@ _SIGS = {
                                                    ctypes.c_int32, _c_i64, _vp, ctypes.c_int, _c_i64, _c_i64,
                                                    _c_i64, _vp, ctypes.c_size_t, _vp]),
     "fgb_check_expert_offsets": (ctypes.c_int, [_vp, ctypes.c_int32, _c_i64, _vp, _vp]),
+    "fgb_act_quant_per_token": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, _vp, _c_i64, _vp, _vp]),
+    "fgb_weight_quant_per_channel": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.c_int, _vp, _vp, _vp]),
+    "fgb_act_quant_static": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, ctypes.c_int, _vp, _c_i64, _vp]),
+    "fgb_weight_quant_block128_ex": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp]),
+    "fgb_w8a8_scaled_gemm": (ctypes.c_int, [_vp, _c_i64, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, _vp, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _vp]),
     "fgb_fp8_encode": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp]),
     "fgb_fp8_decode": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp]),
     "fgb_selftest_quotients": (ctypes.c_int, [_vp, _vp]),

@@ -154,6 +154,97 @@ int fgb_w8a8_block_gemm_noalloc(const uint8_t* a_q, int64_t lda, const float* s_
   return launch_status(fgb::launch_gemm_decode(a, ws, (hipStream_t)stream));
 }
 
+int fgb_weight_quant_block128_ex(const uint16_t* w, int64_t N, int64_t K, int code_fmt, uint8_t* w_q, void* s_w,
+                                 int s_w_fmt, void* stream) {
+  if (code_fmt != FGB_FP8_E4M3 && code_fmt != FGB_FP8_E5M2) return FGB_ERR_ENUM;
+  if (s_w_fmt != FGB_SCALE_F32 && s_w_fmt != FGB_SCALE_UE8M0) return FGB_ERR_ENUM;
+  if (code_fmt == FGB_FP8_E5M2 && s_w_fmt != FGB_SCALE_F32) return FGB_ERR_ENUM;
+  if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim || N % FGB_BLOCK || K % FGB_BLOCK) return FGB_ERR_SHAPE;
+  if (N == 0 || K == 0) return FGB_OK;
+  if (!w || !w_q || !s_w) return FGB_ERR_NULL;
+  if (!aligned16(w) || !aligned16(w_q)) return FGB_ERR_ALIGN;
+  if (s_w_fmt == FGB_SCALE_F32 && ((uintptr_t)s_w & 3u)) return FGB_ERR_ALIGN;
+  if ((N / FGB_BLOCK) * (K / FGB_BLOCK) >= kMaxDim) return FGB_ERR_SHAPE;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_weight_quant(w, N, K, w_q, s_w, s_w_fmt, (hipStream_t)stream,
+                                                code_fmt == FGB_FP8_E5M2 ? 1 : 0));
+}
+
+namespace {
+
+// Per-row quantization (per token or per output channel): rows x K bf16 -> codes, one scale per row.
+int row_quant(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, int code_fmt, uint8_t* q, int64_t ldq,
+              float* s, void* stream) {
+  if (code_fmt != FGB_FP8_E4M3 && code_fmt != FGB_FP8_E5M2) return FGB_ERR_ENUM;
+  if (rows < 0 || K <= 0 || rows >= kMaxDim || K >= kMaxDim || K % FGB_BLOCK) return FGB_ERR_SHAPE;
+  if (rows == 0) return FGB_OK;
+  if (!x || !q || !s) return FGB_ERR_NULL;
+  if (ldx < K || ldq < K) return FGB_ERR_STRIDE;
+  if (!aligned16(x) || !aligned16(q) || ((uintptr_t)s & 3u)) return FGB_ERR_ALIGN;
+  if ((ldx * 2) % 16 || ldq % 16) return FGB_ERR_ALIGN;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_row_quant(x, rows, K, ldx, q, ldq, s, code_fmt == FGB_FP8_E5M2 ? 1 : 0,
+                                             (hipStream_t)stream));
+}
+
+}  // namespace
+
+int fgb_act_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int code_fmt, uint8_t* q,
+                            int64_t ldq, float* s_a, void* stream) {
+  return row_quant(x, M, K, ldx, code_fmt, q, ldq, s_a, stream);
+}
+
+int fgb_weight_quant_per_channel(const uint16_t* w, int64_t N, int64_t K, int code_fmt, uint8_t* w_q, float* s_w,
+                                 void* stream) {
+  if (N % FGB_BLOCK) return FGB_ERR_SHAPE;
+  return row_quant(w, N, K, K, code_fmt, w_q, K, s_w, stream);
+}
+
+int fgb_act_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* scale, int code_fmt,
+                         uint8_t* q, int64_t ldq, void* stream) {
+  if (code_fmt != FGB_FP8_E4M3 && code_fmt != FGB_FP8_E5M2) return FGB_ERR_ENUM;
+  if (M < 0 || K <= 0 || M >= kMaxDim || K >= kMaxDim || K % FGB_BLOCK) return FGB_ERR_SHAPE;
+  if (M == 0) return FGB_OK;
+  if (!x || !q || !scale) return FGB_ERR_NULL;
+  if (ldx < K || ldq < K) return FGB_ERR_STRIDE;
+  if (!aligned16(x) || !aligned16(q) || ((uintptr_t)scale & 3u)) return FGB_ERR_ALIGN;
+  if ((ldx * 2) % 16 || ldq % 16) return FGB_ERR_ALIGN;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  return launch_status(fgb::launch_static_quant(x, M, K, ldx, scale, q, ldq, code_fmt == FGB_FP8_E5M2 ? 1 : 0,
+                                                (hipStream_t)stream));
+}
+
+int fgb_w8a8_scaled_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int act_scale, const uint8_t* w_q,
+                         const void* s_w, int w_scale, int s_w_fmt, int code_fmt, void* y, int y_dtype, int64_t ldy,
+                         int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FGB_ERR_SHAPE;
+  if (N % FGB_BLOCK || K % FGB_BLOCK) return FGB_ERR_SHAPE;
+  if (act_scale != FGB_ACT_SCALE_TOKEN && act_scale != FGB_ACT_SCALE_TENSOR) return FGB_ERR_ENUM;
+  if (w_scale != FGB_W_SCALE_BLOCK128 && w_scale != FGB_W_SCALE_CHANNEL) return FGB_ERR_ENUM;
+  if (s_w_fmt != FGB_SCALE_F32 && s_w_fmt != FGB_SCALE_UE8M0) return FGB_ERR_ENUM;
+  if (code_fmt != FGB_FP8_E4M3 && code_fmt != FGB_FP8_E5M2) return FGB_ERR_ENUM;
+  if (s_w_fmt == FGB_SCALE_UE8M0 && (w_scale != FGB_W_SCALE_BLOCK128 || code_fmt != FGB_FP8_E4M3)) return FGB_ERR_ENUM;
+  if (y_dtype != FGB_OUT_BF16 && y_dtype != FGB_OUT_F32) return FGB_ERR_ENUM;
+  if (M == 0) return FGB_OK;
+  if (!a_q || !s_a || !w_q || !s_w || !y) return FGB_ERR_NULL;
+  if (lda < K || ldy < N) return FGB_ERR_STRIDE;
+  const int64_t ybytes = y_dtype == FGB_OUT_BF16 ? 2 : 4;
+  if (!aligned16(a_q) || !aligned16(w_q) || !aligned16(s_w) || !aligned16(y) || ((uintptr_t)s_a & 3u))
+    return FGB_ERR_ALIGN;
+  if (lda % 16 || (ldy * ybytes) % 16) return FGB_ERR_ALIGN;
+  if (M * lda >= kMax32 || N * K >= kMax32 || K > 32768) return FGB_ERR_SHAPE;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  fgb::GemmArgs a{a_q, lda, s_a, 0, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K, nullptr, 1, act_scale};
+  const int sch = w_scale == FGB_W_SCALE_CHANNEL ? 2 : 1;
+  const int code = code_fmt == FGB_FP8_E5M2 ? 1 : 0;
+  if (M <= 64) return launch_status(fgb::launch_gemm_scaled_decode(a, sch, code, (hipStream_t)stream));
+  return launch_status(fgb::launch_gemm_scaled_prefill(a, sch, code, (hipStream_t)stream));
+}
+
 size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, int32_t E) {
   (void)total_M; (void)N; (void)K; (void)E;
   return 0;

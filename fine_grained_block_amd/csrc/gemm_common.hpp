@@ -28,6 +28,14 @@ __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// The same instruction on E4M3 (CODE 0) or E5M2 (CODE 1) operands, both operands in one format,
+// accumulating into c.
+template <int CODE>
+__device__ __forceinline__ v4f mfma_f8_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
+  static_assert(CODE == 0 || CODE == 1, "E4M3 or E5M2 operands");
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, CODE, CODE, 0, 0, 0, 0);
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 

@@ -75,12 +75,18 @@ __device__ __forceinline__ int swz_g(int row) { return (row & 7) ^ ((row >> 3) &
 // touches 16 half-used lines per instruction, which costs about four times as much address-unit
 // time per byte on gfx950.  No barrier is needed until the partial tiles are added.  MR = 32 or
 // 64 gives each wave MR/16 token tiles, all multiplied by the same weight fragment.
-template <int WK, int MR, int D, int SWF, int OUT>
+//
+// SCH and CODE as for the prefill kernel: 0 = per-group activation and per-block weight scales;
+// 1 = per-block weight scales, the per-token or per-tensor activation scale in the epilogue; 2 =
+// per-channel weight scales and per-token or per-tensor activation scales, both in the epilogue
+// (the MFMAs accumulate in place).  CODE 1: E5M2 operands (schemes 1 and 2).
+template <int WK, int MR, int D, int SWF, int OUT, int SCH = 0, int CODE = 0>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
+  static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
   constexpr int MT = MR >= 16 ? MR / 16 : 1;  // token tiles per wave
   constexpr int WST = 16 * 128, AST = MR * 128, SST = 64 * 4;
   constexpr int STAGE = WST + AST + SST;
-  constexpr int OPS = 2 + MR / 8 + 1;  // direct copies per stage
+  constexpr int OPS = 2 + MR / 8 + (SCH == 0 ? 1 : 0);  // direct copies per stage
   static_assert(MR == 8 || MR == 16 || MR == 32 || MR == 64, "8, 16, 32 or 64 activation rows");
   static_assert((D - 1) * OPS <= 63, "copies in flight fit the vmcnt counter");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[WK * D * STAGE];
@@ -133,14 +139,16 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
       asm volatile("" : "+v"(o));
       __builtin_amdgcn_global_load_lds(GPTR(ab + o), LPTR(st + WST + q * 1024), 16, 0, 0);
     }
-    uint32_t o = soff;
-    asm volatile("" : "+v"(o));
-    __builtin_amdgcn_global_load_lds(GPTR(sb + o), LPTR(st + WST + AST), 4, 0, 0);
+    if constexpr (SCH == 0) {
+      uint32_t o = soff;
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(GPTR(sb + o), LPTR(st + WST + AST), 4, 0, 0);
+    }
   };
 
   // weight-block scales of this wave's slice, lane l holding block kb0 + l + 64 t (K <= 32768)
   float sw0 = 0.0f, sw1 = 0.0f, sw2 = 0.0f, sw3 = 0.0f;
-  {
+  if constexpr (SCH != 2) {
     const int64_t b = nb * KB + kb0;
     sw0 = lane < nk ? load_sw<SWF>(p.s_w, b + lane) : 0.0f;
     sw1 = lane + 64 < nk ? load_sw<SWF>(p.s_w, b + lane + 64) : 0.0f;
@@ -228,13 +236,16 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
       v8i wf;
       wf[0] = w0[0]; wf[1] = w0[1]; wf[2] = w0[2]; wf[3] = w0[3];
       wf[4] = w1[0]; wf[5] = w1[1]; wf[6] = w1[2]; wf[7] = w1[3];
-      const float sw = sw_at(kk);
+      // (schemes 1 and 2 copy no activation scales: their sa reads see stale bytes, unused)
+      const float sw = SCH == 2 ? 0.0f : sw_at(kk);
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
         v8i af;
         af[0] = a0[j][0]; af[1] = a0[j][1]; af[2] = a0[j][2]; af[3] = a0[j][3];
         af[4] = a1[j][0]; af[5] = a1[j][1]; af[6] = a1[j][2]; af[7] = a1[j][3];
-        acc[j] += mfma_e4m3_16x16x128(wf, af) * (sa[j] * sw);
+        if constexpr (SCH == 0) acc[j] += mfma_e4m3_16x16x128(wf, af) * (sa[j] * sw);
+        else if constexpr (SCH == 1) acc[j] += mfma_f8_16x16x128<CODE>(wf, af, v4f{0.0f, 0.0f, 0.0f, 0.0f}) * sw;
+        else acc[j] = mfma_f8_16x16x128<CODE>(wf, af, acc[j]);
       }
     }
   }
@@ -255,7 +266,14 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
     const int m = 16 * j + (lane & 15);
-    if (m < M) store4<OUT>(p.y, p.ldy, m, n0 + 4 * (lane >> 4), acc[j]);
+    if (m < M) {
+      if constexpr (SCH != 0) {
+        // scales that do not vary along K: the token's (or the tensor's), then the channels'
+        acc[j] = acc[j] * gload<float>(p.s_a + (p.a_kind == 2 ? 0 : m));
+        if constexpr (SCH == 2) acc[j] = acc[j] * gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n0 + 4 * (lane >> 4));
+      }
+      store4<OUT>(p.y, p.ldy, m, n0 + 4 * (lane >> 4), acc[j]);
+    }
   }
 }
 

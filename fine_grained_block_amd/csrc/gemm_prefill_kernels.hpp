@@ -105,8 +105,15 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row0, int lane)
   return v;
 }
 
-template <typename C, int SWF, int OUT, bool GROUPED>
+// Scaling schemes (SCH): 0 = 1x128 activation groups and 128x128 weight blocks, scaled per K-block;
+// 1 = weight blocks scaled per K-block, one activation scale per token or per tensor applied in
+// the epilogue; 2 = per-channel weight scales and per-token or per-tensor activation scales, both
+// applied in the epilogue, so the MFMAs accumulate in place with no per-block factor.  CODE: the
+// operands' format (0 E4M3, 1 E5M2; schemes 1 and 2 only).
+template <typename C, int SWF, int OUT, bool GROUPED, int SCH = 0, int CODE = 0>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  static_assert(SCH == 0 || SCH == 1 || SCH == 2, "scheme");
+  static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
   // one __shared__ array per stage, so the compiler can tell in-flight copies from reads
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE];
@@ -242,8 +249,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // is off (num_records = 2^32 - 1): the library validated every operand's extent.
   // Copy d of block kb into stage st: 0 = the activation scales, then the W_LD weight and the
   // A_LD activation 8-row groups.
-  constexpr int NPART = 1 + C::W_LD + C::A_LD;
+  // (schemes 1 and 2 have no per-block activation scales to copy: part 0 is skipped)
+  constexpr int NPART = (SCH == 0 ? 1 : 0) + C::W_LD + C::A_LD;
   auto issue_part = [&](int kb, uint8_t* st, float* sas, int d) {
+    if constexpr (SCH != 0) d += 1;
 #if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, -1, 0x00020000);
@@ -283,9 +292,11 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // one broadcast LDS read.
   constexpr int NBT = C::BN / 128 > 0 ? C::BN / 128 : 1;
   __shared__ __attribute__((aligned(16))) float sws[NBT * 256];
-  for (int idx = tid; idx < NBT * KB; idx += C::THREADS) {
-    const int b = idx / KB, k = idx - b * KB;
-    sws[b * 256 + k] = load_sw<SWF>(p.s_w, sw_base + (n0 / 128 + b) * KB + k);
+  if constexpr (SCH != 2) {
+    for (int idx = tid; idx < NBT * KB; idx += C::THREADS) {
+      const int b = idx / KB, k = idx - b * KB;
+      sws[b * 256 + k] = load_sw<SWF>(p.s_w, sw_base + (n0 / 128 + b) * KB + k);
+    }
   }
   const float* sw_lds = sws + (int)(nb - n0 / 128) * 256;
 
@@ -308,6 +319,29 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     }
     const uint8_t* ws = st + wn * (C::BN / C::WN) * KBYTES;
     const uint8_t* as = st + C::W_BYTES + wm * (C::BM / C::WM) * KBYTES;
+    if constexpr (SCH == 2) {
+      // no per-block factor: every MFMA accumulates into its tile, fragments read in order of
+      // first use as below, the copies spread over the MFMAs
+      v8i af[2], bf[C::TM];
+      af[0] = lds_frag(ws, 0, lane);
+#pragma unroll
+      for (int j = 0; j < C::TM; ++j) bf[j] = lds_frag(as, j * 16, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int T = C::TN * C::TM;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        {
+          constexpr int SP = (NPART - 1) * SPACING < T ? SPACING : (T - 1) / (NPART - 1);
+          static_assert(SP >= 1 && (NPART - 1) * SP < T, "copies fit the MFMA sequence");
+          if (t % SP == 0 && t / SP < NPART) issue_part(kb_next, refill, sas_refill, t / SP);
+        }
+        const int i = t / C::TM, j = t % C::TM;
+        acc[i][j] = mfma_f8_16x16x128<CODE>(af[i & 1], bf[j], acc[i][j]);
+        if (j == 0 && i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
     float sc[C::TM];
     {
       // LDS reads in the order of first use (they complete in order, so a wait covers only what
@@ -336,18 +370,20 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
         }
         if (t < T) {
           const int i = t / C::TM, j = t % C::TM;
-          P[t % (LAG + 1)] = mfma_e4m3_16x16x128(af[i & 1], bf[j]);
+          P[t % (LAG + 1)] = mfma_f8_16x16x128<CODE>(af[i & 1], bf[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
           // fragment i+1 into the buffer whose MFMAs (fragment i-1) are all issued
           if (j == 0 && i + 1 < C::TN) af[(i + 1) & 1] = lds_frag(ws, (i + 1) * 16, lane);
           if (t == 1) {
+            if constexpr (SCH == 0) {
 #pragma unroll
-            for (int jj = 0; jj < C::TM; ++jj) sav[jj] = sas_cur[tok[jj]];
+              for (int jj = 0; jj < C::TM; ++jj) sav[jj] = sas_cur[tok[jj]];
+            }
             swv = *swp;
           }
         }
         if (t == LAG) {
 #pragma unroll
-          for (int j = 0; j < C::TM; ++j) sc[j] = sav[j] * swv;
+          for (int j = 0; j < C::TM; ++j) sc[j] = SCH == 0 ? sav[j] * swv : swv;
         }
         if (t >= LAG) {
           const int u = t - LAG;
@@ -389,6 +425,29 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   // any more; they must have landed before the stages are reused for the output tile below and
   // before the workgroup's LDS is released.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+
+  if constexpr (SCH != 0) {
+    // scales that do not vary along K: the activation scale of each token (or of the tensor),
+    // then, for scheme 2, the channel scale of each output feature
+    float ea[C::TM];
+#pragma unroll
+    for (int j = 0; j < C::TM; ++j) {
+      int64_t m = row0 + tok[j];
+      m = m < row_end ? m : row_end - 1;
+      ea[j] = gload<float>(p.s_a + (p.a_kind == 2 ? 0 : m));
+    }
+#pragma unroll
+    for (int i = 0; i < C::TN; ++i) {
+      v4f ew = {1.0f, 1.0f, 1.0f, 1.0f};
+      if constexpr (SCH == 2)
+        ew = gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n0 + wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4));
+#pragma unroll
+      for (int j = 0; j < C::TM; ++j) {
+        acc[i][j] = acc[i][j] * ea[j];
+        if constexpr (SCH == 2) acc[i][j] = acc[i][j] * ew;
+      }
+    }
+  }
 
   // epilogue.  bf16 tiles go through LDS in rounds of two 64-row chunks (stage0 and stage1, free
   // once every wave is past its last block) so that the global stores write whole 128-byte

@@ -9,7 +9,13 @@ namespace fgb {
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, float* s_a, int64_t ld_sa, hipStream_t stream);
 hipError_t launch_weight_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* wq, void* s_w,
-                               int fmt, hipStream_t stream);
+                               int fmt, hipStream_t stream, int code = 0);
+// one scale per row over the whole row (per-token activations, per-channel weights)
+hipError_t launch_row_quant(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                            float* s, int code, hipStream_t stream);
+// a given per-tensor scale (device float)
+hipError_t launch_static_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* scale,
+                               uint8_t* q, int64_t ldq, int code, hipStream_t stream);
 hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int fmt, int saturate,
                          hipStream_t stream);
 hipError_t launch_decode(const uint8_t* in, float* out, int64_t n, int fmt, hipStream_t stream);
@@ -31,6 +37,9 @@ struct GemmArgs {
   // grouped only
   const int32_t* offsets;
   int32_t E;
+  // other scaling schemes: the activation scale is per token (s_a[m], 1) or one for the tensor
+  // (s_a[0], 2); 0 = per 1x128 group (s_a K-block-major)
+  int a_kind;
 };
 
 // Prefill (M > 64) dense GEMM and the grouped variant.
@@ -38,6 +47,11 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_check_offsets(const int32_t* offsets, int32_t E, int64_t total_M, int32_t* result,
                                 hipStream_t stream);
+
+// The other scaling schemes (sch 1: per-token or per-tensor activation scale with 128x128 weight
+// blocks; sch 2: per-channel weight scales), E4M3 (code 0) or E5M2 (code 1) operands.
+hipError_t launch_gemm_scaled_prefill(const GemmArgs& a, int sch, int code, hipStream_t stream);
+hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int code, hipStream_t stream);
 
 // Split-K decode path (M <= 64).
 int decode_splits(int64_t M, int64_t N, int64_t K);

@@ -81,6 +81,28 @@ __device__ __forceinline__ float absmax8(const uint4 v) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
+constexpr float kE5M2Max = 57344.0f;
+
+// Quantize 8 values (4 bf16 pairs) to E5M2 with the IEEE quotient x / d (E5M2 resolves values down
+// to 2^-17, where the fast quotient may differ in its last bit) and the integer encoder (RNE,
+// saturating at +-57344).
+__device__ __forceinline__ uint2 quant8_e5m2(const uint4 w, float d) {
+  const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                      bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = enc_e5m2_int(f[i] / d, true);
+  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// Codes of 8 values for divisor d (the stored scale, or 1 where the scale is 0) in format CODE
+// (0 E4M3, 1 E5M2).
+template <int CODE>
+__device__ __forceinline__ uint2 quant8_code(const uint4 w, float d) {
+  if constexpr (CODE == 0) return quant8(w, make_divisor(d));
+  else return quant8_e5m2(w, d == 0.0f ? 1.0f : d);
+}
+
 // ---------------------------------------------------------------------------------------------
 // act_quant: a wave takes one work item at a time (grid-stride), an item being 4 * AQ_UNROLL
 // consecutive groups of one token row; 16 lanes per group (16 B = 8 bf16 each), so a wave covers
@@ -139,6 +161,7 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 // ---------------------------------------------------------------------------------------------
 // weight quant: one 256-thread block per 128x128 block; each thread holds 8 x 16 B (64 values).
 // ---------------------------------------------------------------------------------------------
+template <int CODE>
 __global__ __launch_bounds__(256) void weight_quant_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ wq,
     void* __restrict__ s_w, int fmt) {
@@ -165,26 +188,94 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
   am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float s;
   if (fmt == 0) {
-    s = am / kE4M3Max;
+    s = am / (CODE == 0 ? kE4M3Max : kE5M2Max);
     if (t == 0) reinterpret_cast<float*>(s_w)[blockIdx.x] = s;
   } else {
     uint32_t code = ue8m0_from_amax(am);
     s = dec_ue8m0(code);
     if (t == 0) reinterpret_cast<uint8_t*>(s_w)[blockIdx.x] = (uint8_t)code;
   }
-  const Divisor dv = make_divisor(s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int64_t row = nb * kBlock + r0 + 16 * i;
-    *reinterpret_cast<uint2*>(wq + row * K + kb * kBlock + chunk * 8) = quant8(v[i], dv);
+    *reinterpret_cast<uint2*>(wq + row * K + kb * kBlock + chunk * 8) = quant8_code<CODE>(v[i], s);
   }
 }
 
 hipError_t launch_weight_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* wq, void* s_w,
-                               int fmt, hipStream_t stream) {
+                               int fmt, hipStream_t stream, int code) {
   const int64_t blocks = (N / kBlock) * (K / kBlock);
-  hipLaunchKernelGGL(weight_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, K,
-                     wq, s_w, fmt);
+  if (code == 0)
+    hipLaunchKernelGGL(weight_quant_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, K, wq, s_w, fmt);
+  else
+    hipLaunchKernelGGL(weight_quant_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, K, wq, s_w, fmt);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-row quantization: one scale for each whole row (vLLM "FP8 W8A8", "Quantization process":
+// per-token activations and per-output-channel weights of the FP8_DYNAMIC scheme).  One
+// 256-thread workgroup per row: the amax over the row, s = fl32(amax / max), then the row is read
+// again (from the cache) and encoded.
+// ---------------------------------------------------------------------------------------------
+template <int CODE>
+__global__ __launch_bounds__(256) void row_quant_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t ldx,
+                                                        uint8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ s_out) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const int t = threadIdx.x;
+  const int nch = (int)(K / 8);  // 16-byte chunks of the row
+  const uint16_t* xr = x + m * ldx;
+  uint8_t* qr = q + m * ldq;
+  float am = 0.0f;
+  for (int c = t; c < nch; c += 256) am = fmaxf(am, absmax8(*reinterpret_cast<const uint4*>(xr + 8 * c)));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  if ((t & 63) == 0) red[t >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = am / (CODE == 0 ? kE4M3Max : kE5M2Max);  // IEEE float32 division
+  if (t == 0) s_out[m] = s;
+  for (int c = t; c < nch; c += 256)
+    *reinterpret_cast<uint2*>(qr + 8 * c) = quant8_code<CODE>(*reinterpret_cast<const uint4*>(xr + 8 * c), s);
+}
+
+hipError_t launch_row_quant(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                            float* s, int code, hipStream_t stream) {
+  if (code == 0)
+    hipLaunchKernelGGL(row_quant_kernel<0>, dim3((unsigned)rows), dim3(256), 0, stream, x, K, ldx, q, ldq, s);
+  else
+    hipLaunchKernelGGL(row_quant_kernel<1>, dim3((unsigned)rows), dim3(256), 0, stream, x, K, ldx, q, ldq, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Static quantization with a given per-tensor scale (Transformers "Fine-grained FP8", "DeepGEMM
+// fast path": static activations): codes E(fl32(x / s)), s read from device memory.  Grid-stride
+// over 16-byte chunks of the rows.
+// ---------------------------------------------------------------------------------------------
+template <int CODE>
+__global__ __launch_bounds__(256) void static_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                           int64_t ldx, const float* __restrict__ scale,
+                                                           uint8_t* __restrict__ q, int64_t ldq) {
+  const float s = *scale;
+  const int64_t cpr = K / 8, total = M * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / cpr, c = i - m * cpr;
+    *reinterpret_cast<uint2*>(q + m * ldq + 8 * c) =
+        quant8_code<CODE>(*reinterpret_cast<const uint4*>(x + m * ldx + 8 * c), s);
+  }
+}
+
+hipError_t launch_static_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* scale,
+                               uint8_t* q, int64_t ldq, int code, hipStream_t stream) {
+  int64_t blocks = (M * (K / 8) + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (code == 0)
+    hipLaunchKernelGGL(static_quant_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, x, M, K, ldx, scale, q, ldq);
+  else
+    hipLaunchKernelGGL(static_quant_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, x, M, K, ldx, scale, q, ldq);
   return hipGetLastError();
 }
 

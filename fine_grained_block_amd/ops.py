@@ -12,7 +12,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import FP8_E4M3, OUT_BF16, OUT_F32, SCALE_F32, SCALE_UE8M0, check, lib
+from ._lib import (ACT_SCALE_TENSOR, ACT_SCALE_TOKEN, FP8_E4M3, FP8_E5M2, OUT_BF16, OUT_F32, SCALE_F32,
+                   SCALE_UE8M0, W_SCALE_BLOCK128, W_SCALE_CHANNEL, check, lib)
 
 BLOCK = 128
 
@@ -107,10 +108,20 @@ def quantize(x: torch.Tensor, out: tuple | None = None):
     return q, s_a
 
 
-def quantize_weight(w: torch.Tensor, scale_fmt: str = "float"):
-    """Per-128x128-block E4M3 weight quantization of a dense bf16 [N, K] matrix.
+_CODES = {"e4m3": FP8_E4M3, "e5m2": FP8_E5M2}
+
+
+def _code(code: str) -> int:
+    c = _CODES.get(code)
+    _need(c is not None, "code must be 'e4m3' or 'e5m2'")
+    return c
+
+
+def quantize_weight(w: torch.Tensor, scale_fmt: str = "float", code: str = "e4m3"):
+    """Per-128x128-block weight quantization of a dense bf16 [N, K] matrix.
 
     scale_fmt "float" -> s_w float32 [N/128, K/128]; "ue8m0" -> s_w uint8 UE8M0 codes.
+    code "e4m3" (default) or "e5m2" (float32 scales amax/57344).
     """
     _need(isinstance(w, torch.Tensor) and w.dim() == 2, "quantize_weight expects a 2-D tensor")
     _dense(w, "w", (torch.bfloat16,), tuple(w.shape))
@@ -123,9 +134,108 @@ def quantize_weight(w: torch.Tensor, scale_fmt: str = "float"):
     w_q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     sdt = torch.float32 if fmt == SCALE_F32 else torch.uint8
     s_w = torch.empty((max(NB, 1), max(KB, 1)), dtype=sdt, device=w.device)
-    st = lib().fgb_weight_quant_block128(_ptr(w), N, K, _ptr(w_q), _ptr(s_w), fmt, _stream())
-    check("fgb_weight_quant_block128", st)
+    if code == "e4m3":
+        st = lib().fgb_weight_quant_block128(_ptr(w), N, K, _ptr(w_q), _ptr(s_w), fmt, _stream())
+        check("fgb_weight_quant_block128", st)
+    else:
+        st = lib().fgb_weight_quant_block128_ex(_ptr(w), N, K, _code(code), _ptr(w_q), _ptr(s_w), fmt, _stream())
+        check("fgb_weight_quant_block128_ex", st)
     return w_q, s_w
+
+
+def quantize_per_token(x: torch.Tensor, code: str = "e4m3", out: tuple | None = None):
+    """Dynamic per-token quantization (FP8_DYNAMIC activations): one scale per row over the whole
+    K.  Returns (q uint8 [M, K], s_a float32 [M])."""
+    _matrix(x, "x", torch.bfloat16)
+    M, K = x.shape
+    _blocks(K, "K")
+    if out is None:
+        _on_device(("x", x))
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        s_a = torch.empty((max(M, 1),), dtype=torch.float32, device=x.device)
+    else:
+        q, s_a = out
+        _matrix(q, "q", torch.uint8, rows=M, cols=K)
+        _dense(s_a, "s_a", (torch.float32,), (M,))
+        _on_device(("x", x), ("q", q), ("s_a", s_a))
+    st = lib().fgb_act_quant_per_token(_ptr(x), M, K, _row_ld(x), _code(code), _ptr(q), _row_ld(q), _ptr(s_a),
+                                       _stream())
+    check("fgb_act_quant_per_token", st)
+    return q, s_a
+
+
+def quantize_weight_per_channel(w: torch.Tensor, code: str = "e4m3"):
+    """Per-output-channel weight quantization (FP8_DYNAMIC weights) of a dense bf16 [N, K]
+    matrix.  Returns (w_q uint8 [N, K], s_w float32 [N])."""
+    _need(isinstance(w, torch.Tensor) and w.dim() == 2, "expects a 2-D tensor")
+    _dense(w, "w", (torch.bfloat16,), tuple(w.shape))
+    N, K = w.shape
+    _blocks(N, "N"), _blocks(K, "K")
+    _on_device(("w", w))
+    w_q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s_w = torch.empty((max(N, 1),), dtype=torch.float32, device=w.device)
+    st = lib().fgb_weight_quant_per_channel(_ptr(w), N, K, _code(code), _ptr(w_q), _ptr(s_w), _stream())
+    check("fgb_weight_quant_per_channel", st)
+    return w_q, s_w
+
+
+def quantize_static(x: torch.Tensor, scale: torch.Tensor, code: str = "e4m3", out: torch.Tensor | None = None):
+    """Quantization with a given per-tensor scale (static activations): q = E(fl32(x / scale)).
+    scale: float32 device tensor with one element (finite, > 0: not checked)."""
+    _matrix(x, "x", torch.bfloat16)
+    M, K = x.shape
+    _blocks(K, "K")
+    _dense(scale, "scale", (torch.float32,), tuple(scale.shape))
+    _need(scale.numel() == 1, "scale must hold one value")
+    if out is not None:
+        _matrix(out, "out", torch.uint8, rows=M, cols=K)
+    _on_device(("x", x), ("scale", scale), ("out", out))
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if out is None else out
+    st = lib().fgb_act_quant_static(_ptr(x), M, K, _row_ld(x), _ptr(scale), _code(code), _ptr(q), _row_ld(q),
+                                    _stream())
+    check("fgb_act_quant_static", st)
+    return q
+
+
+def scaled_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor,
+                act_scale: str = "token", code: str = "e4m3", out_dtype=torch.bfloat16,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """GEMM with per-token (s_a float32 [M]) or per-tensor (s_a float32 [1]) activation scales and
+    per-channel (s_w float32 [N]) or 128x128-block (s_w [N/128, K/128], float32 or UE8M0) weight
+    scales; both operands in `code` ("e4m3" or "e5m2")."""
+    _matrix(a_q, "a_q", torch.uint8)
+    M, K = a_q.shape
+    KB = _blocks(K, "K")
+    _need(isinstance(w_q, torch.Tensor) and w_q.dim() == 2, "w_q must be [N, K]")
+    N = w_q.shape[0]
+    NB = _blocks(N, "N")
+    _dense(w_q, "w_q", (torch.uint8,), (N, K))
+    if act_scale == "token":
+        ak = ACT_SCALE_TOKEN
+        _dense(s_a, "s_a", (torch.float32,), (M,))
+    elif act_scale == "tensor":
+        ak = ACT_SCALE_TENSOR
+        _dense(s_a, "s_a", (torch.float32,), tuple(s_a.shape))
+        _need(s_a.numel() == 1, "a per-tensor s_a holds one value")
+    else:
+        raise ValueError("act_scale must be 'token' or 'tensor'")
+    if s_w.dim() == 1:
+        wk = W_SCALE_CHANNEL
+        _dense(s_w, "s_w", (torch.float32,), (N,))
+    else:
+        wk = W_SCALE_BLOCK128
+        _dense(s_w, "s_w", (torch.float32, torch.uint8), (NB, KB))
+    if out is not None:
+        _need(out.dtype in (torch.bfloat16, torch.float32), "out must be bf16 or float32")
+        _matrix(out, "out", out.dtype, rows=M, cols=N)
+    _on_device(("a_q", a_q), ("s_a", s_a), ("w_q", w_q), ("s_w", s_w), ("out", out))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    st = lib().fgb_w8a8_scaled_gemm(_ptr(a_q), _row_ld(a_q), _ptr(s_a), ak, _ptr(w_q), _ptr(s_w), wk,
+                                    _scale_fmt(s_w), _code(code), _ptr(out), _out_code(out.dtype), _row_ld(out),
+                                    M, N, K, _stream())
+    check("fgb_w8a8_scaled_gemm", st)
+    return out
 
 
 def _scale_fmt(s_w: torch.Tensor) -> int:

@@ -60,6 +60,17 @@ typedef enum {
   FGB_FP8_E4M3_INT = 3  /* encode only: integer bit-field encoder, to check the hardware path */
 } fgb_fp8_fmt;
 
+/* Activation and weight scale granularities of fgb_w8a8_scaled_gemm. */
+typedef enum {
+  FGB_ACT_SCALE_GROUP128 = 0, /* one scale per token per 1x128 group: fgb_w8a8_block_gemm */
+  FGB_ACT_SCALE_TOKEN = 1,    /* one scale per token (row), float32 [M] */
+  FGB_ACT_SCALE_TENSOR = 2    /* one scale for the whole tensor, float32 [1] */
+} fgb_act_scale;
+typedef enum {
+  FGB_W_SCALE_BLOCK128 = 0, /* one scale per 128x128 block, [N/128, K/128] float32 or UE8M0 */
+  FGB_W_SCALE_CHANNEL = 1   /* one scale per output feature (row of W), float32 [N] */
+} fgb_w_scale;
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fgb_status_string(int status);
 
@@ -165,6 +176,55 @@ int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
  */
 int fgb_check_expert_offsets(const int32_t* expert_offsets, int32_t E, int64_t total_M, int32_t* result,
                              void* stream);
+
+/*
+ * The other FP8 schemes.  FP8_DYNAMIC (vLLM "FP8 W8A8", "Quantization process": static
+ * per-channel weights, dynamic per-token activations, round-to-nearest); static activation
+ * quantization with a given per-tensor scale (Transformers "Fine-grained FP8", "DeepGEMM fast
+ * path"); E5M2 codes (vLLM "FP8 W8A8", "Two FP8 representations").  code_fmt is FGB_FP8_E4M3 or
+ * FGB_FP8_E5M2; every scale divides by that format's maximum (448 or 57344); codes are
+ * E(fl32(x / s)) rounded to nearest-even and saturated to the format's maximum; a scale of 0 (an
+ * all-zero row or block) gives codes +-0 by sign.  Bit-exact.  Other rules as above
+ * (FGB_ERR_ENUM for an unknown or unsupported format).
+ */
+
+/* Per-token activation quantization: s_a[m] = fl32(max_k |x[m, k]| / max) over the whole row.
+ *   x bf16 [M, ldx]; q [M, ldq]; s_a float32 [M] (4-byte aligned).  K % 128 == 0. */
+int fgb_act_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int code_fmt,
+                            uint8_t* q, int64_t ldq, float* s_a, void* stream);
+
+/* Per-output-channel weight quantization: s_w[n] = fl32(max_k |w[n, k]| / max) over row n of
+ * the dense bf16 [N, K] weight; w_q [N, K]; s_w float32 [N].  N and K multiples of 128. */
+int fgb_weight_quant_per_channel(const uint16_t* w, int64_t N, int64_t K, int code_fmt,
+                                 uint8_t* w_q, float* s_w, void* stream);
+
+/* Quantization with a given per-tensor scale: q = E(fl32(x / scale[0])).
+ *   scale: DEVICE float32 [1], finite and > 0 (its value is a precondition: read on the
+ *   device, not checked); x bf16 [M, ldx]; q [M, ldq].  K % 128 == 0. */
+int fgb_act_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* scale,
+                         int code_fmt, uint8_t* q, int64_t ldq, void* stream);
+
+/* fgb_weight_quant_block128 with a choice of code format: E5M2 codes take float32 scales
+ * amax/57344 (s_w_fmt FGB_SCALE_F32 only); E4M3 codes as fgb_weight_quant_block128. */
+int fgb_weight_quant_block128_ex(const uint16_t* w, int64_t N, int64_t K, int code_fmt,
+                                 uint8_t* w_q, void* s_w, int s_w_fmt, void* stream);
+
+/*
+ * GEMM under those scales, both operands in code_fmt (E4M3 x E4M3 or E5M2 x E5M2):
+ *   act_scale TOKEN:  a(m) = s_a[m] (float32 [M]);  TENSOR: a(m) = s_a[0] (float32 [1]);
+ *   w_scale CHANNEL:  y[m, n] = a(m) * s_w[n] * sum_k A_q[m, k] * W_q[n, k]   (s_w float32 [N],
+ *                     16-byte aligned);
+ *   w_scale BLOCK128: y[m, n] = a(m) * sum_kb s_w[n/128, kb] * sum_{k in kb} A_q[m, k] W_q[n, k]
+ *                     (s_w [N/128, K/128] float32, or UE8M0 with E4M3 codes).
+ * Products are summed in float32 on the matrix cores; scales that do not vary along K multiply
+ * the float32 sum once at the end.  a_q [M, lda]; w_q [N, K] dense; y [M, ldy] bf16 or float32.
+ * act_scale GROUP128 is FGB_ERR_ENUM here (that is fgb_w8a8_block_gemm).  One launch, no
+ * workspace.  Size limits as for fgb_w8a8_block_gemm.
+ */
+int fgb_w8a8_scaled_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int act_scale,
+                         const uint8_t* w_q, const void* s_w, int w_scale, int s_w_fmt,
+                         int code_fmt, void* y, int y_dtype, int64_t ldy,
+                         int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Element-wise codecs (vLLM "FP8 W8A8", "Two FP8 representations"; UE8M0 per Transformers

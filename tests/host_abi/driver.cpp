@@ -143,6 +143,48 @@ int main() {
   EXPECT(fgb_selftest_quotients((unsigned long long*)P(F + 4), nullptr), FGB_ERR_ALIGN);
   EXPECT(fgb_selftest_quotients((unsigned long long*)P(F), nullptr), FGB_OK);
 
+  // the other schemes: per-token / per-channel / static quantizers and the scaled GEMM
+  EXPECT(fgb_act_quant_per_token((const uint16_t*)P(F), 64, 1024, 1024, 7, (uint8_t*)P(F), 1024, (float*)P(F),
+                                 nullptr), FGB_ERR_ENUM);
+  EXPECT(fgb_act_quant_per_token((const uint16_t*)P(F), 64, 1000, 1000, 0, (uint8_t*)P(F), 1008, (float*)P(F),
+                                 nullptr), FGB_ERR_SHAPE);
+  EXPECT(fgb_act_quant_per_token((const uint16_t*)P(F), 64, 1024, 1024, 1, (uint8_t*)P(F), 1024, (float*)P(F + 2),
+                                 nullptr), FGB_ERR_ALIGN);
+  EXPECT(fgb_act_quant_per_token((const uint16_t*)P(F), 64, 1024, 512, 1, (uint8_t*)P(F), 1024, (float*)P(F),
+                                 nullptr), FGB_ERR_STRIDE);
+  EXPECT(fgb_act_quant_per_token((const uint16_t*)P(F), 64, 1024, 1024, 1, (uint8_t*)P(F), 1024, (float*)P(F + 4),
+                                 nullptr), FGB_OK);
+  if (strcmp(g_stub.last, "row_quant") || g_stub.M != 64 || g_stub.K != 1024) failures++;
+  EXPECT(fgb_weight_quant_per_channel((const uint16_t*)P(F), 200, 1024, 0, (uint8_t*)P(F), (float*)P(F), nullptr),
+         FGB_ERR_SHAPE);
+  EXPECT(fgb_weight_quant_per_channel((const uint16_t*)P(F), 256, 1024, 0, (uint8_t*)P(F), (float*)P(F), nullptr),
+         FGB_OK);
+  EXPECT(fgb_act_quant_static((const uint16_t*)P(F), 64, 1024, 1024, nullptr, 0, (uint8_t*)P(F), 1024, nullptr),
+         FGB_ERR_NULL);
+  EXPECT(fgb_act_quant_static((const uint16_t*)P(F), 64, 1024, 1024, (const float*)P(F + 1), 0, (uint8_t*)P(F),
+                              1024, nullptr), FGB_ERR_ALIGN);
+  EXPECT(fgb_act_quant_static((const uint16_t*)P(F), 64, 1024, 1024, (const float*)P(F + 4), 1, (uint8_t*)P(F),
+                              1024, nullptr), FGB_OK);
+  EXPECT(fgb_weight_quant_block128_ex((const uint16_t*)P(F), 128, 128, 1, (uint8_t*)P(F), P(F), 1, nullptr),
+         FGB_ERR_ENUM);  // UE8M0 scales go with E4M3 codes
+  EXPECT(fgb_weight_quant_block128_ex((const uint16_t*)P(F), 128, 128, 1, (uint8_t*)P(F), P(F), 0, nullptr), FGB_OK);
+  auto scaled = [](int64_t M, int ak, int wk, int swf, int code, uintptr_t sa = F + 4, uintptr_t sw = F) {
+    return fgb_w8a8_scaled_gemm((const uint8_t*)P(F), 1024, (const float*)P(sa), ak, (const uint8_t*)P(F), P(sw), wk,
+                                swf, code, P(F), 0, 512, M, 512, 1024, nullptr);
+  };
+  EXPECT(scaled(256, FGB_ACT_SCALE_GROUP128, FGB_W_SCALE_BLOCK128, 0, 0), FGB_ERR_ENUM);
+  EXPECT(scaled(256, FGB_ACT_SCALE_TOKEN, 5, 0, 0), FGB_ERR_ENUM);
+  EXPECT(scaled(256, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 1, 0), FGB_ERR_ENUM);   // UE8M0 per channel
+  EXPECT(scaled(256, FGB_ACT_SCALE_TENSOR, FGB_W_SCALE_BLOCK128, 1, 1), FGB_ERR_ENUM);  // UE8M0 with E5M2
+  EXPECT(scaled(256, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 3), FGB_ERR_ENUM);
+  EXPECT(scaled(256, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 0, F + 2), FGB_ERR_ALIGN);
+  EXPECT(scaled(256, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 0, F + 4, F + 4), FGB_ERR_ALIGN);
+  EXPECT(scaled(0, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 0), FGB_OK);
+  EXPECT(scaled(256, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 1), FGB_OK);
+  if (strcmp(g_stub.last, "scaled_prefill") || g_stub.E != 2 || g_stub.M != 256) failures++;
+  EXPECT(scaled(64, FGB_ACT_SCALE_TENSOR, FGB_W_SCALE_BLOCK128, 1, 0), FGB_OK);
+  if (strcmp(g_stub.last, "scaled_decode") || g_stub.E != 1) failures++;
+
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -41,8 +41,28 @@ hipError_t launch_act_quant(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*
                             hipStream_t) {
   return launched("act_quant");
 }
-hipError_t launch_weight_quant(const uint16_t*, int64_t, int64_t, uint8_t*, void*, int, hipStream_t) {
+hipError_t launch_weight_quant(const uint16_t*, int64_t, int64_t, uint8_t*, void*, int, hipStream_t, int) {
   return launched("weight_quant");
+}
+hipError_t launch_row_quant(const uint16_t*, int64_t rows, int64_t K, int64_t, uint8_t*, int64_t, float*, int,
+                            hipStream_t) {
+  g_stub.M = rows;
+  g_stub.K = K;
+  return launched("row_quant");
+}
+hipError_t launch_static_quant(const uint16_t*, int64_t, int64_t, int64_t, const float*, uint8_t*, int64_t, int,
+                               hipStream_t) {
+  return launched("static_quant");
+}
+hipError_t launch_gemm_scaled_prefill(const GemmArgs& a, int sch, int, hipStream_t) {
+  record(a);
+  g_stub.E = sch;
+  return launched("scaled_prefill");
+}
+hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int, hipStream_t) {
+  record(a);
+  g_stub.E = sch;
+  return launched("scaled_decode");
 }
 hipError_t launch_encode(const float*, uint8_t*, int64_t, int, int, hipStream_t) { return launched("encode"); }
 hipError_t launch_decode(const uint8_t*, float*, int64_t, int, hipStream_t) { return launched("decode"); }
