@@ -38,6 +38,7 @@ from .ops import (  # noqa: F401
     scaled_gemm,
     gemm,
     gemm_noalloc,
+    gemm_fused_quant,
     grouped_gemm,
     check_offsets,
     gemm_workspace_bytes,

@@ -245,6 +245,26 @@ int fgb_w8a8_scaled_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int 
   return launch_status(fgb::launch_gemm_scaled_prefill(a, sch, code, (hipStream_t)stream));
 }
 
+int fgb_w8a8_block_gemm_fused_quant(const uint16_t* x, int64_t ldx, const uint8_t* w_q, const void* s_w,
+                                    int s_w_fmt, void* y, int y_dtype, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                    void* stream) {
+  if (M < 0 || M > 64 || N <= 0 || K <= 0 || N >= kMaxDim || K >= kMaxDim) return FGB_ERR_SHAPE;
+  if (N % FGB_BLOCK || K % FGB_BLOCK) return FGB_ERR_SHAPE;
+  if (s_w_fmt != FGB_SCALE_F32 && s_w_fmt != FGB_SCALE_UE8M0) return FGB_ERR_ENUM;
+  if (y_dtype != FGB_OUT_BF16 && y_dtype != FGB_OUT_F32) return FGB_ERR_ENUM;
+  if (M == 0) return FGB_OK;
+  if (!x || !w_q || !s_w || !y) return FGB_ERR_NULL;
+  if (ldx < K || ldy < N) return FGB_ERR_STRIDE;
+  const int64_t ybytes = y_dtype == FGB_OUT_BF16 ? 2 : 4;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(s_w) || !aligned16(y)) return FGB_ERR_ALIGN;
+  if ((ldx * 2) % 16 || (ldy * ybytes) % 16) return FGB_ERR_ALIGN;
+  if (M * ldx * 2 >= kMax32 || N * K >= kMax32 || K > 32768) return FGB_ERR_SHAPE;
+  int st = check_device();
+  if (st != FGB_OK) return st;
+  fgb::GemmArgs a{nullptr, 0, nullptr, 0, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K, nullptr, 1, 0};
+  return launch_status(fgb::launch_gemm_decode_fused(a, x, ldx, (hipStream_t)stream));
+}
+
 size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, int32_t E) {
   (void)total_M; (void)N; (void)K; (void)E;
   return 0;

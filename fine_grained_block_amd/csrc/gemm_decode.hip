@@ -10,12 +10,18 @@ namespace fgb {
 namespace {
 
 // waves splitting K per 16-row tile for the small-M kernel: about 4k waves in total
-int small_waves(int64_t N, int64_t K) {
+int small_waves(int64_t N, int64_t K) { return decode_small_waves(N, K); }
+
+}  // namespace
+
+int decode_small_waves(int64_t N, int64_t K) {
   const int64_t tiles = N / 16;
   int wk = 1;
   while (wk < 8 && tiles * wk * 2 <= 4096 && wk * 2 <= K / 128) wk *= 2;
   return wk;
 }
+
+namespace {
 
 // weights from this size on take the LDS-ring kernel for M <= 16
 constexpr int64_t kRingMinWeightBytes = 48ll << 20;

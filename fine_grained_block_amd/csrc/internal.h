@@ -53,6 +53,11 @@ hipError_t launch_check_offsets(const int32_t* offsets, int32_t E, int64_t total
 hipError_t launch_gemm_scaled_prefill(const GemmArgs& a, int sch, int code, hipStream_t stream);
 hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int code, hipStream_t stream);
 
+// Decode GEMM that quantizes its bf16 activations itself (M <= 64).
+hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream);
+// waves per 16-row workgroup that split K in the M <= 16 decode kernels
+int decode_small_waves(int64_t N, int64_t K);
+
 // Split-K decode path (M <= 64).
 int decode_splits(int64_t M, int64_t N, int64_t K);
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -352,6 +352,31 @@ def check_offsets(offsets: torch.Tensor, total_M: int) -> int:
     return int(result.item())
 
 
+def gemm_fused_quant(x: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor, out_dtype=torch.bfloat16,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode-sized (M <= 64) fine-grained FP8 linear in one launch: the GEMM quantizes the bf16
+    activations per token and 1x128 group itself (same codes and scales as quantize())."""
+    _matrix(x, "x", torch.bfloat16)
+    M, K = x.shape
+    KB = _blocks(K, "K")
+    _need(M <= 64, "gemm_fused_quant is for M <= 64 (use quantize + gemm)")
+    _need(isinstance(w_q, torch.Tensor) and w_q.dim() == 2, "w_q must be [N, K]")
+    N = w_q.shape[0]
+    NB = _blocks(N, "N")
+    _dense(w_q, "w_q", (torch.uint8,), (N, K))
+    _dense(s_w, "s_w", (torch.float32, torch.uint8), (NB, KB))
+    if out is not None:
+        _need(out.dtype in (torch.bfloat16, torch.float32), "out must be bf16 or float32")
+        _matrix(out, "out", out.dtype, rows=M, cols=N)
+    _on_device(("x", x), ("w_q", w_q), ("s_w", s_w), ("out", out))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    st = lib().fgb_w8a8_block_gemm_fused_quant(_ptr(x), _row_ld(x), _ptr(w_q), _ptr(s_w), _scale_fmt(s_w), _ptr(out),
+                                               _out_code(out.dtype), _row_ld(out), M, N, K, _stream())
+    check("fgb_w8a8_block_gemm_fused_quant", st)
+    return out
+
+
 def linear(x: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
     """One fine-grained FP8 linear: dynamic activation quantization, then the block GEMM."""
     q, s_a = quantize(x)

@@ -185,6 +185,20 @@ int main() {
   EXPECT(scaled(64, FGB_ACT_SCALE_TENSOR, FGB_W_SCALE_BLOCK128, 1, 0), FGB_OK);
   if (strcmp(g_stub.last, "scaled_decode") || g_stub.E != 1) failures++;
 
+  // the fused-quantization decode GEMM
+  auto fused = [](int64_t M, int64_t ldx, uintptr_t xp = F) {
+    return fgb_w8a8_block_gemm_fused_quant((const uint16_t*)P(xp), ldx, (const uint8_t*)P(F), P(F), 0, P(F), 0, 512,
+                                           M, 512, 1024, nullptr);
+  };
+  EXPECT(fused(65, 1024), FGB_ERR_SHAPE);
+  EXPECT(fused(16, 1000), FGB_ERR_STRIDE);
+  EXPECT(fused(16, 1028), FGB_ERR_ALIGN);
+  EXPECT(fused(16, 1024, F + 2), FGB_ERR_ALIGN);
+  EXPECT(fused(16, 1024, 0), FGB_ERR_NULL);
+  EXPECT(fused(0, 1024), FGB_OK);
+  EXPECT(fused(64, 1024), FGB_OK);
+  if (strcmp(g_stub.last, "gemm_fused") || g_stub.M != 64) failures++;
+
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -81,6 +81,11 @@ hipError_t launch_check_offsets(const int32_t*, int32_t, int64_t, int32_t*, hipS
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (M == 32 && N == 4096 && K == 4096) ? (size_t)g_stub.ws_bytes_query : 0;
 }
+hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t*, int64_t, hipStream_t) {
+  record(a);
+  return launched("gemm_fused");
+}
+int decode_small_waves(int64_t, int64_t) { return 8; }
 hipError_t decode_scratch(void** out) {
   *out = (void*)0x200000;  // stands for the library's scratch address
   return hipSuccess;
