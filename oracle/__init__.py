@@ -10,7 +10,8 @@ Modules
 -------
 fp8        E4M3 / E5M2 / UE8M0 decode and encode from the bit fields (float64, exact)
 blockquant act_quant (dynamic 1x128 groups), weight_quant (128x128 blocks, float32 or UE8M0)
-gemm       gemm_ref (exact per-block partials, float64), gemm_ref_fast, grouped_ref, bf16_rne
+gemm       gemm_ref (exact per-block partials, float64), gemm_ref_fast, grouped_ref,
+           batched_ref (masked [E, max_M] expert slots), bf16_rne
 schemes    per-token / per-channel (FP8_DYNAMIC) and static per-tensor quantization, E5M2 codes,
            and the GEMM under those scales (scaled_gemm_ref)
 
@@ -23,4 +24,4 @@ the functions above; the GEMM's float32 summation order on the GPU is judged by 
 from . import fp8, blockquant, gemm, schemes  # noqa: F401
 from .fp8 import dec_e4m3, dec_e5m2, dec_ue8m0, enc_e4m3_sat, enc_e5m2, ue8m0_from_amax  # noqa: F401
 from .blockquant import act_quant, weight_quant  # noqa: F401
-from .gemm import gemm_ref, gemm_ref_fast, grouped_ref, bf16_rne  # noqa: F401
+from .gemm import gemm_ref, gemm_ref_fast, grouped_ref, batched_ref, bf16_rne  # noqa: F401

@@ -108,3 +108,25 @@ def bf16_rne(y) -> np.ndarray:
     out = np.where(out > 3.3895313892515355e38, np.inf, out)
     return np.copysign(out, y)
 
+
+def batched_ref(a_q, s_a, w_q, s_w, counts, max_m: int, fmt: str = "f32", fast: bool = False):
+    """Masked batched layout: expert e owns rows e*max_m .. e*max_m + counts[e] - 1 of a_q
+    [E*max_m, K] and s_a [E*max_m, KB]; the remaining rows of its slot are padding.
+
+    Returns (y float64 [E*max_m, N], valid bool [E*max_m]): y holds the per-expert block GEMM on
+    the valid rows and 0 on padding rows (whose output is not defined)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = w_q.shape[0]
+    N = w_q.shape[1]
+    if counts.shape != (E,) or np.any(counts < 0) or np.any(counts > max_m) or a_q.shape[0] != E * max_m:
+        raise ValueError("counts must be [E] within 0 .. max_m, a_q [E*max_m, K]")
+    f = gemm_ref_fast if fast else gemm_ref
+    y = np.zeros((E * max_m, N), dtype=np.float64)
+    valid = np.zeros(E * max_m, dtype=bool)
+    for e in range(E):
+        r0, r1 = e * max_m, e * max_m + counts[e]
+        valid[r0:r1] = True
+        if r1 > r0:
+            y[r0:r1] = f(a_q[r0:r1], s_a[r0:r1], w_q[e], s_w[e], fmt)
+    return y, valid
+

@@ -148,3 +148,25 @@ def test_bf16_rne_matches_torch_on_float32_values():
     x = np.random.default_rng(7).standard_normal(100000).astype(np.float32) * np.float32(1e3)
     t = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
     assert np.array_equal(gemm.bf16_rne(x.astype(np.float64)), t)
+
+
+def test_batched_reduces_to_grouped_with_empty_and_full_experts():
+    """The masked batched layout equals the contiguous grouped layout on the valid rows: gather
+    them in expert order, offsets from the running sum of the counts (zero-count experts, full
+    slots and a partly filled slot included)."""
+    E, max_m, N, K = 5, 24, 256, 384
+    counts = np.array([0, 24, 7, 0, 1])
+    rng = np.random.default_rng(11)
+    aq, sa = blockquant.act_quant(workloads.activations(E * max_m, K, key=(0, 70, 0, 0)))
+    wq = np.stack([blockquant.weight_quant(workloads.weights(N, K, key=(0, 70, 1, e)))[0] for e in range(E)])
+    sw = rng.uniform(1e-4, 1e-3, size=(E, N // 128, K // 128)).astype(np.float32)
+    y, valid = gemm.batched_ref(aq, sa, wq, sw, counts, max_m)
+    rows = np.concatenate([np.arange(e * max_m, e * max_m + counts[e]) for e in range(E)])
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    yg = gemm.grouped_ref(aq[rows], sa[rows], wq, sw, offsets)
+    assert valid.sum() == counts.sum() and np.array_equal(np.nonzero(valid)[0], rows)
+    assert np.array_equal(y[rows], yg)
+    assert np.all(y[~valid] == 0)
+    with pytest.raises(ValueError):
+        gemm.batched_ref(aq, sa, wq, sw, np.array([0, 25, 0, 0, 0]), max_m)
+

@@ -115,6 +115,16 @@ def _scaled_tensor_scale_dropped(a_q, a_scale, w_q, w_scale, **kw):
     return _orig_scaled(a_q, a_scale, w_q, w_scale, **kw)
 
 
+_orig_batched = gemm.batched_ref
+
+
+def _batched_shifted_slots(a_q, s_a, w_q, s_w, counts, max_m, fmt="f32", fast=False):
+    """expert e's slot taken to start one row late"""
+    a2 = np.roll(a_q, -1, axis=0)
+    s2 = np.roll(s_a, -1, axis=0)
+    return _orig_batched(a2, s2, w_q, s_w, counts, max_m, fmt, fast)
+
+
 MUTANTS = [
     ("decode bias 8", fp8, "dec_e4m3", _dec_bias8, [T8.test_e4m3_printed_facts, T8.test_e4m3_matches_torch_table]),
     ("ties away from zero", fp8, "enc_e4m3_sat", _enc_ties_away, [T8.test_enc_e4m3_bruteforce, TQ.test_golden_handworked_groups]),
@@ -130,6 +140,8 @@ MUTANTS = [
      [TS.test_static_quant_divides_by_the_scale]),
     ("channel scale on rows", schemes, "scaled_gemm_ref", _scaled_channel_by_row,
      [TS.test_token_channel_gemm_reduces_to_block_gemm]),
+    ("batched slot off by one row", gemm, "batched_ref", _batched_shifted_slots,
+     [TG.test_batched_reduces_to_grouped_with_empty_and_full_experts]),
     ("static scale dropped", schemes, "scaled_gemm_ref", _scaled_tensor_scale_dropped,
      [lambda: TS.test_tensor_block_gemm_reduces_to_block_gemm("f32")]),
 ]
