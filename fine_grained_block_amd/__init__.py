@@ -40,6 +40,7 @@ from .ops import (  # noqa: F401
     gemm_noalloc,
     gemm_fused_quant,
     grouped_gemm,
+    batched_gemm,
     check_offsets,
     gemm_workspace_bytes,
     fp8_encode,

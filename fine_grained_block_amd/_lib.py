@@ -31,6 +31,9 @@ _SIGS = {
     "fgb_grouped_w8a8_block_gemm": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _vp, _vp, ctypes.c_int, _vp,
                                                    ctypes.c_int32, _c_i64, _vp, ctypes.c_int, _c_i64, _c_i64,
                                                    _c_i64, _vp, ctypes.c_size_t, _vp]),
+    "fgb_batched_w8a8_block_gemm": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _vp, _vp, ctypes.c_int, _vp,
+                                                   ctypes.c_int32, _c_i64, _vp, ctypes.c_int, _c_i64, _c_i64,
+                                                   _c_i64, _vp]),
     "fgb_check_expert_offsets": (ctypes.c_int, [_vp, ctypes.c_int32, _c_i64, _vp, _vp]),
     "fgb_act_quant_per_token": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, ctypes.c_int, _vp, _c_i64, _vp, _vp]),
     "fgb_weight_quant_per_channel": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.c_int, _vp, _vp, _vp]),

@@ -287,6 +287,28 @@ int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
   if (st != FGB_OK) return st;
   fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, total_M, N, K,
                   expert_offsets, E};
+  // at most 64 rows in all (decode-shaped routing): the weight-streaming kernel per expert
+  if (total_M <= 64) return launch_status(fgb::launch_gemm_moe_decode(a, 1, total_M, (hipStream_t)stream));
+  return launch_status(fgb::launch_gemm_grouped(a, (hipStream_t)stream));
+}
+
+int fgb_batched_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                                const uint8_t* w_q, const void* s_w, int s_w_fmt, const int32_t* counts,
+                                int32_t E, int64_t max_M, void* y, int y_dtype, int64_t ldy, int64_t N, int64_t K,
+                                void* stream) {
+  if (E <= 0 || E > 65536 || max_M < 0 || max_M >= kMaxDim) return FGB_ERR_SHAPE;
+  const int64_t rows = (int64_t)E * max_M;
+  if (rows >= kMaxDim) return FGB_ERR_SHAPE;
+  int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, rows, N, K);
+  if (st != FGB_OK || rows == 0) return st;
+  if (!counts) return FGB_ERR_NULL;
+  if (((uintptr_t)counts & 3u)) return FGB_ERR_ALIGN;
+  // tile-count bound of the prefill form: E * ceil(max_M / 128) tile-rows
+  if ((int64_t)E * ((max_M + 127) / 128) * (N / 128) >= kMaxDim) return FGB_ERR_SHAPE;
+  st = check_device();
+  if (st != FGB_OK) return st;
+  fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, rows, N, K, counts, E, 0, max_M};
+  if (max_M <= 64) return launch_status(fgb::launch_gemm_moe_decode(a, 2, max_M, (hipStream_t)stream));
   return launch_status(fgb::launch_gemm_grouped(a, (hipStream_t)stream));
 }
 

@@ -155,6 +155,41 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
 }
 
 // ---------------------------------------------------------------------------------------------
+// MoE with at most 64 rows per expert (decode-shaped routing): the per-wave ring kernel with
+// grid.y = expert; 4 waves split K; mode 1 reads the contiguous grouped layout's offsets, mode 2
+// the masked batched layout's counts (slot = rows per expert slot).
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+template <int MR, int D, int MODE>
+void launch_moe_rows(const GemmArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.N / 16), (unsigned)a.E), block(256);
+  if (a.s_w_fmt == 0) {
+    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 0, 0, 0, 0, MODE>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 0, 1, 0, 0, MODE>), grid, block, 0, stream, a);
+  } else {
+    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 1, 0, 0, 0, MODE>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 1, 1, 0, 0, MODE>), grid, block, 0, stream, a);
+  }
+}
+
+template <int MODE>
+void launch_moe_mr(const GemmArgs& a, int64_t rows_per_expert, hipStream_t stream) {
+  if (rows_per_expert <= 8) launch_moe_rows<8, 5, MODE>(a, stream);
+  else if (rows_per_expert <= 16) launch_moe_rows<16, 4, MODE>(a, stream);
+  else if (rows_per_expert <= 32) launch_moe_rows<32, 3, MODE>(a, stream);
+  else launch_moe_rows<64, 2, MODE>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, int64_t rows_per_expert, hipStream_t stream) {
+  if (mode == 1) launch_moe_mr<1>(a, rows_per_expert, stream);
+  else launch_moe_mr<2>(a, rows_per_expert, stream);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 // Library-owned scratch for callers that cannot allocate (the no-allocation GEMM entry point).
 // One array per GPU, in the code object's device memory for as long as the library is loaded.
 // Host code never uses the array's name as an address: hipGetSymbolAddress gives each device's

@@ -81,9 +81,15 @@ __device__ __forceinline__ int swz_g(int row) { return (row & 7) ^ ((row >> 3) &
 // 1 = per-block weight scales, the per-token or per-tensor activation scale in the epilogue; 2 =
 // per-channel weight scales and per-token or per-tensor activation scales, both in the epilogue
 // (the MFMAs accumulate in place).  CODE 1: E5M2 operands (schemes 1 and 2).
-template <int WK, int MR, int D, int SWF, int OUT, int SCH = 0, int CODE = 0>
+//
+// MODE (MoE, grid.y = expert e, 1x128-group scheme): 1 = the expert's rows are offsets[e] ..
+// offsets[e+1]-1 of the contiguous grouped layout; 2 = rows e*slot .. e*slot + counts[e] - 1 of
+// the masked batched layout.  A workgroup of an expert without rows exits at once, so only the
+// routed experts' weights are read.
+template <int WK, int MR, int D, int SWF, int OUT, int SCH = 0, int CODE = 0, int MODE = 0>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
   static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
+  static_assert(MODE == 0 || SCH == 0, "MoE layouts use the 1x128-group scheme");
   constexpr int MT = MR >= 16 ? MR / 16 : 1;  // token tiles per wave
   constexpr int WST = 16 * 128, AST = MR * 128, SST = 64 * 4;
   constexpr int STAGE = WST + AST + SST;
@@ -94,7 +100,22 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
   __shared__ v4f red[WK > 1 ? WK - 1 : 1][MT][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t K = p.K, M = p.M;
+  const int64_t K = p.K;
+  int64_t M = p.M, row_base = 0, ex = 0;  // this workgroup's rows: row_base .. row_base + M - 1
+  if constexpr (MODE != 0) {
+    ex = blockIdx.y;
+    int64_t r0, r1;
+    if constexpr (MODE == 1) {  // (offsets are a precondition; clamped to 0..total rows)
+      r0 = min(max((int64_t)gload<int>(p.offsets + ex), (int64_t)0), p.M);
+      r1 = min(max((int64_t)gload<int>(p.offsets + ex + 1), r0), p.M);
+    } else {
+      r0 = ex * p.slot;
+      r1 = r0 + min(max((int64_t)gload<int>(p.offsets + ex), (int64_t)0), p.slot);
+    }
+    row_base = __builtin_amdgcn_readfirstlane((int)r0);
+    M = __builtin_amdgcn_readfirstlane((int)(r1 - r0));
+    if (M <= 0) return;
+  }
   const int KB = (int)(K / 128);
   const int per = (KB + WK - 1) / WK;
   const int kb0 = min(KB, wave * per);
@@ -113,11 +134,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
 #pragma unroll
   for (int q = 0; q < MR / 8; ++q) {
     const int r = 8 * q + (lane >> 3);
-    const int64_t m = r < M ? r : M - 1;
+    const int64_t m = row_base + (r < M ? r : M - 1);
     aoff[q] = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
   }
-  const uint32_t soff = (uint32_t)((lane < M ? lane : M - 1) * 4);
-  const uint8_t* wbase = p.w_q + n0 * K;
+  const uint32_t soff = (uint32_t)((row_base + (lane < M ? lane : M - 1)) * 4);
+  const uint8_t* wbase = p.w_q + (ex * p.N + n0) * K;
 
   auto issue = [&](int kk) {
     uint8_t* st = wring + (kk % D) * STAGE;
@@ -150,7 +171,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
   // weight-block scales of this wave's slice, lane l holding block kb0 + l + 64 t (K <= 32768)
   float sw0 = 0.0f, sw1 = 0.0f, sw2 = 0.0f, sw3 = 0.0f;
   if constexpr (SCH != 2) {
-    const int64_t b = nb * KB + kb0;
+    const int64_t b = (ex * (p.N / 128) + nb) * KB + kb0;
     sw0 = lane < nk ? load_sw<SWF>(p.s_w, b + lane) : 0.0f;
     sw1 = lane + 64 < nk ? load_sw<SWF>(p.s_w, b + lane + 64) : 0.0f;
     sw2 = lane + 128 < nk ? load_sw<SWF>(p.s_w, b + lane + 128) : 0.0f;
@@ -273,7 +294,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
         acc[j] = acc[j] * gload<float>(p.s_a + (p.a_kind == 2 ? 0 : m));
         if constexpr (SCH == 2) acc[j] = acc[j] * gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n0 + 4 * (lane >> 4));
       }
-      store4<OUT>(p.y, p.ldy, m, n0 + 4 * (lane >> 4), acc[j]);
+      store4<OUT>(p.y, p.ldy, row_base + m, n0 + 4 * (lane >> 4), acc[j]);
     }
   }
 }

@@ -137,9 +137,15 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   auto expert_chunk = [&](int e0, int& off, int& nxt, int& mt, int& inc) {
     const int idx = e0 + lane0;
     // offsets are a precondition; clamped to 0..M, and an expert whose end lies before its start
-    // gets no tiles, so that bad offsets cannot move a tile's rows outside 0..M-1
-    off = idx <= p.E ? min(max(gload<int>(p.offsets + idx), 0), (int)p.M) : 0;
-    nxt = __shfl_down(off, 1);
+    // gets no tiles, so that bad offsets cannot move a tile's rows outside 0..M-1.  Batched
+    // layout: the slot's first row and its count (clamped to the slot)
+    if (p.slot > 0) {
+      off = idx < p.E ? idx * (int)p.slot : 0;
+      nxt = idx < p.E ? off + min(max(gload<int>(p.offsets + idx), 0), (int)p.slot) : 0;
+    } else {
+      off = idx <= p.E ? min(max(gload<int>(p.offsets + idx), 0), (int)p.M) : 0;
+      nxt = __shfl_down(off, 1);
+    }
     mt = lane0 < 63 && idx < p.E && nxt > off ? (nxt - off + C::BM - 1) / C::BM : 0;
     inc = mt;
 #pragma unroll
@@ -539,13 +545,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
   // Grouped (at most 63 experts): lane l holds offsets[l] and the inclusive prefix sum over
   // experts 0..l of their tile-row counts; tiles are numbered expert by expert, and tiles_m (an
   // upper bound) is replaced by the real count.
-  int c_off = 0, c_inc = 0;
+  int c_off = 0, c_end = 0, c_inc = 0;
   int real_tiles_m = tiles_m;
   if constexpr (GROUPED) {
     // clamped to 0..M, and no tiles for an expert whose end lies before its start (bad offsets
     // then cannot move a tile's rows outside 0..M-1)
-    c_off = lane <= p.E ? min(max(gload<int>(p.offsets + lane), 0), (int)M) : 0;
-    const int nxt = __shfl_down(c_off, 1);
+    if (p.slot > 0) {  // batched layout: the slot's first row and its count (clamped to the slot)
+      c_off = lane < p.E ? lane * (int)p.slot : 0;
+      c_end = lane < p.E ? c_off + min(max(gload<int>(p.offsets + lane), 0), (int)p.slot) : 0;
+    } else {
+      c_off = lane <= p.E ? min(max(gload<int>(p.offsets + lane), 0), (int)M) : 0;
+      c_end = __shfl_down(c_off, 1);
+    }
+    const int nxt = c_end;
     c_inc = lane < p.E && nxt > c_off ? (nxt - c_off + C::BM - 1) / C::BM : 0;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -589,7 +601,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
       const int before = first > 0 ? __builtin_amdgcn_readlane(c_inc, first - 1) : 0;
       t.e = first;
       t.row0 = (int64_t)__builtin_amdgcn_readlane(c_off, first) + (int64_t)(pid_m - before) * C::BM;
-      t.row_end = __builtin_amdgcn_readlane(c_off, first + 1);
+      t.row_end = __builtin_amdgcn_readlane(c_end, first);
     } else {
       t.e = 0;
       t.row0 = (int64_t)pid_m * C::BM;

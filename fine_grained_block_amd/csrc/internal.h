@@ -40,6 +40,9 @@ struct GemmArgs {
   // other scaling schemes: the activation scale is per token (s_a[m], 1) or one for the tensor
   // (s_a[0], 2); 0 = per 1x128 group (s_a K-block-major)
   int a_kind;
+  // masked batched MoE layout (grouped only): expert e owns rows e*slot .. e*slot + counts[e] - 1,
+  // counts[e] read from `offsets` (then E entries); 0 = contiguous rows from offsets [E+1]
+  int64_t slot;
 };
 
 // Prefill (M > 64) dense GEMM and the grouped variant.
@@ -52,6 +55,10 @@ hipError_t launch_check_offsets(const int32_t* offsets, int32_t E, int64_t total
 // blocks; sch 2: per-channel weight scales), E4M3 (code 0) or E5M2 (code 1) operands.
 hipError_t launch_gemm_scaled_prefill(const GemmArgs& a, int sch, int code, hipStream_t stream);
 hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int code, hipStream_t stream);
+
+// MoE with at most 64 rows per expert: mode 1 grouped (offsets [E+1]), mode 2 batched (counts [E],
+// slot rows per expert); rows_per_expert bounds every expert's row count.
+hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, int64_t rows_per_expert, hipStream_t stream);
 
 // Decode GEMM that quantizes its bf16 activations itself (M <= 64).
 hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream);

@@ -340,6 +340,28 @@ def grouped_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: t
     return out
 
 
+def batched_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor,
+                 counts: torch.Tensor, max_m: int, out_dtype=torch.bfloat16,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """MoE GEMM on the masked batched layout: expert e owns rows e*max_m .. e*max_m + counts[e]-1
+    of a_q [E*max_m, K] (and of s_a, out); the rest of each slot is padding, left unwritten.
+
+    counts: contiguous int32 device tensor [E] with 0 <= counts[e] <= max_m."""
+    _need(isinstance(w_q, torch.Tensor) and w_q.dim() == 3, "w_q must be [E, N, K]")
+    E = w_q.shape[0]
+    rows, N, K = _check_gemm_operands(a_q, s_a, w_q, s_w, out, E)
+    _need(int(max_m) >= 0 and rows == E * int(max_m), f"a_q must have E * max_m = {E * int(max_m)} rows")
+    _dense(counts, "counts", (torch.int32,), (E,))
+    _on_device(("a_q", a_q), ("s_a", s_a), ("w_q", w_q), ("s_w", s_w), ("counts", counts), ("out", out))
+    if out is None:
+        out = torch.empty((rows, N), dtype=out_dtype, device=a_q.device)
+    st = lib().fgb_batched_w8a8_block_gemm(_ptr(a_q), _row_ld(a_q), _ptr(s_a), s_a.stride(0), _ptr(w_q),
+                                           _ptr(s_w), _scale_fmt(s_w), _ptr(counts), E, int(max_m), _ptr(out),
+                                           _out_code(out.dtype), _row_ld(out), N, K, _stream())
+    check("fgb_batched_w8a8_block_gemm", st)
+    return out
+
+
 def check_offsets(offsets: torch.Tensor, total_M: int) -> int:
     """Check the grouped GEMM's expert offsets on the device (synchronizes): 0 when they start at
     0, never decrease and end at total_M, else 1 + the first index that breaks that."""

@@ -183,6 +183,25 @@ int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Masked batched MoE layout (Transformers "Fine-grained FP8", "UE8M0 scale format": the
+ * batched_mm experts backend): every expert e has a slot of max_M rows, rows e*max_M ..
+ * e*max_M + counts[e] - 1 of a_q / s_a / y, and only its first counts[e] rows are computed and
+ * written (the rest of the slot is padding: never read into a stored result, never written).
+ *   a_q [E*max_M, lda]; s_a [K/128, ld_sa], ld_sa >= E*max_M (one fgb_act_quant_group128 over all
+ *   E*max_M rows gives both); w_q [E, N, K]; s_w [E, N/128, K/128] float32 or UE8M0;
+ *   counts DEVICE int32 [E], 0 <= counts[e] <= max_M (a precondition; values are clamped to it);
+ *   y [E*max_M, ldy].
+ * max_M <= 64 runs the weight-streaming decode kernel per expert (the workgroups of an expert
+ * with no rows exit at once, so only routed experts' weights are read); larger slots run the
+ * grouped prefill kernel.  No workspace.  Size limits as for fgb_grouped_w8a8_block_gemm.
+ * (fgb_grouped_w8a8_block_gemm also takes the weight-streaming path when total_M <= 64.)
+ */
+int fgb_batched_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
+                                const uint8_t* w_q, const void* s_w, int s_w_fmt,
+                                const int32_t* counts, int32_t E, int64_t max_M,
+                                void* y, int y_dtype, int64_t ldy, int64_t N, int64_t K, void* stream);
+
+/*
  * Debugging aid for the grouped GEMM's precondition (the expert layout of Transformers
  * "Fine-grained FP8": rows sorted by expert, expert e owning rows offsets[e] .. offsets[e+1]-1).
  * Writes to `result` (DEVICE int32, 4-byte aligned; read it after synchronizing the stream) 0

@@ -112,6 +112,22 @@ int main() {
   EXPECT(grouped(4, 256, F, 100), FGB_ERR_SHAPE);
   EXPECT(grouped(4, 256, F), FGB_OK);
   if (strcmp(g_stub.last, "gemm_grouped") || g_stub.E != 4 || g_stub.M != 256) failures++;
+  EXPECT(grouped(4, 64, F), FGB_OK);  // at most 64 rows in all: the per-expert decode kernel
+  if (strcmp(g_stub.last, "moe_decode") || g_stub.K != 1) failures++;
+  auto batched = [](int32_t E, int64_t max_m, uintptr_t cnt, int64_t ld_sa = 4096) {
+    return fgb_batched_w8a8_block_gemm((const uint8_t*)P(F), 1024, (const float*)P(F), ld_sa, (const uint8_t*)P(F),
+                                       P(F), 0, (const int32_t*)P(cnt), E, max_m, P(F), 0, 512, 512, 1024, nullptr);
+  };
+  EXPECT(batched(0, 64, F), FGB_ERR_SHAPE);
+  EXPECT(batched(8, -1, F), FGB_ERR_SHAPE);
+  EXPECT(batched(8, 64, 0), FGB_ERR_NULL);
+  EXPECT(batched(8, 64, F + 2), FGB_ERR_ALIGN);
+  EXPECT(batched(8, 64, F, 500), FGB_ERR_STRIDE);  // ld_sa below E * max_M
+  EXPECT(batched(8, 0, F), FGB_OK);
+  EXPECT(batched(8, 64, F), FGB_OK);
+  if (strcmp(g_stub.last, "moe_decode") || g_stub.K != 2 || g_stub.M != 512) failures++;
+  EXPECT(batched(8, 256, F), FGB_OK);
+  if (strcmp(g_stub.last, "gemm_grouped") || g_stub.M != 2048) failures++;
   EXPECT(fgb_grouped_gemm_workspace_bytes(256, 512, 1024, 4), 0);
 
   // quantizers and codecs

@@ -1,0 +1,115 @@
+"""GPU parity for the MoE layouts beyond the contiguous prefill case, through the C-ABI:
+the masked batched layout [E, max_M] with per-expert counts (fgb_batched_w8a8_block_gemm: the
+per-expert weight-streaming kernel for max_M <= 64, the grouped prefill kernel above), and the
+grouped layout with at most 64 rows in all (decode-shaped routing: the per-expert streaming
+kernel).  Against oracle.gemm.batched_ref / grouped_ref; padding rows of a slot must stay
+untouched.  Tolerances as for the dense GEMM."""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_amd as fgb
+import workloads
+from oracle import blockquant, gemm
+from tests.gemm_helpers import bf16_tensor_to_f64, check_t1, check_t2, sa_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _experts(E, N, K, fmt, key):
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    rng = np.random.default_rng(key)
+    wq = rng.choice(finite, size=(E, N, K))
+    if fmt == "f32":
+        sw = (rng.uniform(0.25, 4.0, size=(E, N // 128, K // 128)) / 448).astype(np.float32)
+    else:
+        sw = rng.integers(112, 124, size=(E, N // 128, K // 128), dtype=np.uint8)
+    return wq, sw
+
+
+@pytest.mark.parametrize("max_m", [1, 5, 16, 40, 64, 100, 300])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_batched_masked_layout(dev, max_m, fmt):
+    E, N, K = 8, 256, 1024
+    rng = np.random.default_rng(max_m)
+    counts = rng.integers(0, max_m + 1, size=E)
+    counts[0], counts[3] = 0, max_m                     # an empty and a full slot
+    x = workloads.activations(E * max_m, K, key=(3, 70, max_m, 0))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, fmt, 100 + max_m)
+    yref, valid = gemm.batched_ref(aq, sa, wq, sw, counts, max_m, fmt)
+    args = (torch.from_numpy(aq).to(dev), sa_device(sa, dev), torch.from_numpy(wq).to(dev),
+            torch.from_numpy(sw).to(dev), torch.from_numpy(counts.astype(np.int32)).to(dev), max_m)
+    for dt in (torch.float32, torch.bfloat16):
+        out = torch.full((E * max_m, N), -7.0, dtype=dt, device=dev)
+        fgb.batched_gemm(*args, out=out)
+        torch.cuda.synchronize()
+        o = out.float().cpu().numpy().astype(np.float64)
+        assert np.all(o[~valid] == -7.0), "padding rows were written"
+        if valid.any():
+            if dt == torch.float32:
+                check_t1(o[valid], yref[valid])
+            else:
+                check_t2(o[valid], yref[valid])
+
+
+def test_batched_equals_grouped_on_the_same_rows(dev):
+    """The batched layout and the contiguous grouped layout agree on every valid row."""
+    E, N, K, max_m = 6, 512, 2048, 48
+    counts = np.array([48, 0, 3, 17, 1, 30])
+    x = workloads.activations(E * max_m, K, key=(3, 71, 0, 0))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, "f32", 7)
+    wqd, swd = torch.from_numpy(wq).to(dev), torch.from_numpy(sw).to(dev)
+    yb = fgb.batched_gemm(torch.from_numpy(aq).to(dev), sa_device(sa, dev), wqd, swd,
+                          torch.from_numpy(counts.astype(np.int32)).to(dev), max_m, out_dtype=torch.float32)
+    rows = np.concatenate([np.arange(e * max_m, e * max_m + counts[e]) for e in range(E)])
+    offsets = workloads.offsets_from_counts(counts)
+    yg = fgb.grouped_gemm(torch.from_numpy(aq[rows]).to(dev), sa_device(sa[rows], dev), wqd, swd,
+                          torch.from_numpy(offsets).to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # (grouped with more than 64 rows runs the prefill kernel: a different summation order)
+    check_t1(yb.cpu().numpy()[rows], yg.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("tokens", [1, 3, 8])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_grouped_decode_shaped_routing(dev, tokens, fmt):
+    """Top-8 routing of a few tokens over 32 experts (Zipf 1.1): at most 64 rows in all, so the
+    grouped GEMM streams each routed expert's weights; unrouted experts read nothing."""
+    E, N, K = 32, 256, 2048
+    _, offsets, counts = workloads.moe_routing(tokens=tokens, E=E, topk=8, key=(3, 72, tokens, 0))
+    T = int(offsets[-1])
+    assert T == 8 * tokens <= 64
+    x = workloads.activations(T, K, key=(3, 73, tokens, 0))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, fmt, 200 + tokens)
+    yref = gemm.grouped_ref(aq, sa, wq, sw, offsets, fmt)
+    args = (torch.from_numpy(aq).to(dev), sa_device(sa, dev), torch.from_numpy(wq).to(dev),
+            torch.from_numpy(sw).to(dev), torch.from_numpy(offsets).to(dev))
+    y32 = fgb.grouped_gemm(*args, out_dtype=torch.float32)
+    y16 = fgb.grouped_gemm(*args, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check_t1(y32.cpu().numpy(), yref)
+    check_t2(bf16_tensor_to_f64(y16), yref)
+
+
+def test_grouped_decode_all_rows_in_one_expert(dev):
+    E, N, K, T = 16, 512, 1024, 64
+    counts = np.zeros(E, dtype=np.int64)
+    counts[5] = T
+    offsets = workloads.offsets_from_counts(counts)
+    x = workloads.activations(T, K, key=(3, 74, 0, 0))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, "f32", 9)
+    yref = gemm.grouped_ref(aq, sa, wq, sw, offsets)
+    y = fgb.grouped_gemm(torch.from_numpy(aq).to(dev), sa_device(sa, dev), torch.from_numpy(wq).to(dev),
+                         torch.from_numpy(sw).to(dev), torch.from_numpy(offsets).to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_t1(y.cpu().numpy(), yref)
+    # one expert holding every row equals the dense GEMM on that expert's weights
+    yd = fgb.gemm(torch.from_numpy(aq).to(dev), sa_device(sa, dev), torch.from_numpy(wq[5]).to(dev),
+                  torch.from_numpy(sw[5]).to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yd)
