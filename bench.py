@@ -263,7 +263,7 @@ def extra_suites(torch, fgb, workloads, np):
         flush_buf.sum()
 
     # decode — hipGraph loop over rotating weight copies (> 2x MALL in total)
-    dec = {}
+    dec, fused = {}, {}
     for (name, N, K) in workloads.DECODE_SHAPES:
         w = workloads.device_bf16((N, K), next_seed(), dev, outliers=False, std=0.02)
         wq0, sw = fgb.quantize_weight(w)
@@ -279,8 +279,62 @@ def extra_suites(torch, fgb, workloads, np):
             byts = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * K / 128 + 2 * M * N
             dec[f"{name}_{N}x{K}_M{M}"] = dict(us=round(us, 2), gbs=round(byts / us / 1e3, 1),
                                                 frac_hbm=round(byts / us / 1e3 / PEAK_HBM_GBS, 3))
+            # the same linear from bf16 activations: act_quant + GEMM (two launches) against the
+            # GEMM that quantizes the activations itself (one launch)
+            two = _graph_time(torch, lambda i: (fgb.quantize(x, out=(q, sa)),
+                                                fgb.gemm(q, sa, wqs[i % copies], sw, out=y, workspace=ws)), 4 * copies)
+            one = _graph_time(torch, lambda i: fgb.gemm_fused_quant(x, wqs[i % copies], sw, out=y), 4 * copies)
+            fbytes = N * K + 4 * (N // 128) * (K // 128) + 2 * M * K + 2 * M * N
+            fused[f"{name}_{N}x{K}_M{M}"] = dict(quant_plus_gemm_us=round(two, 2), fused_us=round(one, 2),
+                                                 fused_frac_hbm=round(fbytes / one / 1e3 / PEAK_HBM_GBS, 3))
         del wqs, wq0
     out["decode"] = dec
+    out["decode_fused_quant"] = fused
+
+    # the other schemes at the Llama-3-8B prefill shapes (M = 4096), back to back: FP8_DYNAMIC
+    # (per-token activations, per-channel weights, E4M3) and static per-tensor activations with
+    # 128x128 weight blocks in E5M2; quantization and GEMM timed per call with HIP events
+    for scheme in ("fp8_dynamic_e4m3", "static_tensor_e5m2"):
+        M = workloads.LLAMA3_8B_PREFILL_M
+        calls = []
+        for (name, N, K) in workloads.LLAMA3_8B_LINEARS:
+            w = workloads.device_bf16((N, K), next_seed(), dev, outliers=False, std=0.02)
+            x = workloads.device_bf16((M, K), next_seed(), dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            if scheme == "fp8_dynamic_e4m3":
+                wq, sw = fgb.quantize_weight_per_channel(w)
+                q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+                sa = torch.empty((M,), dtype=torch.float32, device=dev)
+                quant = (lambda x=x, q=q, sa=sa: fgb.quantize_per_token(x, out=(q, sa)))
+                mm = (lambda q=q, sa=sa, wq=wq, sw=sw, y=y: fgb.scaled_gemm(q, sa, wq, sw, act_scale="token", out=y))
+            else:
+                wq, sw = fgb.quantize_weight(w, "float", code="e5m2")
+                q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+                sa = torch.tensor([float(x.float().abs().max()) / 57344.0], dtype=torch.float32, device=dev)
+                quant = (lambda x=x, q=q, sa=sa: fgb.quantize_static(x, sa, "e5m2", out=q))
+                mm = (lambda q=q, sa=sa, wq=wq, sw=sw, y=y: fgb.scaled_gemm(q, sa, wq, sw, act_scale="tensor",
+                                                                           code="e5m2", out=y))
+            del w
+            calls.append((name, N, K, quant, mm, (x, q, sa, wq, sw, y)))
+        res = {}
+        ev = {n: ([], []) for n, *_ in calls}
+        for rep in range(8):
+            for (name, N, K, quant, mm, _) in calls:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(); quant(); e[1].record(); mm(); e[2].record()
+                if rep >= 3:
+                    ev[name][0].append(e)
+        torch.cuda.synchronize()
+        for (name, N, K, *_r) in calls:
+            qs = sorted(e[0].elapsed_time(e[1]) for e in ev[name][0])
+            gs = sorted(e[1].elapsed_time(e[2]) for e in ev[name][0])
+            g_us, q_us = gs[len(gs) // 2] * 1e3, qs[len(qs) // 2] * 1e3
+            f = 2.0 * M * N * K
+            res[f"{name}_{N}x{K}"] = dict(gemm_us=round(g_us, 1), tflops=round(f / g_us / 1e6, 1),
+                                          frac_mfma=round(f / g_us / 1e6 / PEAK_FP8_TFLOPS, 3), quant_us=round(q_us, 1),
+                                          quant_gbs=round(3.0 * M * K / q_us / 1e3, 1))
+        out[f"{scheme}_m4096"] = res
+        del calls
 
     # DeepSeek-V3-shaped prefill with UE8M0 weight scales (M = 8192), each call alone with cold
     # caches (the headline step runs the same calls back to back)
@@ -319,6 +373,43 @@ def extra_suites(torch, fgb, workloads, np):
         del wq, x, q, y
     moe["expert_rows_max_min"] = [int(counts.max()), int(counts.min())]
     out["moe_grouped_e32"] = moe
+
+    # decode-shaped MoE (32 experts, top-8 Zipf routing of a few tokens): the grouped layout with
+    # 8 or 64 rows in all, and the masked batched layout with 64-row slots for 64 tokens; hipGraph
+    # loop alternating two copies of the expert weights (> 2x the MALL); bytes = the routed
+    # experts' weights and scales + activations, scales and outputs of the routed rows
+    mdec = {}
+    for nm, (N, K) in [("gate_up", workloads.MOE["gate_up"]), ("down", workloads.MOE["down"])]:
+        w = workloads.device_bf16((32 * N, K), next_seed(), dev, outliers=False, std=0.02)
+        wq, sw = fgb.quantize_weight(w)
+        del w
+        wqs = [wq.view(32, N, K), wq.clone().view(32, N, K)]
+        sw = sw.view(32, N // 128, K // 128)
+        for tokens in (1, 8, 64):
+            _, offs, cnts = workloads.moe_routing(tokens=tokens, key=(0, 9, tokens, 1))
+            routed = int((cnts > 0).sum())
+            T = int(offs[-1])
+            if tokens <= 8:
+                x = workloads.device_bf16((T, K), next_seed(), dev)
+                q, sa = fgb.quantize(x)
+                y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+                off_t = torch.from_numpy(offs).to(dev)
+                us = _graph_time(torch, lambda i: fgb.grouped_gemm(q, sa, wqs[i % 2], sw, off_t, out=y), 8)
+                key = f"grouped_{nm}_{N}x{K}_T{tokens}_rows{T}"
+            else:
+                slot = 64
+                x = workloads.device_bf16((32 * slot, K), next_seed(), dev)
+                q, sa = fgb.quantize(x)
+                y = torch.empty((32 * slot, N), dtype=torch.bfloat16, device=dev)
+                cnt_t = torch.from_numpy(np.minimum(cnts, slot).astype(np.int32)).to(dev)
+                T = int(np.minimum(cnts, slot).sum())
+                us = _graph_time(torch, lambda i: fgb.batched_gemm(q, sa, wqs[i % 2], sw, cnt_t, slot, out=y), 8)
+                key = f"batched_{nm}_{N}x{K}_T{tokens}_slot{slot}_rows{T}"
+            byts = routed * (N * K + 4 * (N // 128) * (K // 128)) + T * (K + 4 * K / 128 + 2 * N)
+            mdec[key] = dict(us=round(us, 2), routed_experts=routed, gbs=round(byts / us / 1e3, 1),
+                             frac_hbm=round(byts / us / 1e3 / PEAK_HBM_GBS, 3))
+        del wqs, wq
+    out["moe_decode_e32"] = mdec
 
     # activation quantization bandwidth at the prefill shapes: hipGraph loop over rotating
     # input/output copies whose total exceeds 2x the MALL, so every call streams from HBM

@@ -469,6 +469,206 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_fused_quant_kernel(GemmAr
 }
 
 // ---------------------------------------------------------------------------------------------
+// The fused kernel for M <= 8: only the MQ (>= M, a power of two up to 8) real activation rows are
+// quantized, spread over all 64 lanes (2*MQ elements per lane, 64/MQ lanes per row), so each
+// wave's quantization work per K-block is MQ/16 of the kernel above.  The codes and the row
+// scales go to a per-wave LDS tile in the MFMA operand layout (16 rows of 128 bytes, rows >= MQ
+// never written: they feed only output columns of tokens >= M, which are not stored), from which
+// the B operand is read as for the ring kernel.  Same arithmetic, K split and order as above.
+template <int WK, int MQ, int D, int SWF, int OUT>
+__global__ __launch_bounds__(64 * WK) void gemm_decode_fused_quant_small_kernel(GemmArgs p,
+                                                                                const uint16_t* __restrict__ x,
+                                                                                int64_t ldx) {
+  static_assert(MQ == 1 || MQ == 2 || MQ == 4 || MQ == 8, "1, 2, 4 or 8 quantized rows");
+  constexpr int MRC = MQ < 4 ? 4 : MQ;            // staged bf16 rows (copies move 4 rows at a time)
+  constexpr int WST = 16 * 128, AST = MRC * 256;
+  constexpr int STAGE = WST + AST;
+  constexpr int OPS = 2 + MRC / 4;
+  constexpr int E = 2 * MQ;                        // elements per lane
+  constexpr int LPR = 64 / MQ;                     // lanes per row
+  static_assert((D - 1) * OPS <= 63, "copies in flight fit the vmcnt counter");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[WK * D * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ctile[WK][16 * 128];  // codes, MFMA B layout
+  __shared__ float stile[WK][16];                                         // row scales
+  __shared__ v4f red[WK > 1 ? WK - 1 : 1][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t K = p.K, M = p.M;
+  const int KB = (int)(K / 128);
+  const int per = (KB + WK - 1) / WK;
+  const int kb0 = min(KB, wave * per);
+  const int nk = min(KB, kb0 + per) - kb0;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t nb = n0 / 128;
+  uint8_t* const wring = ring + wave * D * STAGE;
+
+  uint32_t woff[2], aoff[MRC / 4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 8 * q + (lane >> 3);
+    woff[q] = (uint32_t)(r * K + (((lane & 7) ^ swz_g(r)) * 16));
+  }
+#pragma unroll
+  for (int q = 0; q < MRC / 4; ++q) {
+    const int r = 4 * q + (lane >> 4);
+    const int64_t m = r < M ? r : M - 1;
+    aoff[q] = (uint32_t)(m * ldx * 2 + (((lane & 15) ^ (r & 15)) * 16));
+  }
+  const uint8_t* wbase = p.w_q + n0 * K;
+
+  auto issue = [&](int kk) {
+    uint8_t* st = wring + (kk % D) * STAGE;
+    const int64_t kb = kb0 + kk;
+    const uint8_t* wb = wbase + kb * 128;
+    const uint8_t* ab = reinterpret_cast<const uint8_t*>(x) + kb * 256;
+    asm volatile("" : "+s"(wb));
+    asm volatile("" : "+s"(ab));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t o = woff[q];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(GPTR(wb + o), LPTR(st + q * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < MRC / 4; ++q) {
+      uint32_t o = aoff[q];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(GPTR(ab + o), LPTR(st + WST + q * 1024), 16, 0, 0);
+    }
+  };
+
+  float sw0 = 0.0f, sw1 = 0.0f, sw2 = 0.0f, sw3 = 0.0f;
+  {
+    const int64_t b = nb * KB + kb0;
+    sw0 = lane < nk ? load_sw<SWF>(p.s_w, b + lane) : 0.0f;
+    sw1 = lane + 64 < nk ? load_sw<SWF>(p.s_w, b + lane + 64) : 0.0f;
+    sw2 = lane + 128 < nk ? load_sw<SWF>(p.s_w, b + lane + 128) : 0.0f;
+    sw3 = lane + 192 < nk ? load_sw<SWF>(p.s_w, b + lane + 192) : 0.0f;
+  }
+  auto sw_at = [&](int kk) -> float {
+    const int l = kk & 63, t = kk >> 6;
+    const int r0 = __builtin_amdgcn_readlane(__float_as_int(sw0), l);
+    const int r1 = __builtin_amdgcn_readlane(__float_as_int(sw1), l);
+    const int r2 = __builtin_amdgcn_readlane(__float_as_int(sw2), l);
+    const int r3 = __builtin_amdgcn_readlane(__float_as_int(sw3), l);
+    const int lo = (t & 1) ? r1 : r0, hi = (t & 1) ? r3 : r2;
+    return __int_as_float((t & 2) ? hi : lo);
+  };
+
+  // this lane's share of the quantization: row rq, elements eo .. eo + E - 1 of the group
+  const int rq = lane / LPR, eo = (lane % LPR) * E;
+  const uint32_t xsrc = (uint32_t)(WST + rq * 256 + ((((eo * 2) >> 4) ^ (rq & 15)) << 4) + ((eo * 2) & 15));
+  const uint32_t cdst = (uint32_t)(uintptr_t)LPTR(&ctile[wave][0]) + rq * 128 + ((((eo >> 4)) ^ swz_g(rq)) << 4) + (eo & 15);
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t cb0 = (uint32_t)(uintptr_t)LPTR(&ctile[wave][0]) + swz(r, 2 * g);
+  const uint32_t cb1 = (uint32_t)(uintptr_t)LPTR(&ctile[wave][0]) + swz(r, 2 * g + 1);
+  const uint32_t sdst = (uint32_t)(uintptr_t)LPTR(&stile[wave][rq]);
+  const uint32_t ssrc = (uint32_t)(uintptr_t)LPTR(&stile[wave][r]);
+
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) issue(min(i, nk - 1));
+    for (int kk = 0; kk < nk; ++kk) {
+      issue(min(kk + D - 1, nk - 1));
+      __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * OPS>());
+      const uint32_t st = (uint32_t)(uintptr_t)LPTR(wring + (kk % D) * STAGE);
+      // this lane's E bf16 values (one LDS read; E = 16 is two 16-byte chunks)
+      uint32_t xv[E / 2];
+      if constexpr (E == 2) {
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(xv[0]) : "v"(st + xsrc) : "memory");
+      } else if constexpr (E == 4) {
+        v2u t;
+        asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(t) : "v"(st + xsrc) : "memory");
+        xv[0] = t[0]; xv[1] = t[1];
+      } else if constexpr (E == 8) {
+        v4i t;
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(t) : "v"(st + xsrc) : "memory");
+        xv[0] = t[0]; xv[1] = t[1]; xv[2] = t[2]; xv[3] = t[3];
+      } else {
+        // 16 elements = logical chunks 2c and 2c+1 of the row, each at its own swizzled slot
+        const int c = eo >> 3;
+        const uint32_t a0 = st + WST + rq * 256 + (((c) ^ (rq & 15)) << 4);
+        const uint32_t a1 = st + WST + rq * 256 + (((c + 1) ^ (rq & 15)) << 4);
+        v4i t0, t1;
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(t0), "=&v"(t1) : "v"(a0), "v"(a1) : "memory");
+        xv[0] = t0[0]; xv[1] = t0[1]; xv[2] = t0[2]; xv[3] = t0[3];
+        xv[4] = t1[0]; xv[5] = t1[1]; xv[6] = t1[2]; xv[7] = t1[3];
+      }
+      float f[E];
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) {
+        f[2 * i] = bf16_lo(xv[i]);
+        f[2 * i + 1] = bf16_hi(xv[i]);
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) am = fmaxf(am, fabsf(f[i]));
+#pragma unroll
+      for (int d = 1; d < LPR; d <<= 1) am = fmaxf(am, __shfl_xor(am, d));
+      const float sa = am / kE4M3Max;  // IEEE float32 division, as act_quant
+      const Divisor dv = make_divisor(sa);
+      if (__all(dv.fast)) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) f[i] = quot_fast(f[i], dv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) f[i] = quot(f[i], dv);
+      }
+      uint32_t cw[E / 4 > 0 ? E / 4 : 1];
+      if constexpr (E == 2) {
+        cw[0] = cvt_pk_e4m3<false>(f[0], f[1], 0u) & 0xFFFFu;
+        asm volatile("ds_write_b16 %0, %1" ::"v"(cdst), "v"(cw[0]) : "memory");
+      } else {
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i) cw[i] = cvt_pk_e4m3<true>(f[4 * i + 2], f[4 * i + 3], cvt_pk_e4m3<false>(f[4 * i], f[4 * i + 1], 0u));
+        if constexpr (E == 4) {
+          asm volatile("ds_write_b32 %0, %1" ::"v"(cdst), "v"(cw[0]) : "memory");
+        } else if constexpr (E == 8) {
+          v2u t = {cw[0], cw[1]};
+          asm volatile("ds_write_b64 %0, %1" ::"v"(cdst), "v"(t) : "memory");
+        } else {
+          v4i t = {(int)cw[0], (int)cw[1], (int)cw[2], (int)cw[3]};
+          asm volatile("ds_write_b128 %0, %1" ::"v"(cdst), "v"(t) : "memory");
+        }
+      }
+      if (lane % LPR == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(sdst), "v"(sa) : "memory");
+      // the wave's own writes are done before it reads the tile back (LDS serves a wave in order)
+      v4i w0, w1, b0, b1;
+      float sar;
+      const uint32_t aw0 = st + swz(r, 2 * g), aw1 = st + swz(r, 2 * g + 1);
+      asm volatile(
+          "s_waitcnt lgkmcnt(0)\n\t"
+          "ds_read_b128 %0, %5\n\t"
+          "ds_read_b128 %1, %6\n\t"
+          "ds_read_b128 %2, %7\n\t"
+          "ds_read_b128 %3, %8\n\t"
+          "ds_read_b32 %4, %9\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(w0), "=&v"(w1), "=&v"(b0), "=&v"(b1), "=&v"(sar)
+          : "v"(aw0), "v"(aw1), "v"(cb0), "v"(cb1), "v"(ssrc)
+          : "memory");
+      v8i wf, af;
+      wf[0] = w0[0]; wf[1] = w0[1]; wf[2] = w0[2]; wf[3] = w0[3];
+      wf[4] = w1[0]; wf[5] = w1[1]; wf[6] = w1[2]; wf[7] = w1[3];
+      af[0] = b0[0]; af[1] = b0[1]; af[2] = b0[2]; af[3] = b0[3];
+      af[4] = b1[0]; af[5] = b1[1]; af[6] = b1[2]; af[7] = b1[3];
+      acc += mfma_e4m3_16x16x128(wf, af) * (sar * sw_at(kk));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+  if constexpr (WK > 1) {
+    if (wave > 0) red[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
+  }
+  if ((lane & 15) < M) store4<OUT>(p.y, p.ldy, lane & 15, n0 + 4 * (lane >> 4), acc);
+}
+
+// ---------------------------------------------------------------------------------------------
 // 16 < M <= 64: a workgroup of 8 waves owns one 128-row weight block (16 rows per wave) over a
 // slice of K-blocks.  The block's weight rows, the 16*MT activation rows (rows >= M repeat row
 // M-1; their results are dropped) and the activation scales of each K-block stream through a

@@ -36,10 +36,10 @@ void launch_fused_wk(int wk, const GemmArgs& a, const uint16_t* x, int64_t ldx, 
 }  // namespace
 
 hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream) {
+  if (a.M <= 8) return launch_gemm_decode_fused_small(a, x, ldx, stream);
   if (a.M <= 16) {
     const int wk = decode_small_waves(a.N, a.K);
-    if (a.M <= 8) launch_fused_wk<8, 4>(wk, a, x, ldx, stream);
-    else launch_fused_wk<16, 3>(wk, a, x, ldx, stream);
+    launch_fused_wk<16, 3>(wk, a, x, ldx, stream);
   } else if (a.M <= 32) {
     launch_fused<4, 32, 3>(a, x, ldx, stream);
   } else {

@@ -62,6 +62,7 @@ hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, int64_t rows_per_
 
 // Decode GEMM that quantizes its bf16 activations itself (M <= 64).
 hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream);
+hipError_t launch_gemm_decode_fused_small(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream);
 // waves per 16-row workgroup that split K in the M <= 16 decode kernels
 int decode_small_waves(int64_t N, int64_t K);
 

@@ -40,7 +40,7 @@ def _same_kernel_shape(M, N, K):
     return M <= 16 or N * K <= (16 << 20)
 
 
-@pytest.mark.parametrize("M", [1, 3, 8, 9, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 16, 17, 32, 33, 64])
 @pytest.mark.parametrize("N,K", [(512, 2048), (1024, 4096), (4096, 4608)])
 @pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
 def test_fused_matches_two_launch_path_and_oracle(dev, M, N, K, fmt):
