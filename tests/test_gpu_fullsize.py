@@ -13,7 +13,7 @@ import torch
 
 import fine_grained_block_amd as fgb
 import workloads
-from oracle import blockquant, gemm
+from oracle import blockquant, gemm, schemes
 from tests.gemm_helpers import bf16_tensor_to_f64, check_t2
 
 pytestmark = pytest.mark.gpu
@@ -23,15 +23,19 @@ def _bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def _pick(rng, M, N, nrows=16, nblocks=2):
-    """Token rows (always the first and the last) and the columns of whole 128-row weight blocks
-    (always the last block)."""
+def _pick(rng, M, N, nrows=64, nblocks=8):
+    """Token rows (always the first and the last, and both sides of the first 256-row tile edge)
+    and the columns of whole 128-row weight blocks (always the first and the last block, and both
+    sides of the first 256-column tile edge)."""
     if M <= nrows:
         rows = np.arange(M)
     else:
-        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, nrows - 2, replace=False)]))
+        fixed = [0, M - 1] + ([255, 256] if M > 256 else [])
+        rows = np.unique(np.concatenate([fixed, rng.choice(M, nrows - len(fixed), replace=False)]))
     nb = N // 128
-    blocks = np.unique(np.concatenate([[nb - 1], rng.choice(nb, nblocks - 1, replace=False)]))
+    fixed = [0, nb - 1] + ([1, 2] if nb > 2 and nblocks >= 4 else [])
+    extra = max(0, min(nblocks, nb) - len(fixed))
+    blocks = np.unique(np.concatenate([fixed, rng.choice(nb, extra, replace=False)]).astype(np.int64))
     cols = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)
     return rows, cols
 
@@ -110,3 +114,101 @@ def test_moe_grouped_full(dev, proj):
         wq_s, sw_s = blockquant.weight_quant(_bits(w[_idx(e * N + cols, dev)]), "f32")
         yref = gemm.gemm_ref(aq, sa_o, wq_s, sw_s, "f32")
         check_t2(bf16_tensor_to_f64(y[_idx(rows, dev)][:, _idx(cols, dev)]), yref)
+
+
+# ------------------------------------------------------------------------------------------
+# the other paths at full size, in the launch configuration bench.py times
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,N,K", [workloads.LLAMA3_8B_LINEARS[2], workloads.LLAMA3_8B_LINEARS[3]],
+                         ids=["gate_up", "down"])
+def test_fp8_dynamic_llama3_8b_m4096(dev, name, N, K):
+    """Per-token activations, per-channel weights (E4M3); each sampled row and weight row is
+    quantized independently of the others, so the oracle quantizes exactly the sample."""
+    M = workloads.LLAMA3_8B_PREFILL_M
+    seed = sum(map(ord, name)) + 600
+    x = workloads.device_bf16((M, K), seed, dev)
+    w = workloads.device_bf16((N, K), seed + 1, dev, outliers=False, std=0.02)
+    q, sa = fgb.quantize_per_token(x)
+    wq, sw = fgb.quantize_weight_per_channel(w)
+    y = fgb.scaled_gemm(q, sa, wq, sw, act_scale="token")
+    torch.cuda.synchronize()
+    rows, cols = _pick(np.random.default_rng(seed), M, N)
+    aq, sa_o = schemes.token_quant(_bits(x[_idx(rows, dev)]))
+    wq_s, sw_s = schemes.channel_weight_quant(_bits(w[_idx(cols, dev)]))
+    yref = schemes.scaled_gemm_ref(aq, sa_o, wq_s, sw_s, act="token", weight="channel")
+    check_t2(bf16_tensor_to_f64(y[_idx(rows, dev)][:, _idx(cols, dev)]), yref)
+
+
+def test_static_e5m2_llama3_8b_gate_up(dev):
+    """Static per-tensor activation scale with E5M2 codes and E5M2 128x128 weight blocks."""
+    M, (name, N, K) = workloads.LLAMA3_8B_PREFILL_M, workloads.LLAMA3_8B_LINEARS[2]
+    x = workloads.device_bf16((M, K), 700, dev)
+    w = workloads.device_bf16((N, K), 701, dev, outliers=False, std=0.02)
+    s = np.float32(float(x.float().abs().max()) / 57344.0)
+    q = fgb.quantize_static(x, torch.tensor([s], device=dev), "e5m2")
+    wq, sw = fgb.quantize_weight(w, "float", code="e5m2")
+    y = fgb.scaled_gemm(q, torch.tensor([s], device=dev), wq, sw, act_scale="tensor", code="e5m2")
+    torch.cuda.synchronize()
+    rows, cols = _pick(np.random.default_rng(700), M, N)
+    aq = schemes.static_quant(_bits(x[_idx(rows, dev)]), s, "e5m2")
+    wq_s, sw_s = blockquant.weight_quant(_bits(w[_idx(cols, dev)]), "f32", code="e5m2")
+    yref = schemes.scaled_gemm_ref(aq, s, wq_s, sw_s, act="tensor", weight="block", a_code="e5m2", w_code="e5m2")
+    check_t2(bf16_tensor_to_f64(y[_idx(rows, dev)][:, _idx(cols, dev)]), yref)
+
+
+@pytest.mark.parametrize("name,N,K", workloads.DECODE_SHAPES, ids=[s[0] for s in workloads.DECODE_SHAPES])
+def test_fused_quant_decode_full_shapes(dev, name, N, K):
+    """The fused-quantization decode GEMM at every decode batch size and the full weight shape."""
+    seed = sum(map(ord, name)) + 800
+    w = workloads.device_bf16((N, K), seed, dev, outliers=False, std=0.02)
+    wq, sw = fgb.quantize_weight(w)
+    _, cols = _pick(np.random.default_rng(seed), 1, N)
+    wq_s, sw_s = blockquant.weight_quant(_bits(w[_idx(cols, dev)]), "f32")
+    for M in workloads.DECODE_MS:
+        x = workloads.device_bf16((M, K), seed + M, dev)
+        y = fgb.gemm_fused_quant(x, wq, sw)
+        torch.cuda.synchronize()
+        aq, sa = blockquant.act_quant(_bits(x))
+        yref = gemm.gemm_ref(aq, sa, wq_s, sw_s, "f32")
+        check_t2(bf16_tensor_to_f64(y[:, _idx(cols, dev)]), yref)
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+@pytest.mark.parametrize("tokens", [1, 8, 64])
+def test_moe_decode_shaped_full(dev, proj, tokens):
+    """32 experts at the full expert shapes, top-8 Zipf routing of a few tokens: the grouped
+    layout (8 or 64 rows in all) or, for 64 tokens, the batched layout with 64-row slots; every
+    routed row against the oracle on sampled weight columns."""
+    cfg = workloads.MOE
+    E = cfg["E"]
+    N, K = cfg[proj]
+    _, offsets, counts = workloads.moe_routing(tokens=tokens, key=(0, 9, tokens, 1))
+    seed = 900 + tokens + (0 if proj == "gate_up" else 50)
+    w = workloads.device_bf16((E * N, K), seed, dev, outliers=False, std=0.02)
+    wq, sw = fgb.quantize_weight(w)
+    wq3, sw3 = wq.view(E, N, K), sw.view(E, N // 128, K // 128)
+    if tokens <= 8:
+        T = int(offsets[-1])
+        x = workloads.device_bf16((T, K), seed + 1, dev)
+        q, sa = fgb.quantize(x)
+        y = fgb.grouped_gemm(q, sa, wq3, sw3, torch.from_numpy(offsets).to(dev))
+        spans = [(e, offsets[e], offsets[e + 1]) for e in range(E)]
+    else:
+        slot = 64
+        cnt = np.minimum(counts, slot).astype(np.int32)
+        x = workloads.device_bf16((E * slot, K), seed + 1, dev)
+        q, sa = fgb.quantize(x)
+        y = fgb.batched_gemm(q, sa, wq3, sw3, torch.from_numpy(cnt).to(dev), slot)
+        spans = [(e, e * slot, e * slot + cnt[e]) for e in range(E)]
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    for e, r0, r1 in spans:
+        if r1 <= r0:
+            continue
+        rows = np.arange(r0, r1)
+        _, cols = _pick(rng, 1, N, nblocks=2)
+        aq, sa_o = blockquant.act_quant(_bits(x[_idx(rows, dev)]))
+        wq_s, sw_s = blockquant.weight_quant(_bits(w[_idx(e * N + cols, dev)]), "f32")
+        yref = gemm.gemm_ref(aq, sa_o, wq_s, sw_s, "f32")
+        check_t2(bf16_tensor_to_f64(y[_idx(rows, dev)][:, _idx(cols, dev)]), yref)
+
