@@ -9,15 +9,19 @@ namespace fgb {
 
 namespace {
 
-// waves splitting K per 16-row tile for the small-M kernel: about 4k waves in total
 int small_waves(int64_t N, int64_t K) { return decode_small_waves(N, K); }
 
 }  // namespace
 
+// Waves splitting K per 16-row tile in the M <= 16 kernels: 8 for at most 256 tiles (one per CU),
+// else 4 (and at most one per K-block).  Measured over the decode shapes at M = 1 and 8 (graph
+// loop) against the earlier rule of about 4k waves in all (1 wave per tile for 1536 and more
+// tiles): 24576x1536 at M = 1 9.4 -> 8.2 us, 28672x4096 25.0 -> 24.3 us; 4 beats 8 from 384
+// tiles on (6144x4096: 7.6 vs 8.1 us) and 8 beats 4 at 256 tiles (4096x4096: 5.7 vs 5.9 us).
 int decode_small_waves(int64_t N, int64_t K) {
   const int64_t tiles = N / 16;
-  int wk = 1;
-  while (wk < 8 && tiles * wk * 2 <= 4096 && wk * 2 <= K / 128) wk *= 2;
+  int wk = tiles <= 256 ? 8 : 4;
+  while (wk > 1 && wk > K / 128) wk /= 2;
   return wk;
 }
 

@@ -605,8 +605,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_fused_quant_small_kernel(
       float am = 0.0f;
 #pragma unroll
       for (int i = 0; i < E; ++i) am = fmaxf(am, fabsf(f[i]));
-#pragma unroll
-      for (int d = 1; d < LPR; d <<= 1) am = fmaxf(am, __shfl_xor(am, d));
+      am = group_max_nonneg<LPR>(am);
       const float sa = am / kE4M3Max;  // IEEE float32 division, as act_quant
       const Divisor dv = make_divisor(sa);
       if (__all(dv.fast)) {

@@ -12,14 +12,14 @@ void launch_small(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t
   const dim3 grid((unsigned)(a.N / 16)), block(64 * WK);
   if (a.s_w_fmt == 0) {
     if (a.y_dtype == 0)
-      hipLaunchKernelGGL((gemm_decode_fused_quant_small_kernel<WK, MQ, 4, 0, 0>), grid, block, 0, stream, a, x, ldx);
+      hipLaunchKernelGGL((gemm_decode_fused_quant_small_kernel<WK, MQ, 3, 0, 0>), grid, block, 0, stream, a, x, ldx);
     else
-      hipLaunchKernelGGL((gemm_decode_fused_quant_small_kernel<WK, MQ, 4, 0, 1>), grid, block, 0, stream, a, x, ldx);
+      hipLaunchKernelGGL((gemm_decode_fused_quant_small_kernel<WK, MQ, 3, 0, 1>), grid, block, 0, stream, a, x, ldx);
   } else {
     if (a.y_dtype == 0)
-      hipLaunchKernelGGL((gemm_decode_fused_quant_small_kernel<WK, MQ, 4, 1, 0>), grid, block, 0, stream, a, x, ldx);
+      hipLaunchKernelGGL((gemm_decode_fused_quant_small_kernel<WK, MQ, 3, 1, 0>), grid, block, 0, stream, a, x, ldx);
     else
-      hipLaunchKernelGGL((gemm_decode_fused_quant_small_kernel<WK, MQ, 4, 1, 1>), grid, block, 0, stream, a, x, ldx);
+      hipLaunchKernelGGL((gemm_decode_fused_quant_small_kernel<WK, MQ, 3, 1, 1>), grid, block, 0, stream, a, x, ldx);
   }
 }
 

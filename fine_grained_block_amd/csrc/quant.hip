@@ -9,16 +9,6 @@
 
 namespace fgb {
 
-// Max over the 16 lanes of a DPP row (lanes 16r .. 16r+15), via four DPP moves:
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
-  return v;
-}
-
 constexpr float kE5M2Max = 57344.0f;
 
 // Quantize 8 values (4 bf16 pairs) to E5M2 with the IEEE quotient x / d (E5M2 resolves values down

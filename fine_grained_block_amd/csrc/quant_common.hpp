@@ -7,6 +7,47 @@
 
 namespace fgb {
 
+// Max over the 16 lanes of a DPP row (lanes 16r .. 16r+15), via four DPP moves:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// Max over the 8 lanes of a DPP half-row (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror).
+__device__ __forceinline__ float row8_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  return v;
+}
+
+// Max of non-negative values over groups of L consecutive lanes (L = 8, 16, 32 or 64), returned
+// to every lane of the group: DPP within 16-lane rows, then the rows' maxima read with
+// v_readlane and compared as integers (non-negative floats order like their bit patterns).
+template <int L>
+__device__ __forceinline__ float group_max_nonneg(float v) {
+  static_assert(L == 8 || L == 16 || L == 32 || L == 64, "8, 16, 32 or 64 lanes");
+  if constexpr (L == 8) return row8_max(v);
+  v = row16_max(v);
+  if constexpr (L == 16) return v;
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(v), 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(v), 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(v), 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(v), 48);
+  if constexpr (L == 32) {
+    const uint32_t lo = r0 > r1 ? r0 : r1, hi = r2 > r3 ? r2 : r3;
+    return __uint_as_float((threadIdx.x & 32) ? hi : lo);
+  } else {
+    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    return __uint_as_float(a > b ? a : b);
+  }
+}
+
 // Group divisor: the stored scale s, or 1 for an all-zero group (every x is +-0 there and the
 // code keeps the sign).  `r` is the correctly rounded reciprocal 1/d, `fast` says whether d is in
 // the range where the reciprocal-and-correct quotient below equals the IEEE quotient x/d.
