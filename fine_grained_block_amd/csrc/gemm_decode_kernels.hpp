@@ -112,6 +112,9 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
       r0 = ex * p.slot;
       r1 = r0 + min(max((int64_t)gload<int>(p.offsets + ex), (int64_t)0), p.slot);
     }
+    // grid.z splits an expert's rows into chunks of MR (each chunk streams the weights again)
+    r0 += (int64_t)blockIdx.z * MR;
+    r1 = min(r1, r0 + MR);
     row_base = __builtin_amdgcn_readfirstlane((int)r0);
     M = __builtin_amdgcn_readfirstlane((int)(r1 - r0));
     if (M <= 0) return;
@@ -140,6 +143,9 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
   const uint32_t soff = (uint32_t)((row_base + (lane < M ? lane : M - 1)) * 4);
   const uint8_t* wbase = p.w_q + (ex * p.N + n0) * K;
 
+  // 8-row activation copy groups that hold real rows (the others would only repeat row M-1 into
+  // rows whose outputs are not stored): fewer copies where M is below the staged rows
+  const int agrp = (int)min((int64_t)(MR / 8), (M + 7) / 8);
   auto issue = [&](int kk) {
     uint8_t* st = wring + (kk % D) * STAGE;
     const int64_t kb = kb0 + kk;
@@ -157,9 +163,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int q = 0; q < MR / 8; ++q) {
-      uint32_t o = aoff[q];
-      asm volatile("" : "+v"(o));
-      __builtin_amdgcn_global_load_lds(GPTR(ab + o), LPTR(st + WST + q * 1024), 16, 0, 0);
+      if (q < agrp) {
+        uint32_t o = aoff[q];
+        asm volatile("" : "+v"(o));
+        __builtin_amdgcn_global_load_lds(GPTR(ab + o), LPTR(st + WST + q * 1024), 16, 0, 0);
+      }
     }
     if constexpr (SCH == 0) {
       uint32_t o = soff;
@@ -196,7 +204,19 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
     for (int kk = 0; kk < nk; ++kk) {
       // refill the stage consumed one block ago (clamped past the slice: never a pending stage)
       issue(min(kk + D - 1, nk - 1));
-      __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * OPS>());
+      // own copies of this block landed, the D-1 younger stages' may stay in flight
+      // (2 + agrp + 1 copies per stage; the wait count is an immediate, hence the cases)
+      {
+        constexpr int FIX = OPS - MR / 8;
+        if (agrp == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + 1)>());
+        else if (agrp == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 16 ? 2 : 1))>());
+        else if (agrp == 3) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 32 ? 3 : 1))>());
+        else if (agrp == 4) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 32 ? 4 : 1))>());
+        else if (agrp == 5) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 5 : 1))>());
+        else if (agrp == 6) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 6 : 1))>());
+        else if (agrp == 7) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 7 : 1))>());
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * OPS>());
+      }
       // The LDS reads are written as one asm block that also waits for them: the compiler cannot
       // tell this wave's ring stages apart and would otherwise wait for every copy in flight.
       const uint32_t st = (uint32_t)(uintptr_t)LPTR(wring + (kk % D) * STAGE);
