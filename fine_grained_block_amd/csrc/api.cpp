@@ -14,6 +14,7 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // grid and index arithmetic bound
 constexpr int64_t kMax32 = (int64_t)1 << 32;   // bytes addressable by a 32-bit offset
 constexpr int kMaxDevices = 64;
+constexpr int kMaxExperts = 65535;  // experts index grid.y in the per-expert decode kernels
 
 // 0 = unknown, 1 = gfx950, -1 = other
 int g_dev_ok[kMaxDevices];
@@ -276,7 +277,7 @@ int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
                                 void* y, int y_dtype, int64_t ldy, int64_t N, int64_t K,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace; (void)workspace_bytes;
-  if (E <= 0 || E > 65536) return FGB_ERR_SHAPE;
+  if (E <= 0 || E > kMaxExperts) return FGB_ERR_SHAPE;
   int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, total_M, N, K);
   if (st != FGB_OK || total_M == 0) return st;
   if (!expert_offsets) return FGB_ERR_NULL;
@@ -296,7 +297,7 @@ int fgb_batched_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
                                 const uint8_t* w_q, const void* s_w, int s_w_fmt, const int32_t* counts,
                                 int32_t E, int64_t max_M, void* y, int y_dtype, int64_t ldy, int64_t N, int64_t K,
                                 void* stream) {
-  if (E <= 0 || E > 65536 || max_M < 0 || max_M >= kMaxDim) return FGB_ERR_SHAPE;
+  if (E <= 0 || E > kMaxExperts || max_M < 0 || max_M >= kMaxDim) return FGB_ERR_SHAPE;
   const int64_t rows = (int64_t)E * max_M;
   if (rows >= kMaxDim) return FGB_ERR_SHAPE;
   int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, rows, N, K);
@@ -314,7 +315,7 @@ int fgb_batched_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
 
 int fgb_check_expert_offsets(const int32_t* expert_offsets, int32_t E, int64_t total_M, int32_t* result,
                              void* stream) {
-  if (E <= 0 || E > 65536 || total_M < 0) return FGB_ERR_SHAPE;
+  if (E <= 0 || E > kMaxExperts || total_M < 0) return FGB_ERR_SHAPE;
   if (!expert_offsets || !result) return FGB_ERR_NULL;
   if (((uintptr_t)expert_offsets & 3u) || ((uintptr_t)result & 3u)) return FGB_ERR_ALIGN;
   int st = check_device();

@@ -173,8 +173,8 @@ size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, i
  *                   (a precondition: checking it would need a device synchronization);
  *   total_M         host copy of offsets[E];
  *   y [total_M, ldy].
- * Experts with no rows are legal and write nothing.  Size limits as for fgb_w8a8_block_gemm
- * (per expert for W).
+ * Experts with no rows are legal and write nothing.  1 <= E <= 65535.  Size limits as for
+ * fgb_w8a8_block_gemm (per expert for W).
  */
 int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
                                 const uint8_t* w_q, const void* s_w, int s_w_fmt,
@@ -207,7 +207,7 @@ int fgb_batched_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
  * Writes to `result` (DEVICE int32, 4-byte aligned; read it after synchronizing the stream) 0
  * when expert_offsets[0] == 0, the offsets are nondecreasing and expert_offsets[E] == total_M,
  * otherwise 1 + the first index i in 0..E whose entry breaks that.  Reads the E+1 offsets only.
- * FGB_ERR_SHAPE for E outside 1..65536 or total_M < 0, FGB_ERR_NULL, FGB_ERR_ALIGN as usual.
+ * FGB_ERR_SHAPE for E outside 1..65535 or total_M < 0, FGB_ERR_NULL, FGB_ERR_ALIGN as usual.
  */
 int fgb_check_expert_offsets(const int32_t* expert_offsets, int32_t E, int64_t total_M, int32_t* result,
                              void* stream);

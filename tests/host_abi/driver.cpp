@@ -105,7 +105,7 @@ int main() {
                                        nullptr);
   };
   EXPECT(grouped(0, 256, F), FGB_ERR_SHAPE);
-  EXPECT(grouped(65537, 256, F), FGB_ERR_SHAPE);
+  EXPECT(grouped(65536, 256, F), FGB_ERR_SHAPE);
   EXPECT(grouped(4, 256, 0), FGB_ERR_NULL);
   EXPECT(grouped(4, 256, F + 2), FGB_ERR_ALIGN);
   EXPECT(grouped(4, 0, F), FGB_OK);
@@ -119,6 +119,7 @@ int main() {
                                        P(F), 0, (const int32_t*)P(cnt), E, max_m, P(F), 0, 512, 512, 1024, nullptr);
   };
   EXPECT(batched(0, 64, F), FGB_ERR_SHAPE);
+  EXPECT(batched(65536, 0, F), FGB_ERR_SHAPE);
   EXPECT(batched(8, -1, F), FGB_ERR_SHAPE);
   EXPECT(batched(8, 64, 0), FGB_ERR_NULL);
   EXPECT(batched(8, 64, F + 2), FGB_ERR_ALIGN);

@@ -101,7 +101,7 @@ def test_gemm_validation(L):
 def test_check_expert_offsets_validation(L):
     """The offsets check validates its arguments before any device work."""
     assert L.fgb_check_expert_offsets(FAKE, 0, 10, FAKE, None) == ERR["SHAPE"]
-    assert L.fgb_check_expert_offsets(FAKE, 65537, 10, FAKE, None) == ERR["SHAPE"]
+    assert L.fgb_check_expert_offsets(FAKE, 65536, 10, FAKE, None) == ERR["SHAPE"]
     assert L.fgb_check_expert_offsets(FAKE, 4, -1, FAKE, None) == ERR["SHAPE"]
     assert L.fgb_check_expert_offsets(None, 4, 10, FAKE, None) == ERR["NULL"]
     assert L.fgb_check_expert_offsets(FAKE, 4, 10, None, None) == ERR["NULL"]
