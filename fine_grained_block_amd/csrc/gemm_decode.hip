@@ -166,8 +166,8 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
 namespace {
 
 template <int MR, int D, int MODE>
-void launch_moe_rows(const GemmArgs& a, int64_t rows_per_expert, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.N / 16), (unsigned)a.E, (unsigned)((rows_per_expert + MR - 1) / MR)), block(256);
+void launch_moe_rows(const GemmArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.N / 16), (unsigned)a.E), block(256);
   if (a.s_w_fmt == 0) {
     if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 0, 0, 0, 0, MODE>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 0, 1, 0, 0, MODE>), grid, block, 0, stream, a);
@@ -177,15 +177,19 @@ void launch_moe_rows(const GemmArgs& a, int64_t rows_per_expert, hipStream_t str
   }
 }
 
-// 8 or 16 staged rows per workgroup, the expert's rows in chunks of that many along grid.z: with
-// few rows per expert (top-k routing of a few tokens) the ring stays 5 or 4 blocks deep, where 32
-// or 64 staged rows would leave room for only 3 or 2 stages.  Measured, 32 experts, top-8 routing
-// of 8 tokens (64 rows in all, at most 8 per expert): gate+up 4096x7168 247 -> 143 us, down
-// 7168x2048 173 -> 109 us; 64-row batched slots (up to four chunks): 310 -> 274 and 216 -> 190 us.
+// 8 or 16 staged rows per workgroup; one workgroup per (16 weight rows, expert) walks the
+// expert's rows in passes of that many.  With few rows per expert (top-k routing of a few tokens)
+// the ring stays 5 or 4 blocks deep, where 32 staged rows leave room for 3 (measured slower on
+// every case below).  Passes inside the workgroup rather than one workgroup per chunk of rows:
+// the grid then holds no workgroups without rows, which hold a CU slot for the latency of their
+// count load, and a second pass re-reads a weight tile its CU has just streamed.  Measured, 32
+// experts, gate+up 4096x7168 / down 7168x2048, graph loop: top-8 routing of 1 token 44.3 -> 41.8
+// / 33.1 -> 29.1 us, of 8 tokens (64 rows) 143 -> 136 / 109 -> 96 us; 64-row batched slots for 64
+// tokens 274 -> 242 / 190 -> 160 us.
 template <int MODE>
 void launch_moe_mr(const GemmArgs& a, int64_t rows_per_expert, hipStream_t stream) {
-  if (rows_per_expert <= 8) launch_moe_rows<8, 5, MODE>(a, rows_per_expert, stream);
-  else launch_moe_rows<16, 4, MODE>(a, rows_per_expert, stream);
+  if (rows_per_expert <= 8) launch_moe_rows<8, 5, MODE>(a, stream);
+  else launch_moe_rows<16, 4, MODE>(a, stream);
 }
 
 }  // namespace
