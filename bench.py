@@ -283,7 +283,9 @@ def extra_suites(torch, fgb, workloads, np):
             # GEMM that quantizes the activations itself (one launch)
             two = _graph_time(torch, lambda i: (fgb.quantize(x, out=(q, sa)),
                                                 fgb.gemm(q, sa, wqs[i % copies], sw, out=y, workspace=ws)), 4 * copies)
-            one = _graph_time(torch, lambda i: fgb.gemm_fused_quant(x, wqs[i % copies], sw, out=y), 4 * copies)
+            fws = torch.zeros(max(256, fgb.gemm_fused_quant_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+            one = _graph_time(torch, lambda i: fgb.gemm_fused_quant(x, wqs[i % copies], sw, out=y, workspace=fws),
+                              4 * copies)
             fbytes = N * K + 4 * (N // 128) * (K // 128) + 2 * M * K + 2 * M * N
             fused[f"{name}_{N}x{K}_M{M}"] = dict(quant_plus_gemm_us=round(two, 2), fused_us=round(one, 2),
                                                  fused_frac_hbm=round(fbytes / one / 1e3 / PEAK_HBM_GBS, 3))

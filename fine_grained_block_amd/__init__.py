@@ -39,6 +39,7 @@ from .ops import (  # noqa: F401
     gemm,
     gemm_noalloc,
     gemm_fused_quant,
+    gemm_fused_quant_workspace_bytes,
     grouped_gemm,
     batched_gemm,
     check_offsets,

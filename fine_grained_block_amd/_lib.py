@@ -25,8 +25,9 @@ _SIGS = {
                                            _c_i64, _c_i64, _c_i64, _c_i64, _vp, ctypes.c_size_t, _vp]),
     "fgb_w8a8_block_gemm_noalloc": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _vp, _vp, ctypes.c_int, _vp,
                                                    ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _vp]),
+    "fgb_gemm_fused_quant_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "fgb_w8a8_block_gemm_fused_quant": (ctypes.c_int, [_vp, _c_i64, _vp, _vp, ctypes.c_int, _vp, ctypes.c_int,
-                                                       _c_i64, _c_i64, _c_i64, _c_i64, _vp]),
+                                                       _c_i64, _c_i64, _c_i64, _c_i64, _vp, ctypes.c_size_t, _vp]),
     "fgb_grouped_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, ctypes.c_int32]),
     "fgb_grouped_w8a8_block_gemm": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _vp, _vp, ctypes.c_int, _vp,
                                                    ctypes.c_int32, _c_i64, _vp, ctypes.c_int, _c_i64, _c_i64,

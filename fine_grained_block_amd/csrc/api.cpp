@@ -246,9 +246,14 @@ int fgb_w8a8_scaled_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int 
   return launch_status(fgb::launch_gemm_scaled_prefill(a, sch, code, (hipStream_t)stream));
 }
 
+size_t fgb_gemm_fused_quant_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > 64 || N <= 0 || K <= 0 || N % FGB_BLOCK || K % FGB_BLOCK || K > 32768) return 0;
+  return fgb::fused_workspace_bytes(M, N, K);
+}
+
 int fgb_w8a8_block_gemm_fused_quant(const uint16_t* x, int64_t ldx, const uint8_t* w_q, const void* s_w,
                                     int s_w_fmt, void* y, int y_dtype, int64_t ldy, int64_t M, int64_t N, int64_t K,
-                                    void* stream) {
+                                    void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || M > 64 || N <= 0 || K <= 0 || N >= kMaxDim || K >= kMaxDim) return FGB_ERR_SHAPE;
   if (N % FGB_BLOCK || K % FGB_BLOCK) return FGB_ERR_SHAPE;
   if (s_w_fmt != FGB_SCALE_F32 && s_w_fmt != FGB_SCALE_UE8M0) return FGB_ERR_ENUM;
@@ -260,10 +265,13 @@ int fgb_w8a8_block_gemm_fused_quant(const uint16_t* x, int64_t ldx, const uint8_
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(s_w) || !aligned16(y)) return FGB_ERR_ALIGN;
   if ((ldx * 2) % 16 || (ldy * ybytes) % 16) return FGB_ERR_ALIGN;
   if (M * ldx * 2 >= kMax32 || N * K >= kMax32 || K > 32768) return FGB_ERR_SHAPE;
+  const size_t need = fgb::fused_workspace_bytes(M, N, K);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FGB_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return FGB_ERR_ALIGN;
   int st = check_device();
   if (st != FGB_OK) return st;
   fgb::GemmArgs a{nullptr, 0, nullptr, 0, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K, nullptr, 1, 0};
-  return launch_status(fgb::launch_gemm_decode_fused(a, x, ldx, (hipStream_t)stream));
+  return launch_status(fgb::launch_gemm_decode_fused(a, x, ldx, workspace, (hipStream_t)stream));
 }
 
 size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, int32_t E) {

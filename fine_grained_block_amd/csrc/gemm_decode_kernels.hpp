@@ -340,181 +340,18 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// The same weight streaming with the dynamic activation quantization done in the kernel
-// (Transformers "Fine-grained FP8", intro and "DeepGEMM fast path": activation scales computed at
-// run time per token and 1x128 group): each wave streams the bf16 activation rows of its K-slice
-// through its ring next to the weight rows and quantizes every 128-element group right before its
-// MFMA, with the quantizer's own arithmetic (s = fl32(amax / 448), codes E4M3(fl32(x / s))), so
-// the codes and scales equal those of act_quant and, with the same K-split and order as the
-// two-launch path's kernel, so does the float32 result.  Every workgroup quantizes the rows it
-// multiplies, so the quantization is repeated N/16 times: cheap next to the weight stream for a
-// few tokens, not for 64.
-//
-// The bf16 rows are 256 bytes in LDS; 16-byte chunk c of row r sits at c ^ (r & 15), so the 16
-// rows of a tile read at one logical chunk hit 16 distinct bank groups.  Lane l handles row l % 16
-// and the 32 elements 32g .. 32g+31 (g = l / 16) of each group: the bytes the MFMA's B operand
-// takes from that lane.  The 128-element amax is the max over the four lanes of a row.
-template <int WK, int MR, int D, int SWF, int OUT>
-__global__ __launch_bounds__(64 * WK) void gemm_decode_fused_quant_kernel(GemmArgs p, const uint16_t* __restrict__ x,
-                                                                          int64_t ldx) {
-  constexpr int MT = MR >= 16 ? MR / 16 : 1;  // token tiles per wave
-  constexpr int WST = 16 * 128, AST = MR * 256;
-  constexpr int STAGE = WST + AST;
-  constexpr int OPS = 2 + MR / 4;  // direct copies per stage: 2 weight groups, MR/4 activation groups
-  static_assert(MR == 8 || MR == 16 || MR == 32 || MR == 64, "8, 16, 32 or 64 activation rows");
-  static_assert((D - 1) * OPS <= 63, "copies in flight fit the vmcnt counter");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[WK * D * STAGE];
-  __shared__ v4f red[WK > 1 ? WK - 1 : 1][MT][64];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t K = p.K, M = p.M;
-  const int KB = (int)(K / 128);
-  const int per = (KB + WK - 1) / WK;
-  const int kb0 = min(KB, wave * per);
-  const int nk = min(KB, kb0 + per) - kb0;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t nb = n0 / 128;
-  uint8_t* const wring = ring + wave * D * STAGE;
-
-  // weight copy sources as in the ring kernel; activation group q, lane i: LDS row 4q + i/16,
-  // slot i % 16, which holds logical chunk (i % 16) ^ (row & 15) of that row (rows >= M repeat M-1)
-  uint32_t woff[2], aoff[MR / 4];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 8 * q + (lane >> 3);
-    woff[q] = (uint32_t)(r * K + (((lane & 7) ^ swz_g(r)) * 16));
-  }
-#pragma unroll
-  for (int q = 0; q < MR / 4; ++q) {
-    const int r = 4 * q + (lane >> 4);
-    const int64_t m = r < M ? r : M - 1;
-    aoff[q] = (uint32_t)(m * ldx * 2 + (((lane & 15) ^ (r & 15)) * 16));
-  }
-  const uint8_t* wbase = p.w_q + n0 * K;
-
-  auto issue = [&](int kk) {
-    uint8_t* st = wring + (kk % D) * STAGE;
-    const int64_t kb = kb0 + kk;
-    const uint8_t* wb = wbase + kb * 128;
-    const uint8_t* ab = reinterpret_cast<const uint8_t*>(x) + kb * 256;
-    asm volatile("" : "+s"(wb));
-    asm volatile("" : "+s"(ab));
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      uint32_t o = woff[q];
-      asm volatile("" : "+v"(o));
-      __builtin_amdgcn_global_load_lds(GPTR(wb + o), LPTR(st + q * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < MR / 4; ++q) {
-      uint32_t o = aoff[q];
-      asm volatile("" : "+v"(o));
-      __builtin_amdgcn_global_load_lds(GPTR(ab + o), LPTR(st + WST + q * 1024), 16, 0, 0);
-    }
-  };
-
-  float sw0 = 0.0f, sw1 = 0.0f, sw2 = 0.0f, sw3 = 0.0f;
-  {
-    const int64_t b = nb * KB + kb0;
-    sw0 = lane < nk ? load_sw<SWF>(p.s_w, b + lane) : 0.0f;
-    sw1 = lane + 64 < nk ? load_sw<SWF>(p.s_w, b + lane + 64) : 0.0f;
-    sw2 = lane + 128 < nk ? load_sw<SWF>(p.s_w, b + lane + 128) : 0.0f;
-    sw3 = lane + 192 < nk ? load_sw<SWF>(p.s_w, b + lane + 192) : 0.0f;
-  }
-  auto sw_at = [&](int kk) -> float {
-    const int l = kk & 63, t = kk >> 6;
-    const int r0 = __builtin_amdgcn_readlane(__float_as_int(sw0), l);
-    const int r1 = __builtin_amdgcn_readlane(__float_as_int(sw1), l);
-    const int r2 = __builtin_amdgcn_readlane(__float_as_int(sw2), l);
-    const int r3 = __builtin_amdgcn_readlane(__float_as_int(sw3), l);
-    const int lo = (t & 1) ? r1 : r0, hi = (t & 1) ? r3 : r2;
-    return __int_as_float((t & 2) ? hi : lo);
-  };
-
-  const int r = lane & 15, g = lane >> 4;
-  v4f acc[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  if (nk > 0) {
-#pragma unroll
-    for (int i = 0; i < D - 1; ++i) issue(min(i, nk - 1));
-    for (int kk = 0; kk < nk; ++kk) {
-      issue(min(kk + D - 1, nk - 1));
-      __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * OPS>());
-      const uint32_t st = (uint32_t)(uintptr_t)LPTR(wring + (kk % D) * STAGE);
-      const uint32_t aw0 = st + swz(r, 2 * g), aw1 = st + swz(r, 2 * g + 1);
-      v4i w0, w1;
-      asm volatile(
-          "ds_read_b128 %0, %2\n\t"
-          "ds_read_b128 %1, %3\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(w0), "=&v"(w1)
-          : "v"(aw0), "v"(aw1)
-          : "memory");
-      v8i wf;
-      wf[0] = w0[0]; wf[1] = w0[1]; wf[2] = w0[2]; wf[3] = w0[3];
-      wf[4] = w1[0]; wf[5] = w1[1]; wf[6] = w1[2]; wf[7] = w1[3];
-      const float sw = sw_at(kk);
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        // this lane's 32 bf16 of row 16j + r (row r & (MR-1) when MR = 8): logical chunks 4g .. 4g+3
-        const int row = MR >= 16 ? 16 * j + r : (r & (MR - 1));
-        const uint32_t rb = st + WST + row * 256;
-        const int f = row & 15;
-        v4i c0, c1, c2, c3;
-        asm volatile(
-            "ds_read_b128 %0, %4\n\t"
-            "ds_read_b128 %1, %5\n\t"
-            "ds_read_b128 %2, %6\n\t"
-            "ds_read_b128 %3, %7\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(c0), "=&v"(c1), "=&v"(c2), "=&v"(c3)
-            : "v"(rb + (((4 * g) ^ f) << 4)), "v"(rb + (((4 * g + 1) ^ f) << 4)), "v"(rb + (((4 * g + 2) ^ f) << 4)),
-              "v"(rb + (((4 * g + 3) ^ f) << 4))
-            : "memory");
-        const uint4 u0 = make_uint4(c0[0], c0[1], c0[2], c0[3]), u1 = make_uint4(c1[0], c1[1], c1[2], c1[3]);
-        const uint4 u2 = make_uint4(c2[0], c2[1], c2[2], c2[3]), u3 = make_uint4(c3[0], c3[1], c3[2], c3[3]);
-        // the group's amax: this lane's 32 values, then the other three lanes of the row
-        float am = fmaxf(fmaxf(absmax8(u0), absmax8(u1)), fmaxf(absmax8(u2), absmax8(u3)));
-        am = fmaxf(am, __shfl_xor(am, 16));
-        am = fmaxf(am, __shfl_xor(am, 32));
-        const float sa = am / kE4M3Max;  // IEEE float32 division, as act_quant
-        const Divisor dv = make_divisor(sa);
-        const uint2 q0 = quant8(u0, dv), q1 = quant8(u1, dv), q2 = quant8(u2, dv), q3 = quant8(u3, dv);
-        v8i af;
-        af[0] = q0.x; af[1] = q0.y; af[2] = q1.x; af[3] = q1.y;
-        af[4] = q2.x; af[5] = q2.y; af[6] = q3.x; af[7] = q3.y;
-        acc[j] += mfma_e4m3_16x16x128(wf, af) * (sa * sw);
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
-  if constexpr (WK > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int j = 0; j < MT; ++j) red[wave - 1][j][lane] = acc[j];
-    }
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 0; w < WK - 1; ++w)
-#pragma unroll
-      for (int j = 0; j < MT; ++j) acc[j] += red[w][j][lane];
-  }
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int m = 16 * j + (lane & 15);
-    if (m < M) store4<OUT>(p.y, p.ldy, m, n0 + 4 * (lane >> 4), acc[j]);
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
-// The fused kernel for M <= 8: only the MQ (>= M, a power of two up to 8) real activation rows are
-// quantized, spread over all 64 lanes (2*MQ elements per lane, 64/MQ lanes per row), so each
-// wave's quantization work per K-block is MQ/16 of the kernel above.  The codes and the row
-// scales go to a per-wave LDS tile in the MFMA operand layout (16 rows of 128 bytes, rows >= MQ
-// never written: they feed only output columns of tokens >= M, which are not stored), from which
-// the B operand is read as for the ring kernel.  Same arithmetic, K split and order as above.
+// The weight streaming of the ring kernel with the dynamic activation quantization done in the
+// kernel, for M <= 8 (Transformers "Fine-grained FP8", intro and "DeepGEMM fast path":
+// activation scales computed at run time per token and 1x128 group).  Each wave streams its 16
+// weight rows and the bf16 activation rows of its K-slice through its ring and quantizes every
+// 128-element group right before its MFMA with the quantizer's own arithmetic (s = fl32(amax /
+// 448), codes E4M3(fl32(x / s))), so codes and scales equal those of act_quant and, with the
+// two-launch path's K split and summation order, so does the float32 result.  Only the MQ (>= M,
+// a power of two up to 8) real rows are quantized, spread over all 64 lanes (2*MQ elements per
+// lane, 64/MQ lanes per row).  The bf16 rows are 256 bytes in LDS, 16-byte chunk c of row r at
+// c ^ (r & 15).  The codes and the row scales go to a per-wave LDS tile in the MFMA operand
+// layout (16 rows of 128 bytes, rows >= MQ never written: they feed only output columns of
+// tokens >= M, which are not stored), from which the B operand is read as in the ring kernel.
 template <int WK, int MQ, int D, int SWF, int OUT>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_fused_quant_small_kernel(GemmArgs p,
                                                                                 const uint16_t* __restrict__ x,

@@ -1,51 +1,52 @@
-// gemm_fused.hip — launches of the decode GEMM that quantizes its bf16 activations itself
-// (gemm_decode_fused_quant_kernel): one launch for act_quant_group128 + w8a8_block_gemm at M <= 64.
-// The K split follows the two-launch path's per-wave ring and register kernels (the same waves
-// per workgroup, slices and summation order), so where that path uses them the results agree bit
-// for bit.
+// gemm_fused.hip — act_quant_group128 + w8a8_block_gemm from bf16 activations at decode sizes
+// (M <= 64) behind one call.
+//
+// Few tokens: one launch of the GEMM that quantizes its activations itself
+// (gemm_decode_fused_quant_small_kernel).  Every workgroup quantizes the rows it multiplies, so
+// the quantization is repeated N/16 times; measured against act_quant + GEMM (graph loop, the six
+// decode shapes from 4096x4096 to 7168x18432), the one launch is faster up to 4 rows on every
+// shape (e.g. 4096x4096 6.9 vs 9.2 us, 28672x4096 25.7 vs 28.6 us at M = 4) and up to 8 rows
+// only for weights of at most 24 MiB; from 12 rows on the repeated quantization costs more than
+// the launch it saves (28672x4096 at M = 64: 239 vs 33 us).  Beyond those sizes the call
+// quantizes into the caller's workspace and runs the decode GEMM on it: the same kernels as the
+// two calls, so the same bits.
 #include "gemm_decode_kernels.hpp"
 
 namespace fgb {
 
 namespace {
 
-template <int WK, int MR, int D>
-void launch_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.N / 16)), block(64 * WK);
-  if (a.s_w_fmt == 0) {
-    if (a.y_dtype == 0)
-      hipLaunchKernelGGL((gemm_decode_fused_quant_kernel<WK, MR, D, 0, 0>), grid, block, 0, stream, a, x, ldx);
-    else
-      hipLaunchKernelGGL((gemm_decode_fused_quant_kernel<WK, MR, D, 0, 1>), grid, block, 0, stream, a, x, ldx);
-  } else {
-    if (a.y_dtype == 0)
-      hipLaunchKernelGGL((gemm_decode_fused_quant_kernel<WK, MR, D, 1, 0>), grid, block, 0, stream, a, x, ldx);
-    else
-      hipLaunchKernelGGL((gemm_decode_fused_quant_kernel<WK, MR, D, 1, 1>), grid, block, 0, stream, a, x, ldx);
-  }
-}
+bool one_launch(int64_t M, int64_t N, int64_t K) { return M <= 4 || (M <= 8 && N * K <= (24ll << 20)); }
 
-template <int MR, int D>
-void launch_fused_wk(int wk, const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream) {
-  if (wk == 1) launch_fused<1, MR, D>(a, x, ldx, stream);
-  else if (wk == 2) launch_fused<2, MR, D>(a, x, ldx, stream);
-  else if (wk == 4) launch_fused<4, MR, D>(a, x, ldx, stream);
-  else launch_fused<8, MR, D>(a, x, ldx, stream);
-}
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// workspace layout: codes [M, K], scales [K/128, ld_sa] with ld_sa = M rounded up to 4 (16-byte
+// rows), then the decode GEMM's own workspace
+int64_t fused_ld_sa(int64_t M) { return (M + 3) & ~(int64_t)3; }
 
 }  // namespace
 
-hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream) {
-  if (a.M <= 8) return launch_gemm_decode_fused_small(a, x, ldx, stream);
-  if (a.M <= 16) {
-    const int wk = decode_small_waves(a.N, a.K);
-    launch_fused_wk<16, 3>(wk, a, x, ldx, stream);
-  } else if (a.M <= 32) {
-    launch_fused<4, 32, 3>(a, x, ldx, stream);
-  } else {
-    launch_fused<4, 64, 2>(a, x, ldx, stream);
-  }
-  return hipGetLastError();
+size_t fused_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (one_launch(M, N, K)) return 0;
+  return round256((size_t)(M * K)) + round256((size_t)((K / 128) * fused_ld_sa(M) * 4)) +
+         decode_workspace_bytes(M, N, K);
+}
+
+hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, void* workspace,
+                                    hipStream_t stream) {
+  if (one_launch(a.M, a.N, a.K)) return launch_gemm_decode_fused_small(a, x, ldx, stream);
+  uint8_t* q = reinterpret_cast<uint8_t*>(workspace);
+  const int64_t ld_sa = fused_ld_sa(a.M);
+  float* s_a = reinterpret_cast<float*>(q + round256((size_t)(a.M * a.K)));
+  void* ws = reinterpret_cast<uint8_t*>(s_a) + round256((size_t)((a.K / 128) * ld_sa * 4));
+  hipError_t e = launch_act_quant(x, a.M, a.K, ldx, q, a.K, s_a, ld_sa, stream);
+  if (e != hipSuccess) return e;
+  GemmArgs b = a;
+  b.a_q = q;
+  b.lda = a.K;
+  b.s_a = s_a;
+  b.ld_sa = ld_sa;
+  return launch_gemm_decode(b, ws, stream);
 }
 
 }  // namespace fgb

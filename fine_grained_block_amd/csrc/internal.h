@@ -60,8 +60,12 @@ hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int code, hipSt
 // slot rows per expert); rows_per_expert bounds every expert's row count.
 hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, int64_t rows_per_expert, hipStream_t stream);
 
-// Decode GEMM that quantizes its bf16 activations itself (M <= 64).
-hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream);
+// act_quant + decode GEMM from bf16 activations (M <= 64): one launch of the GEMM that quantizes
+// its activations itself where that is faster (workspace 0), else act_quant into the workspace
+// and the decode GEMM.
+size_t fused_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, void* workspace,
+                                    hipStream_t stream);
 hipError_t launch_gemm_decode_fused_small(const GemmArgs& a, const uint16_t* x, int64_t ldx, hipStream_t stream);
 // waves per 16-row workgroup that split K in the M <= 16 decode kernels
 int decode_small_waves(int64_t N, int64_t K);

@@ -374,10 +374,16 @@ def check_offsets(offsets: torch.Tensor, total_M: int) -> int:
     return int(result.item())
 
 
+def gemm_fused_quant_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().fgb_gemm_fused_quant_workspace_bytes(M, N, K))
+
+
 def gemm_fused_quant(x: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor, out_dtype=torch.bfloat16,
-                     out: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode-sized (M <= 64) fine-grained FP8 linear in one launch: the GEMM quantizes the bf16
-    activations per token and 1x128 group itself (same codes and scales as quantize())."""
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode-sized (M <= 64) fine-grained FP8 linear from bf16 activations in one call: the
+    result of quantize() + gemm(), bit for bit.  A few tokens take one launch whose GEMM quantizes
+    the activations itself; more tokens quantize into the workspace (allocated here when none of
+    at least gemm_fused_quant_workspace_bytes(M, N, K) bytes is given)."""
     _matrix(x, "x", torch.bfloat16)
     M, K = x.shape
     KB = _blocks(K, "K")
@@ -390,11 +396,18 @@ def gemm_fused_quant(x: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor, out_
     if out is not None:
         _need(out.dtype in (torch.bfloat16, torch.float32), "out must be bf16 or float32")
         _matrix(out, "out", out.dtype, rows=M, cols=N)
-    _on_device(("x", x), ("w_q", w_q), ("s_w", s_w), ("out", out))
+    if workspace is not None:
+        _need(workspace.is_contiguous(), "workspace must be contiguous")
+    _on_device(("x", x), ("w_q", w_q), ("s_w", s_w), ("out", out), ("workspace", workspace))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    need = gemm_fused_quant_workspace_bytes(M, N, K)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().fgb_w8a8_block_gemm_fused_quant(_ptr(x), _row_ld(x), _ptr(w_q), _ptr(s_w), _scale_fmt(s_w), _ptr(out),
-                                               _out_code(out.dtype), _row_ld(out), M, N, K, _stream())
+                                               _out_code(out.dtype), _row_ld(out), M, N, K, _ptr(workspace),
+                                               ws_bytes, _stream())
     check("fgb_w8a8_block_gemm_fused_quant", st)
     return out
 

@@ -143,21 +143,29 @@ int fgb_w8a8_block_gemm_noalloc(const uint8_t* a_q, int64_t lda, const float* s_
                                 void* y, int y_dtype, int64_t ldy,
                                 int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Host query: workspace bytes fgb_w8a8_block_gemm_fused_quant needs (0 if none, and for shapes it
+ * rejects). */
+size_t fgb_gemm_fused_quant_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 /*
- * Dynamic activation quantization fused into the decode GEMM (Transformers "Fine-grained FP8",
- * intro and "DeepGEMM fast path": activations quantized at run time per token in 1x128 groups):
- * the result of fgb_act_quant_group128 followed by fgb_w8a8_block_gemm, in one launch, for
- * M <= 64 (FGB_ERR_SHAPE above).  The kernel quantizes each 1x128 group of x right before its
- * MFMA with the same arithmetic (s = fl32(amax/448), codes E4M3(fl32(x/s))), so codes and scales
- * are those of fgb_act_quant_group128; neither is written out.  Where the two-launch path runs
- * the same kernel shape (M <= 16, or 16 < M <= 64 with N*K <= 16 MiB) the float32 result is
- * equal bit for bit; otherwise it differs only in the float32 summation order.
+ * Dynamic activation quantization and the decode GEMM in one call (Transformers "Fine-grained
+ * FP8", intro and "DeepGEMM fast path": activations quantized at run time per token in 1x128
+ * groups): the result of fgb_act_quant_group128 followed by fgb_w8a8_block_gemm, for M <= 64
+ * (FGB_ERR_SHAPE above), equal to it bit for bit in float32 and bf16.  For a few tokens (M <= 4,
+ * or M <= 8 with N*K <= 24 MiB) it is one launch of a GEMM that quantizes each 1x128 group of x
+ * right before its MFMA with the same arithmetic (s = fl32(amax/448), codes E4M3(fl32(x/s))),
+ * and the codes and scales are not written out; for more tokens the call quantizes into the
+ * workspace and runs the decode GEMM on it (repeating the quantization in every workgroup would
+ * cost more than the launch it saves).
  *   x    bf16 [M, ldx] row-major, ldx >= K (16-byte rows);
- *   w_q, s_w, s_w_fmt, y, y_dtype, ldy as for fgb_w8a8_block_gemm.  No workspace.
+ *   w_q, s_w, s_w_fmt, y, y_dtype, ldy as for fgb_w8a8_block_gemm;
+ *   workspace  device, 16-byte aligned, >= fgb_gemm_fused_quant_workspace_bytes(M, N, K) bytes
+ *              (may be NULL when that is 0; FGB_ERR_WORKSPACE if missing or too small).
  */
 int fgb_w8a8_block_gemm_fused_quant(const uint16_t* x, int64_t ldx, const uint8_t* w_q,
                                     const void* s_w, int s_w_fmt, void* y, int y_dtype, int64_t ldy,
-                                    int64_t M, int64_t N, int64_t K, void* stream);
+                                    int64_t M, int64_t N, int64_t K, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* Host query: workspace bytes fgb_grouped_w8a8_block_gemm needs (0 if none). */
 size_t fgb_grouped_gemm_workspace_bytes(int64_t total_M, int64_t N, int64_t K, int32_t E);

@@ -202,10 +202,10 @@ int main() {
   EXPECT(scaled(64, FGB_ACT_SCALE_TENSOR, FGB_W_SCALE_BLOCK128, 1, 0), FGB_OK);
   if (strcmp(g_stub.last, "scaled_decode") || g_stub.E != 1) failures++;
 
-  // the fused-quantization decode GEMM
-  auto fused = [](int64_t M, int64_t ldx, uintptr_t xp = F) {
+  // the fused-quantization decode GEMM (the stub's workspace need: 4096 bytes above 8 rows)
+  auto fused = [](int64_t M, int64_t ldx, uintptr_t xp = F, uintptr_t ws = F, size_t ws_bytes = 4096) {
     return fgb_w8a8_block_gemm_fused_quant((const uint16_t*)P(xp), ldx, (const uint8_t*)P(F), P(F), 0, P(F), 0, 512,
-                                           M, 512, 1024, nullptr);
+                                           M, 512, 1024, P(ws), ws_bytes, nullptr);
   };
   EXPECT(fused(65, 1024), FGB_ERR_SHAPE);
   EXPECT(fused(16, 1000), FGB_ERR_STRIDE);
@@ -213,8 +213,13 @@ int main() {
   EXPECT(fused(16, 1024, F + 2), FGB_ERR_ALIGN);
   EXPECT(fused(16, 1024, 0), FGB_ERR_NULL);
   EXPECT(fused(0, 1024), FGB_OK);
+  EXPECT(fused(64, 1024, F, 0, 0), FGB_ERR_WORKSPACE);
+  EXPECT(fused(64, 1024, F, F, 4095), FGB_ERR_WORKSPACE);
+  EXPECT(fused(64, 1024, F, F + 8, 4096), FGB_ERR_ALIGN);
   EXPECT(fused(64, 1024), FGB_OK);
-  if (strcmp(g_stub.last, "gemm_fused") || g_stub.M != 64) failures++;
+  if (strcmp(g_stub.last, "gemm_fused") || g_stub.M != 64 || g_stub.workspace != P(F)) failures++;
+  EXPECT(fused(4, 1024, F, 0, 0), FGB_OK);  // one launch: no workspace needed
+  if (strcmp(g_stub.last, "gemm_fused") || g_stub.M != 4) failures++;
 
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);

@@ -81,8 +81,10 @@ hipError_t launch_check_offsets(const int32_t*, int32_t, int64_t, int32_t*, hipS
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (M == 32 && N == 4096 && K == 4096) ? (size_t)g_stub.ws_bytes_query : 0;
 }
-hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t*, int64_t, hipStream_t) {
+size_t fused_workspace_bytes(int64_t M, int64_t, int64_t) { return M > 8 ? 4096 : 0; }
+hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t*, int64_t, void* ws, hipStream_t) {
   record(a);
+  g_stub.workspace = ws;
   return launched("gemm_fused");
 }
 int decode_small_waves(int64_t, int64_t) { return 8; }

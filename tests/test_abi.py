@@ -98,6 +98,25 @@ def test_gemm_validation(L):
     assert L.fgb_gemm_workspace_bytes(64, 28672, 4096) == 0
 
 
+def test_fused_quant_workspace(L):
+    """The fused-quantization decode call needs a workspace exactly where it quantizes into one
+    (more than 4 rows, or more than 8 with weights above 24 MiB); sizes are checked first."""
+    q = L.fgb_gemm_fused_quant_workspace_bytes
+    for M, N, K in [(1, 28672, 4096), (4, 7168, 18432), (8, 6144, 4096), (8, 4096, 4096)]:
+        assert q(M, N, K) == 0
+    for M, N, K in [(5, 28672, 4096), (8, 24576, 1536), (9, 4096, 4096), (64, 4096, 4096)]:
+        # at least the codes [M, K] and the scales [K/128, M] float32
+        assert q(M, N, K) >= M * K + 4 * M * (K // 128)
+    assert q(65, 4096, 4096) == 0 and q(16, 4000, 4096) == 0
+    f = L.fgb_w8a8_block_gemm_fused_quant
+    need = q(32, 4096, 4096)
+    args = lambda ws, wsb, M=32: (FAKE, 4096, FAKE, FAKE, 0, FAKE, 0, 4096, M, 4096, 4096, ws, wsb, None)
+    assert f(*args(None, 0)) == ERR["WORKSPACE"]
+    assert f(*args(FAKE, need - 1)) == ERR["WORKSPACE"]
+    assert f(*args(FAKE + 8, need)) == ERR["ALIGN"]
+    assert f(*args(None, 0, M=65)) == ERR["SHAPE"]
+
+
 def test_check_expert_offsets_validation(L):
     """The offsets check validates its arguments before any device work."""
     assert L.fgb_check_expert_offsets(FAKE, 0, 10, FAKE, None) == ERR["SHAPE"]

@@ -1,11 +1,12 @@
-"""GPU: the decode GEMM that quantizes its bf16 activations itself (fgb_w8a8_block_gemm_fused_quant)
-against the two-launch path (act_quant_group128 + w8a8_block_gemm) and the oracle, through the
-C-ABI.
+"""GPU: act_quant_group128 + w8a8_block_gemm from bf16 activations in one call
+(fgb_w8a8_block_gemm_fused_quant) against the two-launch path and the oracle, through the C-ABI.
 
-Where the two-launch path runs the same kernel shape (M <= 16, or 16 < M <= 64 with weights of
-at most 16 MiB) the float32 outputs must be equal bit for bit (same codes, scales, K split and
-summation order); elsewhere, and always, the output is held to the oracle's tolerance from the
-same bf16 inputs."""
+A few tokens run one launch whose GEMM quantizes the activations itself; more tokens quantize
+into the workspace and run the decode GEMM.  Either way the float32 and bf16 outputs must equal
+the two-launch path's bit for bit (same codes, scales, K split and summation order), and they are
+held to the oracle's tolerance from the same bf16 inputs."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -26,9 +27,13 @@ def _inputs(M, N, K, key, fmt, edge=False):
         if M > 1:
             xf[1, 128:256] *= np.float32(2.0 ** -118)     # a subnormal scale: IEEE quotient path
         x = workloads.f32_to_bf16_bits(xf)
-    w = workloads.weights(N, K, key=(3, 61, key, N))
-    wq, sw = blockquant.weight_quant(w, fmt)
+    wq, sw = _weights(N, K, key, fmt)
     return x, wq, sw
+
+
+@functools.lru_cache(maxsize=None)
+def _weights(N, K, key, fmt):
+    return blockquant.weight_quant(workloads.weights(N, K, key=(3, 61, key, N)), fmt)
 
 
 def _oracle(x, wq, sw, fmt):
@@ -36,24 +41,23 @@ def _oracle(x, wq, sw, fmt):
     return gemm.gemm_ref(aq, sa, wq, sw, fmt)
 
 
-def _same_kernel_shape(M, N, K):
-    return M <= 16 or N * K <= (16 << 20)
-
-
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 16, 17, 32, 33, 64])
-@pytest.mark.parametrize("N,K", [(512, 2048), (1024, 4096), (4096, 4608)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("N,K", [(512, 2048), (1024, 4096), (4096, 4608), (6144, 4096)])
 @pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
 def test_fused_matches_two_launch_path_and_oracle(dev, M, N, K, fmt):
     x, wq, sw = _inputs(M, N, K, key=N + K, fmt=fmt, edge=True)
     xd = to_dev_bf16(x, dev)
     wqd, swd = torch.from_numpy(wq).to(dev), torch.from_numpy(sw).to(dev)
+    one_launch = M <= 4 or (M <= 8 and N * K <= (24 << 20))
+    assert (fgb.gemm_fused_quant_workspace_bytes(M, N, K) == 0) == one_launch
     y32 = fgb.gemm_fused_quant(xd, wqd, swd, out_dtype=torch.float32)
     q, sa = fgb.quantize(xd)
     y32_two = fgb.gemm(q, sa, wqd, swd, out_dtype=torch.float32)
     y16 = fgb.gemm_fused_quant(xd, wqd, swd, out_dtype=torch.bfloat16)
+    y16_two = fgb.gemm(q, sa, wqd, swd, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    if _same_kernel_shape(M, N, K):
-        assert torch.equal(y32.view(torch.int32), y32_two.view(torch.int32))
+    assert torch.equal(y32.view(torch.int32), y32_two.view(torch.int32))
+    assert torch.equal(y16.view(torch.int16), y16_two.view(torch.int16))
     yref = _oracle(x, wq, sw, fmt)
     y32n = y32.cpu().numpy()
     check_t1(y32n, yref)
