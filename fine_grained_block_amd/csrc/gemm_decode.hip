@@ -27,8 +27,12 @@ int decode_small_waves(int64_t N, int64_t K) {
 
 namespace {
 
-// weights from this size on take the LDS-ring kernel for M <= 16
+// M <= 16: weights from this size on with long rows (K >= 8192: long slices per wave, where the
+// ring reaches its steady state) take the LDS-ring kernel, the others the register kernel.
+// Measured (graph loop): 4096x14336 at M = 16 14.7 vs 15.4 us, 7168x18432 31.5 vs 33.9 us (ring
+// ahead, equal at M <= 4); 28672x4096 at M = 1 25.0 vs 21.9 us (register kernel ahead).
 constexpr int64_t kRingMinWeightBytes = 48ll << 20;
+bool decode_ring(int64_t N, int64_t K) { return N * K >= kRingMinWeightBytes && K >= 8192; }
 
 // 16 < M <= 64 with weights of at most 16 MiB (the 4096 x 4096 projection): the per-wave ring
 // kernel (16 weight rows and the whole K per workgroup, 4 waves, 32 or 64 activation rows), one
@@ -67,7 +71,7 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream) {
-  if (a.M <= 16 && a.N * a.K >= kRingMinWeightBytes) {
+  if (a.M <= 16 && decode_ring(a.N, a.K)) {
     const int wk = small_waves(a.N, a.K);
     const dim3 grid((unsigned)(a.N / 16));
 #define FGB_RING(WK, SWF, OUT)                                                                              \

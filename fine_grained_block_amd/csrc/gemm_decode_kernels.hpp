@@ -5,8 +5,9 @@
 // for few tokens the weight stream dominates (bytes per weight: 1 for FP8, per the Baseten
 // NVFP4 summary, "Less memory, more compute"), so the kernels are organised to keep HBM busy:
 //   * M <= 16: one workgroup per 16 weight rows and the whole K, its waves splitting the
-//     K-blocks; weights >= 48 MiB stream through per-wave LDS rings with whole-line direct
-//     copies, smaller ones load the MFMA operand layout straight into registers.  One launch.
+//     K-blocks; weights >= 48 MiB with K >= 8192 stream through per-wave LDS rings with
+//     whole-line direct copies, the others load whole lines into registers and reorder them
+//     through LDS.  One launch.
 //   * 16 < M <= 64, weights of at most 16 MiB: the per-wave ring kernel with 32 or 64 activation
 //     rows, one launch.
 //   * 16 < M <= 64, larger weights: a workgroup of 8 waves per 128-row weight block over a K slice, weights,
@@ -718,14 +719,22 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
 // ---------------------------------------------------------------------------------------------
 // M <= 16: one workgroup per 16 weight rows and the whole K, its WK waves splitting the K-blocks
 // (contiguous slices) and adding their 16x16 partial tiles through LDS in wave order.  No
-// workspace, one launch; the activation fragments come straight from L2 (the whole activation
-// is at most 16 rows).
+// workspace, one launch.  Each K-block's 16 x 128-byte weight tile is loaded as whole lines (lane
+// l: row l/8 and row l/8 + 8, bytes 16 (l%8) .. +15; each load instruction covers 8 full lines)
+// two blocks per register chunk, two chunks in flight, and reordered into the MFMA operand
+// layout through a per-wave LDS tile (two 16-byte writes and two reads per lane per block).
+// Loaded straight in the operand layout (16 rows x 32 bytes per lane group) every instruction
+// touched 16 half-used lines and cost ~4x the address-unit time per byte; measured (graph loop)
+// 6144x4096 at M = 8 9.1 -> 7.6 us, 24576x1536 10.0 -> 8.5 us, and the 28672x4096 weight, which
+// used to take the LDS-ring kernel, 25.0 -> 21.9 us at M = 1.  The activation fragments come
+// straight from L2 (the whole activation is at most 16 rows).
 // ---------------------------------------------------------------------------------------------
-constexpr int CHS = 2;  // K-blocks per register chunk in the small-M kernel (~100 VGPRs)
+constexpr int CHS = 2;  // K-blocks per register chunk in the small-M kernel (4: no faster)
 
 template <int WK, int SWF, int OUT>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) {
   __shared__ v4f red[WK > 1 ? WK - 1 : 1][64];
+  __shared__ __attribute__((aligned(1024))) uint8_t tile[WK][CHS][16 * 128];  // per wave, per block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t K = p.K, M = p.M;
   const int KB = (int)(K / 128);
@@ -734,12 +743,16 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
   const int nk = min(KB, kb0 + per) - kb0;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t nb = n0 / 128;
-  const int g = lane >> 4;
-  const int64_t m = (lane & 15) < M ? (lane & 15) : M - 1;  // rows past M repeat row M-1
-  const uint8_t* wrow = p.w_q + (n0 + (lane & 15)) * K + (int64_t)kb0 * 128 + 32 * g;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t m = r < M ? r : M - 1;  // rows past M repeat row M-1
+  const uint8_t* wline = p.w_q + (n0 + (lane >> 3)) * K + (int64_t)kb0 * 128 + 16 * (lane & 7);
   const uint8_t* arow = p.a_q + m * p.lda + (int64_t)kb0 * 128 + 32 * g;
   const float* sarow = p.s_a + (int64_t)kb0 * p.ld_sa + m;
   const int64_t swbase = nb * KB + kb0;
+  // LDS tile offsets: whole-line writes (rows l/8 and l/8 + 8, chunk l%8), operand-layout reads
+  // (row l%16, logical chunks 2g and 2g+1), both through the conflict-free swizzle
+  const int wo0 = swz(lane >> 3, lane & 7), wo1 = swz((lane >> 3) + 8, lane & 7);
+  const int ro0 = swz(r, 2 * g), ro1 = swz(r, 2 * g + 1);
 
   int4 wv[2][CHS][2], av[2][CHS][2];
   float sav[2][CHS], swv[2][CHS];
@@ -748,8 +761,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
     for (int u = 0; u < CHS; ++u) {
       if (c + u < nk) {
         const int64_t off = (int64_t)(c + u) * 128;
-        wv[buf][u][0] = gload_i4(wrow + off);
-        wv[buf][u][1] = gload_i4(wrow + off + 16);
+        wv[buf][u][0] = gload_i4(wline + off);
+        wv[buf][u][1] = gload_i4(wline + 8 * K + off);
         av[buf][u][0] = gload_i4(arow + off);
         av[buf][u][1] = gload_i4(arow + off + 16);
         sav[buf][u] = gload<float>(sarow + (int64_t)(c + u) * p.ld_sa);
@@ -762,9 +775,16 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
 #pragma unroll
     for (int u = 0; u < CHS; ++u) {
       if (c + u < nk) {
+        // (one wave's LDS operations complete in order: the reads see the writes, and the next
+        // chunk's writes to this tile follow these reads)
+        uint8_t* t = &tile[wave][u][0];
+        *reinterpret_cast<int4*>(t + wo0) = wv[buf][u][0];
+        *reinterpret_cast<int4*>(t + wo1) = wv[buf][u][1];
+        const int4 lo = *reinterpret_cast<const int4*>(t + ro0);
+        const int4 hi = *reinterpret_cast<const int4*>(t + ro1);
         v8i af, bf;
-        af[0] = wv[buf][u][0].x; af[1] = wv[buf][u][0].y; af[2] = wv[buf][u][0].z; af[3] = wv[buf][u][0].w;
-        af[4] = wv[buf][u][1].x; af[5] = wv[buf][u][1].y; af[6] = wv[buf][u][1].z; af[7] = wv[buf][u][1].w;
+        af[0] = lo.x; af[1] = lo.y; af[2] = lo.z; af[3] = lo.w;
+        af[4] = hi.x; af[5] = hi.y; af[6] = hi.z; af[7] = hi.w;
         bf[0] = av[buf][u][0].x; bf[1] = av[buf][u][0].y; bf[2] = av[buf][u][0].z; bf[3] = av[buf][u][0].w;
         bf[4] = av[buf][u][1].x; bf[5] = av[buf][u][1].y; bf[6] = av[buf][u][1].z; bf[7] = av[buf][u][1].w;
         const float sc = sav[buf][u] * swv[buf][u];
@@ -788,7 +808,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
 #pragma unroll
     for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
   }
-  if ((lane & 15) < M) store4<OUT>(p.y, p.ldy, lane & 15, n0 + 4 * g, acc);
+  if (r < M) store4<OUT>(p.y, p.ldy, r, n0 + 4 * g, acc);
 }
 
 }  // namespace

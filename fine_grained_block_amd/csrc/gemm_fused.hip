@@ -3,20 +3,21 @@
 //
 // Few tokens: one launch of the GEMM that quantizes its activations itself
 // (gemm_decode_fused_quant_small_kernel).  Every workgroup quantizes the rows it multiplies, so
-// the quantization is repeated N/16 times; measured against act_quant + GEMM (graph loop, the six
-// decode shapes from 4096x4096 to 7168x18432), the one launch is faster up to 4 rows on every
-// shape (e.g. 4096x4096 6.9 vs 9.2 us, 28672x4096 25.7 vs 28.6 us at M = 4) and up to 8 rows
-// only for weights of at most 24 MiB; from 12 rows on the repeated quantization costs more than
-// the launch it saves (28672x4096 at M = 64: 239 vs 33 us).  Beyond those sizes the call
-// quantizes into the caller's workspace and runs the decode GEMM on it: the same kernels as the
-// two calls, so the same bits.
+// the quantization is repeated N/16 times.  Measured against act_quant + GEMM (graph loop, the six
+// decode shapes from 4096x4096 to 7168x18432, M = 1 ... 64): the one launch is faster up to 4
+// rows where K >= 4096 (4096x4096 6.6-7.0 vs 8.6-9.0 us, 4096x14336 13.2-13.9 vs 15.5-15.9 us)
+// and up to 8 rows for weights of at most 16 MiB (4096x4096 8.2 vs 9.3 us at M = 8); with short
+// rows (24576x1536) or more rows the separate quantization costs less (6144x4096 at M = 8 11.5 vs
+// 10.9 us; 28672x4096 at M = 64 239 vs 33 us with an earlier 16-64-row fused kernel).  Beyond
+// those sizes the call quantizes into the caller's workspace and runs the decode GEMM on it: the
+// same kernels as the two calls, so the same bits.
 #include "gemm_decode_kernels.hpp"
 
 namespace fgb {
 
 namespace {
 
-bool one_launch(int64_t M, int64_t N, int64_t K) { return M <= 4 || (M <= 8 && N * K <= (24ll << 20)); }
+bool one_launch(int64_t M, int64_t N, int64_t K) { return (M <= 4 && K >= 4096) || (M <= 8 && N * K <= (16ll << 20)); }
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 

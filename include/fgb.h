@@ -151,8 +151,8 @@ size_t fgb_gemm_fused_quant_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Dynamic activation quantization and the decode GEMM in one call (Transformers "Fine-grained
  * FP8", intro and "DeepGEMM fast path": activations quantized at run time per token in 1x128
  * groups): the result of fgb_act_quant_group128 followed by fgb_w8a8_block_gemm, for M <= 64
- * (FGB_ERR_SHAPE above), equal to it bit for bit in float32 and bf16.  For a few tokens (M <= 4,
- * or M <= 8 with N*K <= 24 MiB) it is one launch of a GEMM that quantizes each 1x128 group of x
+ * (FGB_ERR_SHAPE above), equal to it bit for bit in float32 and bf16.  For a few tokens (M <= 4
+ * with K >= 4096, or M <= 8 with N*K <= 16 MiB) it is one launch of a GEMM that quantizes each 1x128 group of x
  * right before its MFMA with the same arithmetic (s = fl32(amax/448), codes E4M3(fl32(x/s))),
  * and the codes and scales are not written out; for more tokens the call quantizes into the
  * workspace and runs the decode GEMM on it (repeating the quantization in every workgroup would

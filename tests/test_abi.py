@@ -100,11 +100,12 @@ def test_gemm_validation(L):
 
 def test_fused_quant_workspace(L):
     """The fused-quantization decode call needs a workspace exactly where it quantizes into one
-    (more than 4 rows, or more than 8 with weights above 24 MiB); sizes are checked first."""
+    (one launch only for M <= 4 with K >= 4096 or M <= 8 with weights of at most 16 MiB); sizes
+    are checked first."""
     q = L.fgb_gemm_fused_quant_workspace_bytes
-    for M, N, K in [(1, 28672, 4096), (4, 7168, 18432), (8, 6144, 4096), (8, 4096, 4096)]:
+    for M, N, K in [(1, 28672, 4096), (4, 7168, 18432), (8, 4096, 4096), (8, 1024, 2048)]:
         assert q(M, N, K) == 0
-    for M, N, K in [(5, 28672, 4096), (8, 24576, 1536), (9, 4096, 4096), (64, 4096, 4096)]:
+    for M, N, K in [(5, 28672, 4096), (1, 24576, 1536), (8, 6144, 4096), (9, 4096, 4096), (64, 4096, 4096)]:
         # at least the codes [M, K] and the scales [K/128, M] float32
         assert q(M, N, K) >= M * K + 4 * M * (K // 128)
     assert q(65, 4096, 4096) == 0 and q(16, 4000, 4096) == 0

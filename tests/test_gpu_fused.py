@@ -42,13 +42,13 @@ def _oracle(x, wq, sw, fmt):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64])
-@pytest.mark.parametrize("N,K", [(512, 2048), (1024, 4096), (4096, 4608), (6144, 4096)])
+@pytest.mark.parametrize("N,K", [(512, 2048), (1024, 4096), (4096, 4608), (4096, 4096), (12288, 1536)])
 @pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
 def test_fused_matches_two_launch_path_and_oracle(dev, M, N, K, fmt):
     x, wq, sw = _inputs(M, N, K, key=N + K, fmt=fmt, edge=True)
     xd = to_dev_bf16(x, dev)
     wqd, swd = torch.from_numpy(wq).to(dev), torch.from_numpy(sw).to(dev)
-    one_launch = M <= 4 or (M <= 8 and N * K <= (24 << 20))
+    one_launch = (M <= 4 and K >= 4096) or (M <= 8 and N * K <= (16 << 20))
     assert (fgb.gemm_fused_quant_workspace_bytes(M, N, K) == 0) == one_launch
     y32 = fgb.gemm_fused_quant(xd, wqd, swd, out_dtype=torch.float32)
     q, sa = fgb.quantize(xd)

@@ -147,8 +147,8 @@ _RING_W = {}
 
 
 def _ring_weights(fmt):
-    """A 2048 x 24576 weight (exactly 48 MiB of codes, the size from which M <= 16 calls take the
-    LDS-ring decode kernel): random finite E4M3 codes and random block scales."""
+    """A 2048 x 24576 weight (exactly 48 MiB of codes with K >= 8192, from which M <= 16 calls take
+    the LDS-ring decode kernel): random finite E4M3 codes and random block scales."""
     if fmt not in _RING_W:
         N, K = 2048, 24576
         rng = np.random.default_rng(77)
@@ -289,8 +289,9 @@ def test_repeated_runs_are_bitwise_identical(dev):
     differences.  Each shape runs six times with the caches flushed before every other run:
     256x256 and 256x128 prefill tiles, the persistent 256x256 form (bf16 output, two tiles per
     workgroup), the 128x128 tile (N % 256 != 0), the decode ring kernel
-    (M <= 16, 48 MiB of weights), the 16 < M <= 64 kernel with a K slicing and its reduction, and
-    the grouped GEMM."""
+    (M <= 16, 48 MiB of weights with K >= 8192), the M <= 16 register kernel with its per-wave LDS
+    reorder (small and large weights), the 16 < M <= 64 kernel with a K slicing and its
+    reduction, and the grouped GEMM."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(11)
@@ -302,7 +303,8 @@ def test_repeated_runs_are_bitwise_identical(dev):
     def scales(shape):
         return torch.rand(shape, generator=gen, device=dev) * (2.0 / 448) + 0.25 / 448
 
-    cases = [(4096, 4096, 2048), (4096, 6144, 4096), (1024, 1152, 1024), (8, 2048, 24576), (48, 1024, 3200)]
+    cases = [(4096, 4096, 2048), (4096, 6144, 4096), (1024, 1152, 1024), (8, 2048, 24576), (48, 1024, 3200),
+             (4, 6144, 4096), (16, 28672, 4096)]
     for (M, N, K) in cases:
         aq, sa = codes((M, K)), scales((K // 128, M))
         wq, sw = codes((N, K)), scales((N // 128, K // 128))
