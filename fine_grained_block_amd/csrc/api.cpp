@@ -297,7 +297,7 @@ int fgb_grouped_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
   fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, total_M, N, K,
                   expert_offsets, E};
   // at most 64 rows in all (decode-shaped routing): the weight-streaming kernel per expert
-  if (total_M <= 64) return launch_status(fgb::launch_gemm_moe_decode(a, 1, total_M, (hipStream_t)stream));
+  if (total_M <= 64) return launch_status(fgb::launch_gemm_moe_decode(a, 1, (hipStream_t)stream));
   return launch_status(fgb::launch_gemm_grouped(a, (hipStream_t)stream));
 }
 
@@ -317,7 +317,7 @@ int fgb_batched_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_
   st = check_device();
   if (st != FGB_OK) return st;
   fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, rows, N, K, counts, E, 0, max_M};
-  if (max_M <= 64) return launch_status(fgb::launch_gemm_moe_decode(a, 2, max_M, (hipStream_t)stream));
+  if (max_M <= 64) return launch_status(fgb::launch_gemm_moe_decode(a, 2, (hipStream_t)stream));
   return launch_status(fgb::launch_gemm_grouped(a, (hipStream_t)stream));
 }
 

@@ -163,44 +163,38 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
 }
 
 // ---------------------------------------------------------------------------------------------
-// MoE with at most 64 rows per expert (decode-shaped routing): the per-wave ring kernel with
-// grid.y = expert; 4 waves split K; mode 1 reads the contiguous grouped layout's offsets, mode 2
-// the masked batched layout's counts (slot = rows per expert slot).
+// MoE with at most 64 rows per expert (decode-shaped routing): the M <= 16 register kernel with
+// grid.y = expert, 4 waves splitting K, one workgroup per (16 weight rows, expert) walking the
+// expert's rows in passes of 16; mode 1 reads the contiguous grouped layout's offsets, mode 2 the
+// masked batched layout's counts (slot = rows per expert slot).
+//
+// Measured (32 experts, graph loop, gate+up 4096x7168 / down 7168x2048): against the per-wave LDS
+// ring kernel with 8 or 16 staged rows (the same K split, so the same bits) top-8 routing of 1
+// token 41.9 -> 40.9 / 28.8 -> 22.5 us, of 8 tokens 136.5 -> 130.7 / 96.8 -> 66.8 us, 64-row
+// batched slots for 64 tokens 236 -> 230 / 159 -> 119 us: down's 16 K-blocks give each wave 4,
+// too few for a ring to fill.  Passes inside the workgroup rather than one workgroup per chunk
+// of rows: the grid then holds no workgroups without rows, which hold a CU slot for the latency
+// of their count load (ring kernel: 143 -> 136 and 109 -> 96 us at 8 tokens).
 // ---------------------------------------------------------------------------------------------
 namespace {
 
-template <int MR, int D, int MODE>
-void launch_moe_rows(const GemmArgs& a, hipStream_t stream) {
+template <int MODE>
+void launch_moe(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.N / 16), (unsigned)a.E), block(256);
   if (a.s_w_fmt == 0) {
-    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 0, 0, 0, 0, MODE>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 0, 1, 0, 0, MODE>), grid, block, 0, stream, a);
+    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_small_kernel<4, 0, 0, MODE>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_decode_small_kernel<4, 0, 1, MODE>), grid, block, 0, stream, a);
   } else {
-    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 1, 0, 0, 0, MODE>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_decode_ring_kernel<4, MR, D, 1, 1, 0, 0, MODE>), grid, block, 0, stream, a);
+    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_small_kernel<4, 1, 0, MODE>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_decode_small_kernel<4, 1, 1, MODE>), grid, block, 0, stream, a);
   }
-}
-
-// 8 or 16 staged rows per workgroup; one workgroup per (16 weight rows, expert) walks the
-// expert's rows in passes of that many.  With few rows per expert (top-k routing of a few tokens)
-// the ring stays 5 or 4 blocks deep, where 32 staged rows leave room for 3 (measured slower on
-// every case below).  Passes inside the workgroup rather than one workgroup per chunk of rows:
-// the grid then holds no workgroups without rows, which hold a CU slot for the latency of their
-// count load, and a second pass re-reads a weight tile its CU has just streamed.  Measured, 32
-// experts, gate+up 4096x7168 / down 7168x2048, graph loop: top-8 routing of 1 token 44.3 -> 41.8
-// / 33.1 -> 29.1 us, of 8 tokens (64 rows) 143 -> 136 / 109 -> 96 us; 64-row batched slots for 64
-// tokens 274 -> 242 / 190 -> 160 us.
-template <int MODE>
-void launch_moe_mr(const GemmArgs& a, int64_t rows_per_expert, hipStream_t stream) {
-  if (rows_per_expert <= 8) launch_moe_rows<8, 5, MODE>(a, stream);
-  else launch_moe_rows<16, 4, MODE>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, int64_t rows_per_expert, hipStream_t stream) {
-  if (mode == 1) launch_moe_mr<1>(a, rows_per_expert, stream);
-  else launch_moe_mr<2>(a, rows_per_expert, stream);
+hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, hipStream_t stream) {
+  if (mode == 1) launch_moe<1>(a, stream);
+  else launch_moe<2>(a, stream);
   return hipGetLastError();
 }
 

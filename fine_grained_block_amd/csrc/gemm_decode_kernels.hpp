@@ -83,14 +83,9 @@ __device__ __forceinline__ int swz_g(int row) { return (row & 7) ^ ((row >> 3) &
 // per-channel weight scales and per-token or per-tensor activation scales, both in the epilogue
 // (the MFMAs accumulate in place).  CODE 1: E5M2 operands (schemes 1 and 2).
 //
-// MODE (MoE, grid.y = expert e, 1x128-group scheme): 1 = the expert's rows are offsets[e] ..
-// offsets[e+1]-1 of the contiguous grouped layout; 2 = rows e*slot .. e*slot + counts[e] - 1 of
-// the masked batched layout.  A workgroup of an expert without rows exits at once, so only the
-// routed experts' weights are read.
-template <int WK, int MR, int D, int SWF, int OUT, int SCH = 0, int CODE = 0, int MODE = 0>
+template <int WK, int MR, int D, int SWF, int OUT, int SCH = 0, int CODE = 0>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
   static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
-  static_assert(MODE == 0 || SCH == 0, "MoE layouts use the 1x128-group scheme");
   constexpr int MT = MR >= 16 ? MR / 16 : 1;  // token tiles per wave
   constexpr int WST = 16 * 128, AST = MR * 128, SST = 64 * 4;
   constexpr int STAGE = WST + AST + SST;
@@ -102,22 +97,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t K = p.K;
-  // this workgroup's rows: row_base .. r_end - 1 (MoE: the expert's rows, in passes of MR)
-  int64_t row_base = 0, r_end = p.M, ex = 0;
-  if constexpr (MODE != 0) {
-    ex = blockIdx.y;
-    int64_t r0, r1;
-    if constexpr (MODE == 1) {  // (offsets are a precondition; clamped to 0..total rows)
-      r0 = min(max((int64_t)gload<int>(p.offsets + ex), (int64_t)0), p.M);
-      r1 = min(max((int64_t)gload<int>(p.offsets + ex + 1), r0), p.M);
-    } else {
-      r0 = ex * p.slot;
-      r1 = r0 + min(max((int64_t)gload<int>(p.offsets + ex), (int64_t)0), p.slot);
-    }
-    row_base = __builtin_amdgcn_readfirstlane((int)r0);
-    r_end = __builtin_amdgcn_readfirstlane((int)r1);
-    if (r_end <= row_base) return;
-  }
+  const int64_t M = p.M;
   const int KB = (int)(K / 128);
   const int per = (KB + WK - 1) / WK;
   const int kb0 = min(KB, wave * per);
@@ -129,7 +109,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
   // weight-block scales of this wave's slice, lane l holding block kb0 + l + 64 t (K <= 32768)
   float sw0 = 0.0f, sw1 = 0.0f, sw2 = 0.0f, sw3 = 0.0f;
   if constexpr (SCH != 2) {
-    const int64_t b = (ex * (p.N / 128) + nb) * KB + kb0;
+    const int64_t b = nb * KB + kb0;
     sw0 = lane < nk ? load_sw<SWF>(p.s_w, b + lane) : 0.0f;
     sw1 = lane + 64 < nk ? load_sw<SWF>(p.s_w, b + lane + 64) : 0.0f;
     sw2 = lane + 128 < nk ? load_sw<SWF>(p.s_w, b + lane + 128) : 0.0f;
@@ -152,192 +132,175 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_ring_kernel(GemmArgs p) {
     const int r = 8 * q + (lane >> 3);
     woff[q] = (uint32_t)(r * K + (((lane & 7) ^ swz_g(r)) * 16));
   }
-  const uint8_t* wbase = p.w_q + (ex * p.N + n0) * K;
+  const uint8_t* wbase = p.w_q + n0 * K;
 
-  // One pass over the rows row_base .. row_base + M - 1 (M <= MR).
-  auto pass = [&](const int64_t row_base, const int64_t M) {
-    uint32_t aoff[MR / 8];
+  uint32_t aoff[MR / 8];
+#pragma unroll
+  for (int q = 0; q < MR / 8; ++q) {
+    const int r = 8 * q + (lane >> 3);
+    const int64_t m = r < M ? r : M - 1;
+    aoff[q] = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
+  }
+  const uint32_t soff = (uint32_t)((lane < M ? lane : M - 1) * 4);
+
+  // 8-row activation copy groups that hold real rows (the others would only repeat row M-1 into
+  // rows whose outputs are not stored): fewer copies where M is below the staged rows
+  const int agrp = (int)min((int64_t)(MR / 8), (M + 7) / 8);
+  auto issue = [&](int kk) {
+    uint8_t* st = wring + (kk % D) * STAGE;
+    const int64_t kb = kb0 + kk;
+    const uint8_t* wb = wbase + kb * 128;
+    const uint8_t* ab = p.a_q + kb * 128;
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(p.s_a + kb * p.ld_sa);
+    asm volatile("" : "+s"(wb));
+    asm volatile("" : "+s"(ab));
+    asm volatile("" : "+s"(sb));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t o = woff[q];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(GPTR(wb + o), LPTR(st + q * 1024), 16, 0, 0);
+    }
 #pragma unroll
     for (int q = 0; q < MR / 8; ++q) {
-      const int r = 8 * q + (lane >> 3);
-      const int64_t m = row_base + (r < M ? r : M - 1);
-      aoff[q] = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
-    }
-    const uint32_t soff = (uint32_t)((row_base + (lane < M ? lane : M - 1)) * 4);
-
-    // 8-row activation copy groups that hold real rows (the others would only repeat row M-1 into
-    // rows whose outputs are not stored): fewer copies where M is below the staged rows
-    const int agrp = (int)min((int64_t)(MR / 8), (M + 7) / 8);
-    auto issue = [&](int kk) {
-      uint8_t* st = wring + (kk % D) * STAGE;
-      const int64_t kb = kb0 + kk;
-      const uint8_t* wb = wbase + kb * 128;
-      const uint8_t* ab = p.a_q + kb * 128;
-      const uint8_t* sb = reinterpret_cast<const uint8_t*>(p.s_a + kb * p.ld_sa);
-      asm volatile("" : "+s"(wb));
-      asm volatile("" : "+s"(ab));
-      asm volatile("" : "+s"(sb));
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        uint32_t o = woff[q];
+      if (q < agrp) {
+        uint32_t o = aoff[q];
         asm volatile("" : "+v"(o));
-        __builtin_amdgcn_global_load_lds(GPTR(wb + o), LPTR(st + q * 1024), 16, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < MR / 8; ++q) {
-        if (q < agrp) {
-          uint32_t o = aoff[q];
-          asm volatile("" : "+v"(o));
-          __builtin_amdgcn_global_load_lds(GPTR(ab + o), LPTR(st + WST + q * 1024), 16, 0, 0);
-        }
-      }
-      if constexpr (SCH == 0) {
-        uint32_t o = soff;
-        asm volatile("" : "+v"(o));
-        __builtin_amdgcn_global_load_lds(GPTR(sb + o), LPTR(st + WST + AST), 4, 0, 0);
-      }
-    };
-
-    v4f acc[MT];
-#pragma unroll
-    for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    if (nk > 0) {
-#pragma unroll
-      for (int i = 0; i < D - 1; ++i) issue(min(i, nk - 1));
-      for (int kk = 0; kk < nk; ++kk) {
-        // refill the stage consumed one block ago (clamped past the slice: never a pending stage)
-        issue(min(kk + D - 1, nk - 1));
-        // own copies of this block landed, the D-1 younger stages' may stay in flight
-        // (2 + agrp + 1 copies per stage; the wait count is an immediate, hence the cases)
-        {
-          constexpr int FIX = OPS - MR / 8;
-          if (agrp == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + 1)>());
-          else if (agrp == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 16 ? 2 : 1))>());
-          else if (agrp == 3) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 32 ? 3 : 1))>());
-          else if (agrp == 4) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 32 ? 4 : 1))>());
-          else if (agrp == 5) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 5 : 1))>());
-          else if (agrp == 6) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 6 : 1))>());
-          else if (agrp == 7) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 7 : 1))>());
-          else __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * OPS>());
-        }
-        // The LDS reads are written as one asm block that also waits for them: the compiler cannot
-        // tell this wave's ring stages apart and would otherwise wait for every copy in flight.
-        const uint32_t st = (uint32_t)(uintptr_t)LPTR(wring + (kk % D) * STAGE);
-        const int r = lane & 15, g = lane >> 4;
-        const uint32_t aw0 = st + swz(r, 2 * g), aw1 = st + swz(r, 2 * g + 1);
-        const int ra = r & (MR - 1);
-        const uint32_t aa0 = st + WST + swz(ra, 2 * g), aa1 = st + WST + swz(ra, 2 * g + 1);
-        const uint32_t as = st + WST + AST + 4 * r;
-        v4i w0, w1, a0[MT], a1[MT];
-        float sa[MT];
-        if constexpr (MT == 1) {
-          asm volatile(
-              "ds_read_b128 %0, %5\n\t"
-              "ds_read_b128 %1, %6\n\t"
-              "ds_read_b128 %2, %7\n\t"
-              "ds_read_b128 %3, %8\n\t"
-              "ds_read_b32 %4, %9\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(sa[0])
-              : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
-              : "memory");
-        } else if constexpr (MT == 2) {
-          asm volatile(
-              "ds_read_b128 %0, %8\n\t"
-              "ds_read_b128 %1, %9\n\t"
-              "ds_read_b128 %2, %10\n\t"
-              "ds_read_b128 %3, %11\n\t"
-              "ds_read_b128 %4, %10 offset:2048\n\t"
-              "ds_read_b128 %5, %11 offset:2048\n\t"
-              "ds_read_b32 %6, %12\n\t"
-              "ds_read_b32 %7, %12 offset:64\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(a0[1]), "=&v"(a1[1]), "=&v"(sa[0]),
-                "=&v"(sa[1])
-              : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
-              : "memory");
-        } else {
-          asm volatile(
-              "ds_read_b128 %0, %14\n\t"
-              "ds_read_b128 %1, %15\n\t"
-              "ds_read_b128 %2, %16\n\t"
-              "ds_read_b128 %3, %17\n\t"
-              "ds_read_b128 %4, %16 offset:2048\n\t"
-              "ds_read_b128 %5, %17 offset:2048\n\t"
-              "ds_read_b128 %6, %16 offset:4096\n\t"
-              "ds_read_b128 %7, %17 offset:4096\n\t"
-              "ds_read_b128 %8, %16 offset:6144\n\t"
-              "ds_read_b128 %9, %17 offset:6144\n\t"
-              "ds_read_b32 %10, %18\n\t"
-              "ds_read_b32 %11, %18 offset:64\n\t"
-              "ds_read_b32 %12, %18 offset:128\n\t"
-              "ds_read_b32 %13, %18 offset:192\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(a0[1]), "=&v"(a1[1]), "=&v"(a0[2]),
-                "=&v"(a1[2]), "=&v"(a0[3]), "=&v"(a1[3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3])
-              : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
-              : "memory");
-        }
-        v8i wf;
-        wf[0] = w0[0]; wf[1] = w0[1]; wf[2] = w0[2]; wf[3] = w0[3];
-        wf[4] = w1[0]; wf[5] = w1[1]; wf[6] = w1[2]; wf[7] = w1[3];
-        // (schemes 1 and 2 copy no activation scales: their sa reads see stale bytes, unused)
-        const float sw = SCH == 2 ? 0.0f : sw_at(kk);
-#pragma unroll
-        for (int j = 0; j < MT; ++j) {
-          v8i af;
-          af[0] = a0[j][0]; af[1] = a0[j][1]; af[2] = a0[j][2]; af[3] = a0[j][3];
-          af[4] = a1[j][0]; af[5] = a1[j][1]; af[6] = a1[j][2]; af[7] = a1[j][3];
-          if constexpr (SCH == 0) acc[j] += mfma_e4m3_16x16x128(wf, af) * (sa[j] * sw);
-          else if constexpr (SCH == 1) acc[j] += mfma_f8_16x16x128<CODE>(wf, af, v4f{0.0f, 0.0f, 0.0f, 0.0f}) * sw;
-          else acc[j] = mfma_f8_16x16x128<CODE>(wf, af, acc[j]);
-        }
+        __builtin_amdgcn_global_load_lds(GPTR(ab + o), LPTR(st + WST + q * 1024), 16, 0, 0);
       }
     }
-    // the clamped copies past the slice must land before the ring is reused or released
-    __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
-    auto store_rows = [&]() {
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        const int m = 16 * j + (lane & 15);
-        if (m < M) {
-          if constexpr (SCH != 0) {
-            // scales that do not vary along K: the token's (or the tensor's), then the channels'
-            acc[j] = acc[j] * gload<float>(p.s_a + (p.a_kind == 2 ? 0 : m));
-            if constexpr (SCH == 2) acc[j] = acc[j] * gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n0 + 4 * (lane >> 4));
-          }
-          store4<OUT>(p.y, p.ldy, row_base + m, n0 + 4 * (lane >> 4), acc[j]);
-        }
-      }
-    };
-    if constexpr (WK > 1) {
-      if (wave > 0) {
-#pragma unroll
-        for (int j = 0; j < MT; ++j) red[wave - 1][j][lane] = acc[j];
-      }
-      __syncthreads();
-      if constexpr (MODE == 0) {
-        if (wave > 0) return;
-      }
-      if (wave == 0) {
-#pragma unroll
-        for (int w = 0; w < WK - 1; ++w)
-#pragma unroll
-          for (int j = 0; j < MT; ++j) acc[j] += red[w][j][lane];
-        store_rows();
-      }
-      if constexpr (MODE != 0) __syncthreads();  // the next pass rewrites red
-    } else {
-      store_rows();
+    if constexpr (SCH == 0) {
+      uint32_t o = soff;
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(GPTR(sb + o), LPTR(st + WST + AST), 4, 0, 0);
     }
   };
-  if constexpr (MODE == 0) {
-    pass(0, p.M);
-  } else {
-    // an expert's rows in passes of MR: the passes after the first find the weight tile they
-    // stream again mostly still in the caches
-    for (int64_t rb = row_base; rb < r_end; rb += MR) pass(rb, min((int64_t)MR, r_end - rb));
+
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) issue(min(i, nk - 1));
+    for (int kk = 0; kk < nk; ++kk) {
+      // refill the stage consumed one block ago (clamped past the slice: never a pending stage)
+      issue(min(kk + D - 1, nk - 1));
+      // own copies of this block landed, the D-1 younger stages' may stay in flight
+      // (2 + agrp + 1 copies per stage; the wait count is an immediate, hence the cases)
+      {
+        constexpr int FIX = OPS - MR / 8;
+        if (agrp == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + 1)>());
+        else if (agrp == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 16 ? 2 : 1))>());
+        else if (agrp == 3) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 32 ? 3 : 1))>());
+        else if (agrp == 4) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 32 ? 4 : 1))>());
+        else if (agrp == 5) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 5 : 1))>());
+        else if (agrp == 6) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 6 : 1))>());
+        else if (agrp == 7) __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * (FIX + (MR >= 64 ? 7 : 1))>());
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only<(D - 1) * OPS>());
+      }
+      // The LDS reads are written as one asm block that also waits for them: the compiler cannot
+      // tell this wave's ring stages apart and would otherwise wait for every copy in flight.
+      const uint32_t st = (uint32_t)(uintptr_t)LPTR(wring + (kk % D) * STAGE);
+      const int r = lane & 15, g = lane >> 4;
+      const uint32_t aw0 = st + swz(r, 2 * g), aw1 = st + swz(r, 2 * g + 1);
+      const int ra = r & (MR - 1);
+      const uint32_t aa0 = st + WST + swz(ra, 2 * g), aa1 = st + WST + swz(ra, 2 * g + 1);
+      const uint32_t as = st + WST + AST + 4 * r;
+      v4i w0, w1, a0[MT], a1[MT];
+      float sa[MT];
+      if constexpr (MT == 1) {
+        asm volatile(
+            "ds_read_b128 %0, %5\n\t"
+            "ds_read_b128 %1, %6\n\t"
+            "ds_read_b128 %2, %7\n\t"
+            "ds_read_b128 %3, %8\n\t"
+            "ds_read_b32 %4, %9\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(sa[0])
+            : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
+            : "memory");
+      } else if constexpr (MT == 2) {
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %9\n\t"
+            "ds_read_b128 %2, %10\n\t"
+            "ds_read_b128 %3, %11\n\t"
+            "ds_read_b128 %4, %10 offset:2048\n\t"
+            "ds_read_b128 %5, %11 offset:2048\n\t"
+            "ds_read_b32 %6, %12\n\t"
+            "ds_read_b32 %7, %12 offset:64\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(a0[1]), "=&v"(a1[1]), "=&v"(sa[0]),
+              "=&v"(sa[1])
+            : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
+            : "memory");
+      } else {
+        asm volatile(
+            "ds_read_b128 %0, %14\n\t"
+            "ds_read_b128 %1, %15\n\t"
+            "ds_read_b128 %2, %16\n\t"
+            "ds_read_b128 %3, %17\n\t"
+            "ds_read_b128 %4, %16 offset:2048\n\t"
+            "ds_read_b128 %5, %17 offset:2048\n\t"
+            "ds_read_b128 %6, %16 offset:4096\n\t"
+            "ds_read_b128 %7, %17 offset:4096\n\t"
+            "ds_read_b128 %8, %16 offset:6144\n\t"
+            "ds_read_b128 %9, %17 offset:6144\n\t"
+            "ds_read_b32 %10, %18\n\t"
+            "ds_read_b32 %11, %18 offset:64\n\t"
+            "ds_read_b32 %12, %18 offset:128\n\t"
+            "ds_read_b32 %13, %18 offset:192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w0), "=&v"(w1), "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(a0[1]), "=&v"(a1[1]), "=&v"(a0[2]),
+              "=&v"(a1[2]), "=&v"(a0[3]), "=&v"(a1[3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3])
+            : "v"(aw0), "v"(aw1), "v"(aa0), "v"(aa1), "v"(as)
+            : "memory");
+      }
+      v8i wf;
+      wf[0] = w0[0]; wf[1] = w0[1]; wf[2] = w0[2]; wf[3] = w0[3];
+      wf[4] = w1[0]; wf[5] = w1[1]; wf[6] = w1[2]; wf[7] = w1[3];
+      // (schemes 1 and 2 copy no activation scales: their sa reads see stale bytes, unused)
+      const float sw = SCH == 2 ? 0.0f : sw_at(kk);
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        v8i af;
+        af[0] = a0[j][0]; af[1] = a0[j][1]; af[2] = a0[j][2]; af[3] = a0[j][3];
+        af[4] = a1[j][0]; af[5] = a1[j][1]; af[6] = a1[j][2]; af[7] = a1[j][3];
+        if constexpr (SCH == 0) acc[j] += mfma_e4m3_16x16x128(wf, af) * (sa[j] * sw);
+        else if constexpr (SCH == 1) acc[j] += mfma_f8_16x16x128<CODE>(wf, af, v4f{0.0f, 0.0f, 0.0f, 0.0f}) * sw;
+        else acc[j] = mfma_f8_16x16x128<CODE>(wf, af, acc[j]);
+      }
+    }
   }
+  // the clamped copies past the slice must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+  auto store_rows = [&]() {
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const int m = 16 * j + (lane & 15);
+      if (m < M) {
+        if constexpr (SCH != 0) {
+          // scales that do not vary along K: the token's (or the tensor's), then the channels'
+          acc[j] = acc[j] * gload<float>(p.s_a + (p.a_kind == 2 ? 0 : m));
+          if constexpr (SCH == 2) acc[j] = acc[j] * gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n0 + 4 * (lane >> 4));
+        }
+        store4<OUT>(p.y, p.ldy, m, n0 + 4 * (lane >> 4), acc[j]);
+      }
+    }
+  };
+  if constexpr (WK > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j) red[wave - 1][j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+      for (int j = 0; j < MT; ++j) acc[j] += red[w][j][lane];
+  }
+  store_rows();
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -731,12 +694,34 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
 // ---------------------------------------------------------------------------------------------
 constexpr int CHS = 2;  // K-blocks per register chunk in the small-M kernel (4: no faster)
 
-template <int WK, int SWF, int OUT>
+// MODE (MoE with at most 64 rows per expert, grid.y = expert e): 1 = the expert's rows are
+// offsets[e] .. offsets[e+1]-1 of the contiguous grouped layout; 2 = rows e*slot .. e*slot +
+// counts[e] - 1 of the masked batched layout.  The workgroup walks its expert's rows in passes of
+// 16 (a pass after the first re-reads the weight tile its CU has just streamed), and a workgroup
+// whose expert has no rows exits after its 4-byte count load, so only routed experts' weights
+// are read.
+template <int WK, int SWF, int OUT, int MODE = 0>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) {
   __shared__ v4f red[WK > 1 ? WK - 1 : 1][64];
   __shared__ __attribute__((aligned(1024))) uint8_t tile[WK][CHS][16 * 128];  // per wave, per block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t K = p.K, M = p.M;
+  // this workgroup's rows: row_base .. r_end - 1 (MoE: the expert's rows, in passes of 16)
+  int64_t row_base = 0, r_end = p.M, ex = 0;
+  if constexpr (MODE != 0) {
+    ex = blockIdx.y;
+    int64_t r0, r1;
+    if constexpr (MODE == 1) {  // (offsets are a precondition; clamped to 0..total rows)
+      r0 = min(max((int64_t)gload<int>(p.offsets + ex), (int64_t)0), p.M);
+      r1 = min(max((int64_t)gload<int>(p.offsets + ex + 1), r0), p.M);
+    } else {
+      r0 = ex * p.slot;
+      r1 = r0 + min(max((int64_t)gload<int>(p.offsets + ex), (int64_t)0), p.slot);
+    }
+    row_base = __builtin_amdgcn_readfirstlane((int)r0);
+    r_end = __builtin_amdgcn_readfirstlane((int)r1);
+    if (r_end <= row_base) return;
+  }
+  const int64_t K = p.K;
   const int KB = (int)(K / 128);
   const int per = (KB + WK - 1) / WK;
   const int kb0 = min(KB, wave * per);
@@ -744,71 +729,86 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t nb = n0 / 128;
   const int g = lane >> 4, r = lane & 15;
-  const int64_t m = r < M ? r : M - 1;  // rows past M repeat row M-1
-  const uint8_t* wline = p.w_q + (n0 + (lane >> 3)) * K + (int64_t)kb0 * 128 + 16 * (lane & 7);
-  const uint8_t* arow = p.a_q + m * p.lda + (int64_t)kb0 * 128 + 32 * g;
-  const float* sarow = p.s_a + (int64_t)kb0 * p.ld_sa + m;
-  const int64_t swbase = nb * KB + kb0;
+  const uint8_t* wline = p.w_q + (ex * p.N + n0 + (lane >> 3)) * K + (int64_t)kb0 * 128 + 16 * (lane & 7);
+  const int64_t swbase = (ex * (p.N / 128) + nb) * KB + kb0;
   // LDS tile offsets: whole-line writes (rows l/8 and l/8 + 8, chunk l%8), operand-layout reads
   // (row l%16, logical chunks 2g and 2g+1), both through the conflict-free swizzle
   const int wo0 = swz(lane >> 3, lane & 7), wo1 = swz((lane >> 3) + 8, lane & 7);
   const int ro0 = swz(r, 2 * g), ro1 = swz(r, 2 * g + 1);
 
-  int4 wv[2][CHS][2], av[2][CHS][2];
-  float sav[2][CHS], swv[2][CHS];
-  auto load_chunk = [&](int c, int buf) {
+  // One pass over the rows row_base .. row_base + M - 1 (M <= 16).
+  auto pass = [&](const int64_t row_base, const int64_t M) {
+    const int64_t m = row_base + (r < M ? r : M - 1);  // rows past M repeat row M-1
+    const uint8_t* arow = p.a_q + m * p.lda + (int64_t)kb0 * 128 + 32 * g;
+    const float* sarow = p.s_a + (int64_t)kb0 * p.ld_sa + m;
+    int4 wv[2][CHS][2], av[2][CHS][2];
+    float sav[2][CHS], swv[2][CHS];
+    auto load_chunk = [&](int c, int buf) {
 #pragma unroll
-    for (int u = 0; u < CHS; ++u) {
-      if (c + u < nk) {
-        const int64_t off = (int64_t)(c + u) * 128;
-        wv[buf][u][0] = gload_i4(wline + off);
-        wv[buf][u][1] = gload_i4(wline + 8 * K + off);
-        av[buf][u][0] = gload_i4(arow + off);
-        av[buf][u][1] = gload_i4(arow + off + 16);
-        sav[buf][u] = gload<float>(sarow + (int64_t)(c + u) * p.ld_sa);
-        swv[buf][u] = load_sw<SWF>(p.s_w, swbase + c + u);
+      for (int u = 0; u < CHS; ++u) {
+        if (c + u < nk) {
+          const int64_t off = (int64_t)(c + u) * 128;
+          wv[buf][u][0] = gload_i4(wline + off);
+          wv[buf][u][1] = gload_i4(wline + 8 * K + off);
+          av[buf][u][0] = gload_i4(arow + off);
+          av[buf][u][1] = gload_i4(arow + off + 16);
+          sav[buf][u] = gload<float>(sarow + (int64_t)(c + u) * p.ld_sa);
+          swv[buf][u] = load_sw<SWF>(p.s_w, swbase + c + u);
+        }
+      }
+    };
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute_chunk = [&](int c, int buf) {
+#pragma unroll
+      for (int u = 0; u < CHS; ++u) {
+        if (c + u < nk) {
+          // (one wave's LDS operations complete in order: the reads see the writes, and the next
+          // chunk's writes to this tile follow these reads)
+          uint8_t* t = &tile[wave][u][0];
+          *reinterpret_cast<int4*>(t + wo0) = wv[buf][u][0];
+          *reinterpret_cast<int4*>(t + wo1) = wv[buf][u][1];
+          const int4 lo = *reinterpret_cast<const int4*>(t + ro0);
+          const int4 hi = *reinterpret_cast<const int4*>(t + ro1);
+          v8i af, bf;
+          af[0] = lo.x; af[1] = lo.y; af[2] = lo.z; af[3] = lo.w;
+          af[4] = hi.x; af[5] = hi.y; af[6] = hi.z; af[7] = hi.w;
+          bf[0] = av[buf][u][0].x; bf[1] = av[buf][u][0].y; bf[2] = av[buf][u][0].z; bf[3] = av[buf][u][0].w;
+          bf[4] = av[buf][u][1].x; bf[5] = av[buf][u][1].y; bf[6] = av[buf][u][1].z; bf[7] = av[buf][u][1].w;
+          const float sc = sav[buf][u] * swv[buf][u];
+          acc += mfma_e4m3_16x16x128(af, bf) * sc;
+        }
+      }
+    };
+    load_chunk(0, 0);
+    for (int c = 0; c < nk; c += 2 * CHS) {
+      if (c + CHS < nk) load_chunk(c + CHS, 1);
+      compute_chunk(c, 0);
+      if (c + CHS < nk) {
+        if (c + 2 * CHS < nk) load_chunk(c + 2 * CHS, 0);
+        compute_chunk(c + CHS, 1);
       }
     }
-  };
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute_chunk = [&](int c, int buf) {
-#pragma unroll
-    for (int u = 0; u < CHS; ++u) {
-      if (c + u < nk) {
-        // (one wave's LDS operations complete in order: the reads see the writes, and the next
-        // chunk's writes to this tile follow these reads)
-        uint8_t* t = &tile[wave][u][0];
-        *reinterpret_cast<int4*>(t + wo0) = wv[buf][u][0];
-        *reinterpret_cast<int4*>(t + wo1) = wv[buf][u][1];
-        const int4 lo = *reinterpret_cast<const int4*>(t + ro0);
-        const int4 hi = *reinterpret_cast<const int4*>(t + ro1);
-        v8i af, bf;
-        af[0] = lo.x; af[1] = lo.y; af[2] = lo.z; af[3] = lo.w;
-        af[4] = hi.x; af[5] = hi.y; af[6] = hi.z; af[7] = hi.w;
-        bf[0] = av[buf][u][0].x; bf[1] = av[buf][u][0].y; bf[2] = av[buf][u][0].z; bf[3] = av[buf][u][0].w;
-        bf[4] = av[buf][u][1].x; bf[5] = av[buf][u][1].y; bf[6] = av[buf][u][1].z; bf[7] = av[buf][u][1].w;
-        const float sc = sav[buf][u] * swv[buf][u];
-        acc += mfma_e4m3_16x16x128(af, bf) * sc;
+    if constexpr (WK > 1) {
+      if (wave > 0) red[wave - 1][lane] = acc;
+      __syncthreads();
+      if constexpr (MODE == 0) {
+        if (wave > 0) return;
       }
+      if (wave == 0) {
+#pragma unroll
+        for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
+        if (r < M) store4<OUT>(p.y, p.ldy, row_base + r, n0 + 4 * g, acc);
+      }
+      if constexpr (MODE != 0) __syncthreads();  // the next pass rewrites red
+    } else {
+      if (r < M) store4<OUT>(p.y, p.ldy, row_base + r, n0 + 4 * g, acc);
     }
   };
-  load_chunk(0, 0);
-  for (int c = 0; c < nk; c += 2 * CHS) {
-    if (c + CHS < nk) load_chunk(c + CHS, 1);
-    compute_chunk(c, 0);
-    if (c + CHS < nk) {
-      if (c + 2 * CHS < nk) load_chunk(c + 2 * CHS, 0);
-      compute_chunk(c + CHS, 1);
-    }
+  if constexpr (MODE == 0) {
+    pass(0, p.M);
+  } else {
+    for (int64_t rb = row_base; rb < r_end; rb += 16) pass(rb, min((int64_t)16, r_end - rb));
   }
-  if constexpr (WK > 1) {
-    if (wave > 0) red[wave - 1][lane] = acc;
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
-  }
-  if (r < M) store4<OUT>(p.y, p.ldy, r, n0 + 4 * g, acc);
 }
 
 }  // namespace

@@ -57,8 +57,8 @@ hipError_t launch_gemm_scaled_prefill(const GemmArgs& a, int sch, int code, hipS
 hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int code, hipStream_t stream);
 
 // MoE with at most 64 rows per expert: mode 1 grouped (offsets [E+1]), mode 2 batched (counts [E],
-// slot rows per expert); rows_per_expert bounds every expert's row count.
-hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, int64_t rows_per_expert, hipStream_t stream);
+// slot rows per expert).
+hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, hipStream_t stream);
 
 // act_quant + decode GEMM from bf16 activations (M <= 64): one launch of the GEMM that quantizes
 // its activations itself where that is faster (workspace 0), else act_quant into the workspace

@@ -88,7 +88,7 @@ hipError_t launch_gemm_decode_fused(const GemmArgs& a, const uint16_t*, int64_t,
   return launched("gemm_fused");
 }
 int decode_small_waves(int64_t, int64_t) { return 8; }
-hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, int64_t, hipStream_t) {
+hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, hipStream_t) {
   record(a);
   g_stub.K = mode;  // (the driver checks which layout reached the launcher)
   return launched("moe_decode");
