@@ -263,13 +263,15 @@ def extra_suites(torch, fgb, workloads, np):
         flush_buf.sum()
 
     # decode — hipGraph loop over rotating weight copies (> 2x MALL in total)
-    dec, fused = {}, {}
+    dec, fused, fp8dyn = {}, {}, {}
     for (name, N, K) in workloads.DECODE_SHAPES:
         w = workloads.device_bf16((N, K), next_seed(), dev, outliers=False, std=0.02)
         wq0, sw = fgb.quantize_weight(w)
+        wc0, swc = fgb.quantize_weight_per_channel(w)  # FP8_DYNAMIC weights (per channel)
         del w
         copies = max(2, -(-2 * MALL_BYTES // (N * K)) + 1)
         wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+        wcs = [wc0] + [wc0.clone() for _ in range(copies - 1)]
         for M in workloads.DECODE_MS:
             x = workloads.device_bf16((M, K), next_seed(), dev)
             q, sa = fgb.quantize(x)
@@ -289,9 +291,16 @@ def extra_suites(torch, fgb, workloads, np):
             fbytes = N * K + 4 * (N // 128) * (K // 128) + 2 * M * K + 2 * M * N
             fused[f"{name}_{N}x{K}_M{M}"] = dict(quant_plus_gemm_us=round(two, 2), fused_us=round(one, 2),
                                                  fused_frac_hbm=round(fbytes / one / 1e3 / PEAK_HBM_GBS, 3))
-        del wqs, wq0
+            # FP8_DYNAMIC: per-token activation and per-channel weight scales, E4M3
+            qt, st = fgb.quantize_per_token(x)
+            tdyn = _graph_time(torch, lambda i: fgb.scaled_gemm(qt, st, wcs[i % copies], swc, act_scale="token",
+                                                                out=y, workspace=ws), 4 * copies)
+            dbytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
+            fp8dyn[f"{name}_{N}x{K}_M{M}"] = dict(us=round(tdyn, 2), frac_hbm=round(dbytes / tdyn / 1e3 / PEAK_HBM_GBS, 3))
+        del wqs, wq0, wcs, wc0
     out["decode"] = dec
     out["decode_fused_quant"] = fused
+    out["decode_fp8_dynamic"] = fp8dyn
 
     # the other schemes at the Llama-3-8B prefill shapes (M = 4096), back to back: FP8_DYNAMIC
     # (per-token activations, per-channel weights, E4M3) and static per-tensor activations with

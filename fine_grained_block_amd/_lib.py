@@ -41,7 +41,8 @@ _SIGS = {
     "fgb_act_quant_static": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, ctypes.c_int, _vp, _c_i64, _vp]),
     "fgb_weight_quant_block128_ex": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp]),
     "fgb_w8a8_scaled_gemm": (ctypes.c_int, [_vp, _c_i64, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_int,
-                                            ctypes.c_int, _vp, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _vp]),
+                                            ctypes.c_int, _vp, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i64, _vp,
+                                            ctypes.c_size_t, _vp]),
     "fgb_fp8_encode": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp]),
     "fgb_fp8_decode": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp]),
     "fgb_selftest_quotients": (ctypes.c_int, [_vp, _vp]),

@@ -220,7 +220,7 @@ int fgb_act_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
 
 int fgb_w8a8_scaled_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int act_scale, const uint8_t* w_q,
                          const void* s_w, int w_scale, int s_w_fmt, int code_fmt, void* y, int y_dtype, int64_t ldy,
-                         int64_t M, int64_t N, int64_t K, void* stream) {
+                         int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FGB_ERR_SHAPE;
   if (N % FGB_BLOCK || K % FGB_BLOCK) return FGB_ERR_SHAPE;
   if (act_scale != FGB_ACT_SCALE_TOKEN && act_scale != FGB_ACT_SCALE_TENSOR) return FGB_ERR_ENUM;
@@ -237,12 +237,16 @@ int fgb_w8a8_scaled_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int 
     return FGB_ERR_ALIGN;
   if (lda % 16 || (ldy * ybytes) % 16) return FGB_ERR_ALIGN;
   if (M * lda >= kMax32 || N * K >= kMax32 || K > 32768) return FGB_ERR_SHAPE;
+  // the same decode plan (and workspace) as fgb_w8a8_block_gemm
+  const size_t need = M <= 64 ? fgb::decode_workspace_bytes(M, N, K) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FGB_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return FGB_ERR_ALIGN;
   int st = check_device();
   if (st != FGB_OK) return st;
   fgb::GemmArgs a{a_q, lda, s_a, 0, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K, nullptr, 1, act_scale};
   const int sch = w_scale == FGB_W_SCALE_CHANNEL ? 2 : 1;
   const int code = code_fmt == FGB_FP8_E5M2 ? 1 : 0;
-  if (M <= 64) return launch_status(fgb::launch_gemm_scaled_decode(a, sch, code, (hipStream_t)stream));
+  if (M <= 64) return launch_status(fgb::launch_gemm_scaled_decode(a, sch, code, workspace, (hipStream_t)stream));
   return launch_status(fgb::launch_gemm_scaled_prefill(a, sch, code, (hipStream_t)stream));
 }
 

@@ -25,8 +25,6 @@ int decode_small_waves(int64_t N, int64_t K) {
   return wk;
 }
 
-namespace {
-
 // M <= 16: weights from this size on with long rows (K >= 8192: long slices per wave, where the
 // ring reaches its steady state) take the LDS-ring kernel, the others the register kernel.
 // Measured (graph loop): 4096x14336 at M = 16 14.7 vs 15.4 us, 7168x18432 31.5 vs 33.9 us (ring
@@ -41,8 +39,6 @@ bool decode_ring(int64_t N, int64_t K) { return N * K >= kRingMinWeightBytes && 
 // weights the per-wave copies of all activation rows cost more than the second launch.
 bool ring_mid_rows(int64_t N, int64_t K) { return N * K <= (16ll << 20); }
 
-constexpr int MID_D = 4;  // LDS stages of the 16 < M <= 64 kernel (measured: 4 >= 5, 6)
-
 // K-blocks per workgroup of the 16 < M <= 64 kernel.  One slice when the weight blocks alone give
 // 160 or more workgroups; otherwise slices for about 224 workgroups (one per CU, most of the
 // 256), each at least 8 blocks long (shorter slices spend their time filling the ring and their
@@ -55,8 +51,6 @@ int mid_kpw(int64_t N, int64_t K) {
   S = S > smax ? smax : S;
   return (KB + S - 1) / S;
 }
-
-}  // namespace
 
 int decode_splits(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 || ring_mid_rows(N, K)) return 1;  // these kernels need no workspace
@@ -137,7 +131,7 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
     const dim3 grid((unsigned)((a.N / 128) * S)), block(512);
     float* ws = reinterpret_cast<float*>(workspace);
 #define FGB_MID(MT_, SWF, OUT) \
-  hipLaunchKernelGGL((gemm_decode_mid_kernel<MT_, MID_D, SWF, OUT>), grid, block, 0, stream, a, kpw, S, ws)
+  hipLaunchKernelGGL((gemm_decode_mid_kernel<MT_, kMidStages, SWF, OUT>), grid, block, 0, stream, a, kpw, S, ws)
 #define FGB_MID_MT(SWF, OUT)                     \
   do {                                           \
     if (a.M <= 32) FGB_MID(2, SWF, OUT);         \
@@ -155,9 +149,11 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
     const int64_t total = a.M * (a.N / 4);
     const dim3 rgrid((unsigned)((total + 255) / 256));
     if (a.y_dtype == 0)
-      hipLaunchKernelGGL(splitk_reduce_kernel<0>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
+      hipLaunchKernelGGL(splitk_reduce_kernel<0>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy,
+                         nullptr, 0, nullptr);
     else
-      hipLaunchKernelGGL(splitk_reduce_kernel<1>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy);
+      hipLaunchKernelGGL(splitk_reduce_kernel<1>, rgrid, dim3(256), 0, stream, ws, S, a.M, a.N, a.y, a.ldy,
+                         nullptr, 0, nullptr);
     return hipGetLastError();
   }
 }

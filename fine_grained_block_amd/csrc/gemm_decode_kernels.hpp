@@ -34,10 +34,13 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 // Sum of the S partial slices in slice order; all loads of a group of 8 slices are issued
-// before they are added.
-template <int OUT>
+// before they are added.  SCH 1 and 2 (scales that do not vary along K, see the ring kernel)
+// then multiply by the token's or the tensor's activation scale s_a (a_kind 1 or 2) and, for
+// SCH 2, by the channels' weight scales s_w[n .. n+3].
+template <int OUT, int SCH = 0>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int S, int64_t M,
-                                                            int64_t N, void* y, int64_t ldy) {
+                                                            int64_t N, void* y, int64_t ldy, const float* s_a,
+                                                            int a_kind, const float* s_w) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one float4 of y
   const int64_t total = M * (N / 4);
   if (q >= total) return;
@@ -54,6 +57,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     for (int u = 0; u < 8; ++u) {
       if (i0 + u < S) s += v[u];
     }
+  }
+  if constexpr (SCH != 0) {
+    s = s * gload<float>(s_a + (a_kind == 2 ? 0 : m));
+    if constexpr (SCH == 2) s = s * gload<v4f>(s_w + n);
   }
   store4<OUT>(y, ldy, m, n, s);
 }
@@ -515,14 +522,17 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_fused_quant_small_kernel(
 // ring of D LDS stages shared by the waves, with whole-line buffer-form direct copies issued
 // D-1 blocks ahead and one barrier per block; the activation stream is read once per 128 weight
 // rows.  Slices (S > 1) write float32 partials [S][M][N] for the ordered reduction launch.
+// SCH and CODE as for the ring kernel (schemes 1 and 2 copy no activation scales; their scales
+// that do not vary along K multiply the finished sums, here or in the reduction).
 // ---------------------------------------------------------------------------------------------
-template <int MT, int D, int SWF, int OUT>
+template <int MT, int D, int SWF, int OUT, int SCH = 0, int CODE = 0>
 __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int kpw, int S, float* ws) {
+  static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
   constexpr int MROWS = 16 * MT;
   constexpr int WB = 128 * 128, AB = MROWS * 128, SB = 64 * 4;
   constexpr int STAGE = WB + AB + SB;
   constexpr int A_GRP = MROWS / 8;                 // 8-row copy groups of the activation rows
-  constexpr int OPS = 2 + 1 + 1;                   // copies per wave per block: W, A, scales
+  constexpr int OPS = 2 + 1 + (SCH == 0 ? 1 : 0);  // copies per wave per block: W, A, scales
   static_assert(D >= 3 && D <= 6, "three to six stages");
   static_assert(MT == 2 || MT == 4, "32 or 64 activation rows");
   __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
@@ -569,7 +579,8 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + 8 * i) * 1024), 16, woff[i], koff, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + WB + aq * 1024), 16, aoff, koff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(st + WB + AB), 4, soff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
+    if constexpr (SCH == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(st + WB + AB), 4, soff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
 #endif
   };
   auto stage = [&](int i) -> uint8_t* {
@@ -583,7 +594,8 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
     }
   };
 
-  for (int c = tid; c < nk; c += 512) sws[c] = load_sw<SWF>(p.s_w, (n0 / 128) * KB + kb0 + c);
+  if constexpr (SCH != 2)
+    for (int c = tid; c < nk; c += 512) sws[c] = load_sw<SWF>(p.s_w, (n0 / 128) * KB + kb0 + c);
 
   v4f acc[MT];
 #pragma unroll
@@ -646,13 +658,16 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
     v8i wf;
     wf[0] = wl[0]; wf[1] = wl[1]; wf[2] = wl[2]; wf[3] = wl[3];
     wf[4] = wh[0]; wf[5] = wh[1]; wf[6] = wh[2]; wf[7] = wh[3];
-    const float sw = sws[kk];
+    // (schemes 1 and 2 copy no activation scales: their sa reads see stale bytes, unused)
+    const float sw = SCH == 2 ? 0.0f : sws[kk];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
       v8i bf;
       bf[0] = al[j][0]; bf[1] = al[j][1]; bf[2] = al[j][2]; bf[3] = al[j][3];
       bf[4] = ah[j][0]; bf[5] = ah[j][1]; bf[6] = ah[j][2]; bf[7] = ah[j][3];
-      acc[j] += mfma_e4m3_16x16x128(wf, bf) * (sa[j] * sw);
+      if constexpr (SCH == 0) acc[j] += mfma_e4m3_16x16x128(wf, bf) * (sa[j] * sw);
+      else if constexpr (SCH == 1) acc[j] += mfma_f8_16x16x128<CODE>(wf, bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}) * sw;
+      else acc[j] = mfma_f8_16x16x128<CODE>(wf, bf, acc[j]);
     }
   };
 
@@ -673,8 +688,17 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
   for (int j = 0; j < MT; ++j) {
     const int64_t m = 16 * j + r;
     if (m < M) {
-      if (S == 1) store4<OUT>(p.y, p.ldy, m, n, acc[j]);
-      else gstore<v4f>(ws + ((int64_t)split * M + m) * N + n, acc[j]);
+      if (S == 1) {
+        if constexpr (SCH != 0) {
+          // scales that do not vary along K: the token's (or the tensor's), then the channels'
+          // (sliced calls apply them in the reduction)
+          acc[j] = acc[j] * gload<float>(p.s_a + (p.a_kind == 2 ? 0 : m));
+          if constexpr (SCH == 2) acc[j] = acc[j] * gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n);
+        }
+        store4<OUT>(p.y, p.ldy, m, n, acc[j]);
+      } else {
+        gstore<v4f>(ws + ((int64_t)split * M + m) * N + n, acc[j]);
+      }
     }
   }
 }
@@ -699,9 +723,11 @@ constexpr int CHS = 2;  // K-blocks per register chunk in the small-M kernel (4:
 // counts[e] - 1 of the masked batched layout.  The workgroup walks its expert's rows in passes of
 // 16 (a pass after the first re-reads the weight tile its CU has just streamed), and a workgroup
 // whose expert has no rows exits after its 4-byte count load, so only routed experts' weights
-// are read.
-template <int WK, int SWF, int OUT, int MODE = 0>
+// are read.  SCH and CODE as for the ring kernel (MoE layouts: scheme 0 only).
+template <int WK, int SWF, int OUT, int MODE = 0, int SCH = 0, int CODE = 0>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) {
+  static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
+  static_assert(MODE == 0 || SCH == 0, "MoE layouts use the 1x128-group scheme");
   __shared__ v4f red[WK > 1 ? WK - 1 : 1][64];
   __shared__ __attribute__((aligned(1024))) uint8_t tile[WK][CHS][16 * 128];  // per wave, per block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -752,8 +778,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
           wv[buf][u][1] = gload_i4(wline + 8 * K + off);
           av[buf][u][0] = gload_i4(arow + off);
           av[buf][u][1] = gload_i4(arow + off + 16);
-          sav[buf][u] = gload<float>(sarow + (int64_t)(c + u) * p.ld_sa);
-          swv[buf][u] = load_sw<SWF>(p.s_w, swbase + c + u);
+          if constexpr (SCH == 0) sav[buf][u] = gload<float>(sarow + (int64_t)(c + u) * p.ld_sa);
+          if constexpr (SCH != 2) swv[buf][u] = load_sw<SWF>(p.s_w, swbase + c + u);
         }
       }
     };
@@ -774,8 +800,9 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
           af[4] = hi.x; af[5] = hi.y; af[6] = hi.z; af[7] = hi.w;
           bf[0] = av[buf][u][0].x; bf[1] = av[buf][u][0].y; bf[2] = av[buf][u][0].z; bf[3] = av[buf][u][0].w;
           bf[4] = av[buf][u][1].x; bf[5] = av[buf][u][1].y; bf[6] = av[buf][u][1].z; bf[7] = av[buf][u][1].w;
-          const float sc = sav[buf][u] * swv[buf][u];
-          acc += mfma_e4m3_16x16x128(af, bf) * sc;
+          if constexpr (SCH == 0) acc += mfma_e4m3_16x16x128(af, bf) * (sav[buf][u] * swv[buf][u]);
+          else if constexpr (SCH == 1) acc += mfma_f8_16x16x128<CODE>(af, bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}) * swv[buf][u];
+          else acc = mfma_f8_16x16x128<CODE>(af, bf, acc);
         }
       }
     };
@@ -788,6 +815,16 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
         compute_chunk(c + CHS, 1);
       }
     }
+    auto finish = [&]() {
+      if (r < M) {
+        if constexpr (SCH != 0) {
+          // scales that do not vary along K: the token's (or the tensor's), then the channels'
+          acc = acc * gload<float>(p.s_a + (p.a_kind == 2 ? 0 : row_base + r));
+          if constexpr (SCH == 2) acc = acc * gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n0 + 4 * g);
+        }
+        store4<OUT>(p.y, p.ldy, row_base + r, n0 + 4 * g, acc);
+      }
+    };
     if constexpr (WK > 1) {
       if (wave > 0) red[wave - 1][lane] = acc;
       __syncthreads();
@@ -797,11 +834,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
       if (wave == 0) {
 #pragma unroll
         for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
-        if (r < M) store4<OUT>(p.y, p.ldy, row_base + r, n0 + 4 * g, acc);
+        finish();
       }
       if constexpr (MODE != 0) __syncthreads();  // the next pass rewrites red
     } else {
-      if (r < M) store4<OUT>(p.y, p.ldy, row_base + r, n0 + 4 * g, acc);
+      finish();
     }
   };
   if constexpr (MODE == 0) {

@@ -54,7 +54,7 @@ hipError_t launch_check_offsets(const int32_t* offsets, int32_t E, int64_t total
 // The other scaling schemes (sch 1: per-token or per-tensor activation scale with 128x128 weight
 // blocks; sch 2: per-channel weight scales), E4M3 (code 0) or E5M2 (code 1) operands.
 hipError_t launch_gemm_scaled_prefill(const GemmArgs& a, int sch, int code, hipStream_t stream);
-hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int code, hipStream_t stream);
+hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int code, void* workspace, hipStream_t stream);
 
 // MoE with at most 64 rows per expert: mode 1 grouped (offsets [E+1]), mode 2 batched (counts [E],
 // slot rows per expert).
@@ -70,7 +70,13 @@ hipError_t launch_gemm_decode_fused_small(const GemmArgs& a, const uint16_t* x, 
 // waves per 16-row workgroup that split K in the M <= 16 decode kernels
 int decode_small_waves(int64_t N, int64_t K);
 
-// Split-K decode path (M <= 64).
+// Decode path selection (M <= 64): the LDS-ring kernel for M <= 16 (large weights, long rows);
+// the per-wave ring kernel for 16 < M <= 64 (small weights); the K-blocks per workgroup of the
+// shared-ring 16 < M <= 64 kernel and its number of slices (> 1: partials and a second launch).
+bool decode_ring(int64_t N, int64_t K);
+bool ring_mid_rows(int64_t N, int64_t K);
+int mid_kpw(int64_t N, int64_t K);
+constexpr int kMidStages = 4;  // LDS stages of the shared-ring kernel (measured: 4 >= 5, 6)
 int decode_splits(int64_t M, int64_t N, int64_t K);
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream);

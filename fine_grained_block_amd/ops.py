@@ -199,10 +199,11 @@ def quantize_static(x: torch.Tensor, scale: torch.Tensor, code: str = "e4m3", ou
 
 def scaled_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: torch.Tensor,
                 act_scale: str = "token", code: str = "e4m3", out_dtype=torch.bfloat16,
-                out: torch.Tensor | None = None) -> torch.Tensor:
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """GEMM with per-token (s_a float32 [M]) or per-tensor (s_a float32 [1]) activation scales and
     per-channel (s_w float32 [N]) or 128x128-block (s_w [N/128, K/128], float32 or UE8M0) weight
-    scales; both operands in `code` ("e4m3" or "e5m2")."""
+    scales; both operands in `code` ("e4m3" or "e5m2").  Decode sizes may need a workspace of
+    gemm_workspace_bytes(M, N, K) bytes (allocated here when none is given)."""
     _matrix(a_q, "a_q", torch.uint8)
     M, K = a_q.shape
     KB = _blocks(K, "K")
@@ -228,12 +229,18 @@ def scaled_gemm(a_q: torch.Tensor, s_a: torch.Tensor, w_q: torch.Tensor, s_w: to
     if out is not None:
         _need(out.dtype in (torch.bfloat16, torch.float32), "out must be bf16 or float32")
         _matrix(out, "out", out.dtype, rows=M, cols=N)
-    _on_device(("a_q", a_q), ("s_a", s_a), ("w_q", w_q), ("s_w", s_w), ("out", out))
+    if workspace is not None:
+        _need(workspace.is_contiguous(), "workspace must be contiguous")
+    _on_device(("a_q", a_q), ("s_a", s_a), ("w_q", w_q), ("s_w", s_w), ("out", out), ("workspace", workspace))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    need = gemm_workspace_bytes(M, N, K)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=a_q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().fgb_w8a8_scaled_gemm(_ptr(a_q), _row_ld(a_q), _ptr(s_a), ak, _ptr(w_q), _ptr(s_w), wk,
                                     _scale_fmt(s_w), _code(code), _ptr(out), _out_code(out.dtype), _row_ld(out),
-                                    M, N, K, _stream())
+                                    M, N, K, _ptr(workspace), ws_bytes, _stream())
     check("fgb_w8a8_scaled_gemm", st)
     return out
 

@@ -104,7 +104,8 @@ int fgb_act_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
 int fgb_weight_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* w_q, void* s_w,
                               int s_w_fmt, void* stream);
 
-/* Host query: workspace bytes fgb_w8a8_block_gemm needs for this shape (0 if none). */
+/* Host query: workspace bytes fgb_w8a8_block_gemm (and fgb_w8a8_scaled_gemm, which follows the same
+ * decode plan) needs for this shape (0 if none). */
 size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -261,13 +262,16 @@ int fgb_weight_quant_block128_ex(const uint16_t* w, int64_t N, int64_t K, int co
  *                     (s_w [N/128, K/128] float32, or UE8M0 with E4M3 codes).
  * Products are summed in float32 on the matrix cores; scales that do not vary along K multiply
  * the float32 sum once at the end.  a_q [M, lda]; w_q [N, K] dense; y [M, ldy] bf16 or float32.
- * act_scale GROUP128 is FGB_ERR_ENUM here (that is fgb_w8a8_block_gemm).  One launch, no
- * workspace.  Size limits as for fgb_w8a8_block_gemm.
+ * act_scale GROUP128 is FGB_ERR_ENUM here (that is fgb_w8a8_block_gemm).  Size limits, the
+ * decode kernels (M <= 64) and the workspace as for fgb_w8a8_block_gemm: workspace device,
+ * 16-byte aligned, >= fgb_gemm_workspace_bytes(M, N, K) bytes (NULL when that is 0;
+ * FGB_ERR_WORKSPACE if missing or too small); the sliced decode calls add their float32 partials
+ * in a second launch that also applies the scales.
  */
 int fgb_w8a8_scaled_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int act_scale,
-                         const uint8_t* w_q, const void* s_w, int w_scale, int s_w_fmt,
-                         int code_fmt, void* y, int y_dtype, int64_t ldy,
-                         int64_t M, int64_t N, int64_t K, void* stream);
+                         const uint8_t* w_q, const void* s_w, int w_scale, int s_w_fmt, int code_fmt,
+                         void* y, int y_dtype, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Element-wise codecs (vLLM "FP8 W8A8", "Two FP8 representations"; UE8M0 per Transformers

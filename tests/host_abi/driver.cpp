@@ -185,9 +185,10 @@ int main() {
   EXPECT(fgb_weight_quant_block128_ex((const uint16_t*)P(F), 128, 128, 1, (uint8_t*)P(F), P(F), 1, nullptr),
          FGB_ERR_ENUM);  // UE8M0 scales go with E4M3 codes
   EXPECT(fgb_weight_quant_block128_ex((const uint16_t*)P(F), 128, 128, 1, (uint8_t*)P(F), P(F), 0, nullptr), FGB_OK);
-  auto scaled = [](int64_t M, int ak, int wk, int swf, int code, uintptr_t sa = F + 4, uintptr_t sw = F) {
-    return fgb_w8a8_scaled_gemm((const uint8_t*)P(F), 1024, (const float*)P(sa), ak, (const uint8_t*)P(F), P(sw), wk,
-                                swf, code, P(F), 0, 512, M, 512, 1024, nullptr);
+  auto scaled = [](int64_t M, int ak, int wk, int swf, int code, uintptr_t sa = F + 4, uintptr_t sw = F,
+                   int64_t N = 512, int64_t K = 1024, uintptr_t ws = 0, size_t wsb = 0) {
+    return fgb_w8a8_scaled_gemm((const uint8_t*)P(F), K, (const float*)P(sa), ak, (const uint8_t*)P(F), P(sw), wk,
+                                swf, code, P(F), 0, N, M, N, K, P(ws), wsb, nullptr);
   };
   EXPECT(scaled(256, FGB_ACT_SCALE_GROUP128, FGB_W_SCALE_BLOCK128, 0, 0), FGB_ERR_ENUM);
   EXPECT(scaled(256, FGB_ACT_SCALE_TOKEN, 5, 0, 0), FGB_ERR_ENUM);
@@ -201,6 +202,13 @@ int main() {
   if (strcmp(g_stub.last, "scaled_prefill") || g_stub.E != 2 || g_stub.M != 256) failures++;
   EXPECT(scaled(64, FGB_ACT_SCALE_TENSOR, FGB_W_SCALE_BLOCK128, 1, 0), FGB_OK);
   if (strcmp(g_stub.last, "scaled_decode") || g_stub.E != 1) failures++;
+  // a decode plan with partials (the stub's plan for 32 x 4096 x 4096) needs the workspace
+  const size_t need = fgb_gemm_workspace_bytes(32, 4096, 4096);
+  EXPECT(scaled(32, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 0, F + 4, F, 4096, 4096), FGB_ERR_WORKSPACE);
+  EXPECT(scaled(32, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 0, F + 4, F, 4096, 4096, F, need - 1), FGB_ERR_WORKSPACE);
+  EXPECT(scaled(32, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 0, F + 4, F, 4096, 4096, F + 8, need), FGB_ERR_ALIGN);
+  EXPECT(scaled(32, FGB_ACT_SCALE_TOKEN, FGB_W_SCALE_CHANNEL, 0, 0, F + 4, F, 4096, 4096, F, need), FGB_OK);
+  if (strcmp(g_stub.last, "scaled_decode") || g_stub.workspace != P(F)) failures++;
 
   // the fused-quantization decode GEMM (the stub's workspace need: 4096 bytes above 8 rows)
   auto fused = [](int64_t M, int64_t ldx, uintptr_t xp = F, uintptr_t ws = F, size_t ws_bytes = 4096) {

@@ -59,9 +59,10 @@ hipError_t launch_gemm_scaled_prefill(const GemmArgs& a, int sch, int, hipStream
   g_stub.E = sch;
   return launched("scaled_prefill");
 }
-hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int, hipStream_t) {
+hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int, void* ws, hipStream_t) {
   record(a);
   g_stub.E = sch;
+  g_stub.workspace = ws;
   return launched("scaled_decode");
 }
 hipError_t launch_encode(const float*, uint8_t*, int64_t, int, int, hipStream_t) { return launched("encode"); }

@@ -145,6 +145,27 @@ def test_scaled_gemm_parity(dev, code, act, weight):
         assert np.array_equal(bf16_tensor_to_f64(y16), gemm.bf16_rne(y32.astype(np.float64))), (M, N, K)
 
 
+# decode shapes that reach each decode kernel: M <= 16 with >= 48 MiB of weights and K >= 8192
+# (LDS-ring kernel); 16 < M <= 64 with more than 16 MiB of weights: the shared-ring kernel in one
+# K slice (>= 160 weight blocks of 128 rows) or in several, with partials and the scaling
+# reduction (fewer blocks)
+DECODE_PATHS = [(4, 2048, 24576), (16, 2048, 24576), (17, 20480, 1024), (33, 20480, 1024), (64, 20480, 1024),
+                (40, 4096, 8192), (64, 4096, 14336)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_PATHS)
+@pytest.mark.parametrize("act,weight,code,fmt", [("token", "channel", "e4m3", "f32"), ("tensor", "block", "e5m2", "f32"),
+                                                 ("token", "block", "e4m3", "ue8m0")])
+def test_scaled_gemm_decode_kernels(dev, M, N, K, act, weight, code, fmt):
+    ops = _operands(M, N, K, act, weight, code, fmt=fmt, key=40 + M)
+    yref = schemes.scaled_gemm_ref(*ops, act=act, weight=weight, a_code=code, w_code=code, w_scale_fmt=fmt)
+    y32 = _run(ops, dev, act, code, torch.float32).cpu().numpy()
+    check_t1(y32, yref)
+    y16 = _run(ops, dev, act, code, torch.bfloat16)
+    check_t2(bf16_tensor_to_f64(y16), yref)
+    assert np.array_equal(bf16_tensor_to_f64(y16), gemm.bf16_rne(y32.astype(np.float64)))
+
+
 @pytest.mark.parametrize("M", [8, 64, 300])
 def test_static_block_gemm_ue8m0(dev, M):
     N, K = 512, 1024
