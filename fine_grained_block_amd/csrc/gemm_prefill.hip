@@ -30,6 +30,8 @@ hipError_t launch_cfg(const GemmArgs& a, int tiles_m, hipStream_t stream) {
   return hipGetLastError();
 }
 
+}  // namespace
+
 // Compute units of the current device (cached per device).
 int cu_count() {
   static int cached[64] = {};
@@ -42,6 +44,8 @@ int cu_count() {
   }
   return cached[dev];
 }
+
+namespace {
 
 template <typename C>
 int64_t tiles_for(int64_t M, int64_t N) { return ((M + C::BM - 1) / C::BM) * (N / C::BN); }
@@ -68,6 +72,8 @@ bool use_persistent(const GemmArgs& a, int64_t max_kb) {
 // own launch, with n_big chosen to minimize the waves of tiles over the CUs (one tile per CU at
 // a time), weighted 1 and 0.6.  Whole waves of big tiles plus one wave of half tiles can beat
 // either tile alone: QKV at M = 4096 (384 big tiles) runs 256 big + 256 half tiles.
+}  // namespace
+
 int64_t big_columns(int64_t M, int64_t N, int64_t K) {
   if (K < 8 * KBYTES) return 0;
   const int64_t cus = cu_count(), nc = N / Big::BN;
@@ -81,8 +87,6 @@ int64_t big_columns(int64_t M, int64_t N, int64_t K) {
   }
   return best_c * Big::BN;
 }
-
-}  // namespace
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
   if (a.N % Big::BN != 0 || a.N % Half::BN != 0)

@@ -34,10 +34,33 @@ void launch_cfg_sch(const GemmArgs& a, int sch, int code, hipStream_t stream) {
 
 }  // namespace
 
-// 256 x 256 tiles where N is a multiple of 256 and K has at least 8 blocks, else 128 x 128.
+// The block scheme's column split (N % 256 == 0): the first big_columns() output columns as
+// 256 x 256 tiles, the rest as 256 x 128 tiles, each part in its own launch (offset weight rows,
+// weight scales and output columns); else 128 x 128 tiles.  Measured at the Llama-3-8B QKV shape
+// 6144x4096, M = 4096 (384 tiles of 256 x 256 before, 256 + 256 split tiles now): FP8_DYNAMIC
+// 107.8 -> 93.3 us, static per-tensor E5M2 112.4 -> 97.7 us.
 hipError_t launch_gemm_scaled_prefill(const GemmArgs& a, int sch, int code, hipStream_t stream) {
-  if (a.N % Big::BN == 0 && a.K >= 8 * KBYTES) launch_cfg_sch<Big>(a, sch, code, stream);
-  else launch_cfg_sch<Narrow>(a, sch, code, stream);
+  if (a.N % Big::BN != 0 || a.N % Half::BN != 0) {
+    launch_cfg_sch<Narrow>(a, sch, code, stream);
+    return hipGetLastError();
+  }
+  const int64_t n_big = big_columns(a.M, a.N, a.K);
+  if (n_big > 0) {
+    GemmArgs b = a;
+    b.N = n_big;
+    launch_cfg_sch<Big>(b, sch, code, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_big == a.N) return e;
+  }
+  GemmArgs h = a;
+  h.N = a.N - n_big;
+  h.w_q = a.w_q + n_big * a.K;
+  if (sch == 2)
+    h.s_w = reinterpret_cast<const float*>(a.s_w) + n_big;
+  else
+    h.s_w = (const uint8_t*)a.s_w + (n_big / 128) * (a.K / KBYTES) * (a.s_w_fmt == 0 ? 4 : 1);
+  h.y = (uint8_t*)a.y + n_big * (a.y_dtype == 0 ? 2 : 4);
+  launch_cfg_sch<Half>(h, sch, code, stream);
   return hipGetLastError();
 }
 

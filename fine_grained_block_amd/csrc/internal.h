@@ -47,6 +47,10 @@ struct GemmArgs {
 
 // Prefill (M > 64) dense GEMM and the grouped variant.
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream);
+// compute units of the current device; output columns of a dense prefill GEMM (N % 256 == 0) that
+// run as 256 x 256 tiles (the rest as 256 x 128 tiles)
+int cu_count();
+int64_t big_columns(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_check_offsets(const int32_t* offsets, int32_t E, int64_t total_M, int32_t* result,
                                 hipStream_t stream);
