@@ -590,19 +590,28 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
     Tile t;
     const int pid = xcd_remap(v, ntiles);
     const int in_group = GROUP_M * tiles_n;
-    const int first_m = (pid / in_group) * GROUP_M;
-    const int gsize = min(real_tiles_m - first_m, GROUP_M);
-    const int pid_m = first_m + (pid % in_group) % gsize;
-    t.n0 = (int64_t)((pid % in_group) / gsize) * C::BN;
     if constexpr (GROUPED) {
-      // the first expert whose tile-rows reach past pid_m (an empty expert's prefix equals the
-      // one before it, so the first lane past pid_m has tiles)
-      const int first = __builtin_amdgcn_readfirstlane(__ffsll((long long)__ballot(c_inc > pid_m)) - 1);
+      // Expert e owns tiles tiles_n * (tile-rows before e) onward; inside an expert the tiles
+      // run in bands of GROUP_M of its tile-rows, so a band's concurrent tiles share the
+      // expert's weight tiles (bands across experts mixed several experts' weights).  The
+      // expert is the first lane whose tile prefix reaches past pid (an empty expert's prefix
+      // equals the one before it).
+      const int first = __builtin_amdgcn_readfirstlane(__ffsll((long long)__ballot(c_inc * tiles_n > pid)) - 1);
       const int before = first > 0 ? __builtin_amdgcn_readlane(c_inc, first - 1) : 0;
+      const int mt = __builtin_amdgcn_readlane(c_inc, first) - before;
+      const int local = pid - before * tiles_n;
+      const int first_m = (local / in_group) * GROUP_M;
+      const int gsize = min(mt - first_m, GROUP_M);
+      const int pid_m = first_m + (local % in_group) % gsize;
+      t.n0 = (int64_t)((local % in_group) / gsize) * C::BN;
       t.e = first;
-      t.row0 = (int64_t)__builtin_amdgcn_readlane(c_off, first) + (int64_t)(pid_m - before) * C::BM;
+      t.row0 = (int64_t)__builtin_amdgcn_readlane(c_off, first) + (int64_t)pid_m * C::BM;
       t.row_end = __builtin_amdgcn_readlane(c_end, first);
     } else {
+      const int first_m = (pid / in_group) * GROUP_M;
+      const int gsize = min(real_tiles_m - first_m, GROUP_M);
+      const int pid_m = first_m + (pid % in_group) % gsize;
+      t.n0 = (int64_t)((pid % in_group) / gsize) * C::BN;
       t.e = 0;
       t.row0 = (int64_t)pid_m * C::BM;
       t.row_end = M;
