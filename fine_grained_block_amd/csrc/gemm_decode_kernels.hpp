@@ -10,13 +10,17 @@
 //     through LDS.  One launch.
 //   * 16 < M <= 64, weights of at most 16 MiB: the per-wave ring kernel with 32 or 64 activation
 //     rows, one launch.
-//   * 16 < M <= 64, larger weights: a workgroup of 8 waves per 128-row weight block over a K slice, weights,
-//     activations and their scales streamed through a 4-stage LDS ring shared by the waves; K is
-//     sliced only to occupy the CUs, and sliced shapes add their float32 partials [S][M][N] in a
-//     second, ordered launch.  (A reduction inside the same launch costs more on this multi-XCD
-//     part, whose L2s are not coherent with each other: with release fences the L2 is written
-//     back; with the partials stored and loaded at device scope past the L2 and a counter
-//     electing the last slice, 1.7-2.4x slower than the second launch.)
+//   * 16 < M <= 64, larger weights: a workgroup of 8 waves per 128-row weight block over a K
+//     slice, weights, activations and their scales streamed through a 4-stage LDS ring shared by
+//     the waves; K is sliced only to occupy the CUs, and sliced shapes add their float32 partials
+//     [S][M][N] in a second, ordered launch.  (A reduction inside the same launch costs more on
+//     this multi-XCD part, whose L2s are not coherent with each other: with release fences the L2
+//     is written back; with the partials stored and loaded at device scope past the L2 and a
+//     counter electing the last slice, 1.7-2.4x slower than the second launch.)
+//   * MoE with at most 64 rows per expert: the M <= 16 register kernel per (16 weight rows,
+//     expert), walking the expert's rows in passes of 16.
+//   * From bf16 activations, a few tokens: the per-wave ring kernel that quantizes each 1x128
+//     group itself before its MFMA.
 #pragma once
 #include "gemm_common.hpp"
 #include "internal.h"
