@@ -598,8 +598,12 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
     }
   };
 
-  if constexpr (SCH != 2)
+  if constexpr (SCH != 2) {
     for (int c = tid; c < nk; c += 512) sws[c] = load_sw<SWF>(p.s_w, (n0 / 128) * KB + kb0 + c);
+    // own LDS writes complete before the first step's barrier, which has no fence: LDS
+    // operations of different waves may be served out of order
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+  }
 
   v4f acc[MT];
 #pragma unroll

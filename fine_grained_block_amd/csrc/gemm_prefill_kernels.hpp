@@ -303,6 +303,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       const int b = idx / KB, k = idx - b * KB;
       sws[b * 256 + k] = load_sw<SWF>(p.s_w, sw_base + (n0 / 128 + b) * KB + k);
     }
+    // own LDS writes complete before the first step's barrier (a barrier without a fence)
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
   }
   const float* sw_lds = sws + (int)(nb - n0 / 128) * 256;
 
