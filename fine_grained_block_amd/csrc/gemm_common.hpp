@@ -66,17 +66,23 @@ __device__ __forceinline__ float load_sw(const void* s_w, int64_t idx) {
   }
 }
 
+// Two float32 values -> two bf16 (round to nearest even) packed in one dword, lo in bits 15:0:
+// one v_cvt_pk_bf16_f32 (element-wise casts convert one value per instruction and then need a
+// shift and an OR to pack).
+typedef float v2f_cvt __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_cvt{lo, hi}, v2bf));
+}
+
 // Store four consecutive output features of one token.
 template <int OUT>
 __device__ __forceinline__ void store4(void* y, int64_t ldy, int64_t m, int64_t n, v4f v) {
   if constexpr (OUT == 0) {
     uint16_t* p = reinterpret_cast<uint16_t*>(y) + m * ldy + n;
-    // float32 -> bf16 round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950)
     v2u w;
-    w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
-    w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+    w[0] = pack_bf16x2(v[0], v[1]);
+    w[1] = pack_bf16x2(v[2], v[3]);
     gstore<v2u>(p, w);
   } else {
     gstore<v4f>(reinterpret_cast<float*>(y) + m * ldy + n, v);

@@ -464,23 +464,25 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   constexpr int ROWB = C::BN * 2 + 16;  // padded LDS row: the 16 rows of a fragment hit distinct banks
   if constexpr (OUT == 0 && C::BM % 128 == 0 && 64 * ROWB <= C::STAGE) {
     constexpr int CPR = C::BN * 2 / 16;  // 16-byte chunks per output row
+    // a wave's token rows lie inside one 64-row chunk, so the round and the chunk that take them
+    // follow from the wave index alone (a wave-uniform branch: each wave converts its values once)
+    static_assert(64 % (C::BM / C::WM) == 0, "a wave's rows stay inside one 64-row chunk");
+    const int wrow = wm * (C::BM / C::WM);
 #pragma unroll
     for (int r = 0; r < C::BM / 128; ++r) {
       wg_barrier();
+      if ((wrow >> 7) == r) {
+        uint8_t* const half = (wrow & 64) ? stage1 : stage0;
 #pragma unroll
-      for (int j = 0; j < C::TM; ++j) {
-        const int ml = wm * (C::BM / C::WM) + j * 16 + (lane & 15);
-        if ((ml >> 7) == r) {
-          uint8_t* const half = (ml & 64) ? stage1 : stage0;
+        for (int j = 0; j < C::TM; ++j) {
+          const int ml = (wrow & 63) + j * 16 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < C::TN; ++i) {
             const int nl = wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4);
             uint2 w;
-            w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][0]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][1]) << 16);
-            w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][2]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][3]) << 16);
-            *reinterpret_cast<uint2*>(half + (ml & 63) * ROWB + nl * 2) = w;
+            w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+            *reinterpret_cast<uint2*>(half + ml * ROWB + nl * 2) = w;
           }
         }
       }
@@ -748,10 +750,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_prefill_persistent_kernel(
           for (int i = 0; i < C::TN; ++i) {
             const int nl = wn * 128 + i * 16 + 4 * (el >> 4);
             uint2 w;
-            w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][0]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][1]) << 16);
-            w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][2]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][3]) << 16);
+            w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
             *reinterpret_cast<uint2*>(stage1 + mh * ROW + (((nl >> 3) ^ (mh & 15)) << 4) + ((nl & 4) << 1)) = w;
           }
         }
