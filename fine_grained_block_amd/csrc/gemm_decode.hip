@@ -52,8 +52,23 @@ int mid_kpw(int64_t N, int64_t K) {
   return (KB + S - 1) / S;
 }
 
+// Waves (16 weight rows each) per workgroup of the 16 < M <= 64 kernel.  With at most 32
+// activation rows and 32-63 K-blocks, workgroups of 2 or 4 waves cover the weight rows without K
+// slices (one launch), 2 when that gives at most 256 workgroups, else 4 up to 512; otherwise 8
+// (one 128-row block).  Measured (graph loop, interleaved A/B, at M = 17/24/32): 6144x4096 with 2
+// waves 10.0-10.1 vs 10.2/10.5/11.0 us (8 waves, 4 K slices + reduction), 28672x4096 with 4
+// waves 25.5/25.9/26.5 vs 27.0/27.1/27.3 us (8 waves, one slice); at 64 rows (4 waves 30.3 vs
+// 28.5), 12 K-blocks (24576x1536) or 112-144 (4096x14336, 7168x18432) 8 waves stay ahead.
+int mid_waves(int64_t M, int64_t N, int64_t K) {
+  if (M > 32 || K < 32 * 128 || K >= 64 * 128) return 8;
+  if (N / 32 <= 256) return 2;
+  if (N / 64 <= 512) return 4;
+  return 8;
+}
+
 int decode_splits(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 || ring_mid_rows(N, K)) return 1;  // these kernels need no workspace
+  if (mid_waves(M, N, K) < 8) return 1;
   const int KB = (int)(K / 128);
   const int kpw = mid_kpw(N, K);
   return (KB + kpw - 1) / kpw;
@@ -126,16 +141,19 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
     return hipGetLastError();
   }
   {
-    const int kpw = mid_kpw(a.N, a.K);
     const int S = decode_splits(a.M, a.N, a.K);
-    const dim3 grid((unsigned)((a.N / 128) * S)), block(512);
+    const int nw = mid_waves(a.M, a.N, a.K);
+    const int kpw = S == 1 ? (int)(a.K / 128) : mid_kpw(a.N, a.K);
+    const dim3 grid((unsigned)((a.N / (16 * nw)) * S)), block(64 * nw);
     float* ws = reinterpret_cast<float*>(workspace);
-#define FGB_MID(MT_, SWF, OUT) \
-  hipLaunchKernelGGL((gemm_decode_mid_kernel<MT_, kMidStages, SWF, OUT>), grid, block, 0, stream, a, kpw, S, ws)
-#define FGB_MID_MT(SWF, OUT)                     \
-  do {                                           \
-    if (a.M <= 32) FGB_MID(2, SWF, OUT);         \
-    else FGB_MID(4, SWF, OUT);                   \
+#define FGB_MID(NW_, MT_, D_, SWF, OUT) \
+  hipLaunchKernelGGL((gemm_decode_mid_kernel<NW_, MT_, D_, SWF, OUT>), grid, block, 0, stream, a, kpw, S, ws)
+#define FGB_MID_MT(SWF, OUT)                                    \
+  do {                                                          \
+    if (a.M > 32) FGB_MID(8, 4, kMidStages, SWF, OUT);          \
+    else if (nw == 2) FGB_MID(2, 2, 6, SWF, OUT);               \
+    else if (nw == 4) FGB_MID(4, 2, 4, SWF, OUT);               \
+    else FGB_MID(8, 2, kMidStages, SWF, OUT);                   \
   } while (0)
     if (a.s_w_fmt == 0) {
       if (a.y_dtype == 0) FGB_MID_MT(0, 0); else FGB_MID_MT(0, 1);

@@ -520,31 +520,31 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_fused_quant_small_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// 16 < M <= 64: a workgroup of 8 waves owns one 128-row weight block (16 rows per wave) over a
-// slice of K-blocks.  The block's weight rows, the 16*MT activation rows (rows >= M repeat row
-// M-1; their results are dropped) and the activation scales of each K-block stream through a
-// ring of D LDS stages shared by the waves, with whole-line buffer-form direct copies issued
-// D-1 blocks ahead and one barrier per block; the activation stream is read once per 128 weight
+// 16 < M <= 64: a workgroup of NW waves owns 16*NW weight rows (16 per wave; 8 waves: one 128-row
+// weight block) over a slice of K-blocks.  The rows, the 16*MT activation rows (rows >= M repeat
+// row M-1; their results are dropped) and the activation scales of each K-block stream through a
+// ring of D LDS stages shared by the waves, with whole-line buffer-form direct copies issued D-1
+// blocks ahead and one barrier per block; the activation stream is read once per 16*NW weight
 // rows.  Slices (S > 1) write float32 partials [S][M][N] for the ordered reduction launch.
 // SCH and CODE as for the ring kernel (schemes 1 and 2 copy no activation scales; their scales
 // that do not vary along K multiply the finished sums, here or in the reduction).
 // ---------------------------------------------------------------------------------------------
-template <int MT, int D, int SWF, int OUT, int SCH = 0, int CODE = 0>
-__global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int kpw, int S, float* ws) {
+template <int NW, int MT, int D, int SWF, int OUT, int SCH = 0, int CODE = 0>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_decode_mid_kernel(GemmArgs p, int kpw, int S, float* ws) {
   static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
+  static_assert(NW == 2 || NW == 4 || NW == 8, "2, 4 or 8 waves");
   constexpr int MROWS = 16 * MT;
-  constexpr int WB = 128 * 128, AB = MROWS * 128, SB = 64 * 4;
+  constexpr int WB = 16 * NW * 128, AB = MROWS * 128, SB = 64 * 4;
   constexpr int STAGE = WB + AB + SB;
-  constexpr int A_GRP = MROWS / 8;                 // 8-row copy groups of the activation rows
-  constexpr int OPS = 2 + 1 + (SCH == 0 ? 1 : 0);  // copies per wave per block: W, A, scales
-  static_assert(D >= 3 && D <= 6, "three to six stages");
+  constexpr int A_GRP = MROWS / 8;                      // 8-row copy groups of the activation rows
+  constexpr int A_PER = A_GRP >= NW ? A_GRP / NW : 1;   // activation copies per wave per block
+  constexpr int OPS = 2 + A_PER + (SCH == 0 ? 1 : 0);   // copies per wave per block: W, A, scales
+  static_assert(D >= 3 && (D - 2) * OPS <= 63, "three or more stages, in-flight copies within vmcnt");
   static_assert(MT == 2 || MT == 4, "32 or 64 activation rows");
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[D > 3 ? STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t st4[D > 4 ? STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t st5[D > 5 ? STAGE : 16];
+  static_assert(D * STAGE + 1024 <= 160 * 1024, "the ring fits in LDS");
+  // one array: the stages' LDS reads are asm blocks that wait for themselves (below), so the
+  // compiler need not tell the stages apart
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[D * STAGE];
   __shared__ float sws[256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -553,22 +553,24 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
   const int nt = blockIdx.x / S, split = blockIdx.x - nt * S;
   const int kb0 = split * kpw;
   const int nk = min(KB, kb0 + kpw) - kb0;
-  const int64_t n0 = (int64_t)nt * 128;
+  const int64_t n0 = (int64_t)nt * 16 * NW;
 
-  // copy sources: lane i of 8-row group q takes row 8q + i/8, logical chunk (i%8) ^ g(row); the
-  // activation groups past A_GRP repeat earlier ones (same bytes to the same place: no branch)
+  // copy sources: lane i of 8-row group q takes row 8q + i/8, logical chunk (i%8) ^ g(row); with
+  // more waves than activation groups, waves repeat earlier groups (same bytes to the same place)
   uint32_t woff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int r = 8 * (wave + 8 * i) + (lane >> 3);
+    const int r = 8 * (wave + NW * i) + (lane >> 3);
     woff[i] = (uint32_t)(r * K + (((lane & 7) ^ swz_g(r)) * 16));
   }
-  const int aq = wave % A_GRP;
-  uint32_t aoff;
-  {
-    const int r = 8 * aq + (lane >> 3);
+  int agrp[A_PER];
+  uint32_t aoff[A_PER];
+#pragma unroll
+  for (int j = 0; j < A_PER; ++j) {
+    agrp[j] = A_GRP >= NW ? wave + NW * j : wave % A_GRP;
+    const int r = 8 * agrp[j] + (lane >> 3);
     const int64_t m = r < M ? r : M - 1;
-    aoff = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
+    aoff[j] = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
   }
   const uint32_t soff = (uint32_t)((lane < M ? lane : M - 1) * 4);
 
@@ -581,25 +583,18 @@ __global__ __launch_bounds__(512, 1) void gemm_decode_mid_kernel(GemmArgs p, int
     const uint32_t koff = (uint32_t)kb * 128;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + 8 * i) * 1024), 16, woff[i], koff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + WB + aq * 1024), 16, aoff, koff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + NW * i) * 1024), 16, woff[i], koff, 0, 0);
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + WB + agrp[j] * 1024), 16, aoff[j], koff, 0, 0);
     if constexpr (SCH == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(st + WB + AB), 4, soff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
 #endif
   };
-  auto stage = [&](int i) -> uint8_t* {
-    switch (i) {
-      case 0: return st0;
-      case 1: return st1;
-      case 2: return st2;
-      case 3: return st3;
-      case 4: return st4;
-      default: return st5;
-    }
-  };
+  auto stage = [&](int i) -> uint8_t* { return ring + i * STAGE; };
 
   if constexpr (SCH != 2) {
-    for (int c = tid; c < nk; c += 512) sws[c] = load_sw<SWF>(p.s_w, (n0 / 128) * KB + kb0 + c);
+    for (int c = tid; c < nk; c += 64 * NW) sws[c] = load_sw<SWF>(p.s_w, (n0 / 128) * KB + kb0 + c);
     // own LDS writes complete before the first step's barrier, which has no fence: LDS
     // operations of different waves may be served out of order
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)

@@ -32,16 +32,25 @@ void launch_small_sch(const GemmArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_decode_small_kernel<WK, SWF, 1, 0, SCH, CODE>), grid, block, 0, stream, a);
 }
 
+template <int NW, int MT, int D, int SCH, int SWF, int CODE>
+void launch_mid_nw(const GemmArgs& a, int kpw, int S, float* ws, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.N / (16 * NW)) * S)), block(64 * NW);
+  if (a.y_dtype == 0)
+    hipLaunchKernelGGL((gemm_decode_mid_kernel<NW, MT, D, SWF, 0, SCH, CODE>), grid, block, 0, stream, a, kpw, S, ws);
+  else
+    hipLaunchKernelGGL((gemm_decode_mid_kernel<NW, MT, D, SWF, 1, SCH, CODE>), grid, block, 0, stream, a, kpw, S, ws);
+}
+
 template <int MT, int SCH, int SWF, int CODE>
 void launch_mid_sch(const GemmArgs& a, void* workspace, hipStream_t stream) {
-  const int kpw = mid_kpw(a.N, a.K);
   const int S = decode_splits(a.M, a.N, a.K);
-  const dim3 grid((unsigned)((a.N / 128) * S)), block(512);
+  const int nw = mid_waves(a.M, a.N, a.K);
+  const int kpw = S == 1 ? (int)(a.K / 128) : mid_kpw(a.N, a.K);
   float* ws = reinterpret_cast<float*>(workspace);
-  if (a.y_dtype == 0)
-    hipLaunchKernelGGL((gemm_decode_mid_kernel<MT, kMidStages, SWF, 0, SCH, CODE>), grid, block, 0, stream, a, kpw, S, ws);
-  else
-    hipLaunchKernelGGL((gemm_decode_mid_kernel<MT, kMidStages, SWF, 1, SCH, CODE>), grid, block, 0, stream, a, kpw, S, ws);
+  // (mid_waves returns 2 or 4 only for at most 32 activation rows)
+  if (MT == 2 && nw == 2) launch_mid_nw<2, 2, 6, SCH, SWF, CODE>(a, kpw, S, ws, stream);
+  else if (MT == 2 && nw == 4) launch_mid_nw<4, 2, 4, SCH, SWF, CODE>(a, kpw, S, ws, stream);
+  else launch_mid_nw<8, MT, kMidStages, SCH, SWF, CODE>(a, kpw, S, ws, stream);
   if (S == 1) return;
   const int64_t total = a.M * (a.N / 4);
   const dim3 rgrid((unsigned)((total + 255) / 256));

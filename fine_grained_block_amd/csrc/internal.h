@@ -81,6 +81,7 @@ bool decode_ring(int64_t N, int64_t K);
 bool ring_mid_rows(int64_t N, int64_t K);
 int mid_kpw(int64_t N, int64_t K);
 constexpr int kMidStages = 4;  // LDS stages of the shared-ring kernel (measured: 4 >= 5, 6)
+int mid_waves(int64_t M, int64_t N, int64_t K);
 int decode_splits(int64_t M, int64_t N, int64_t K);
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream);

@@ -85,10 +85,14 @@ def test_gemm_validation(L):
     assert _gemm(L, lda=1032) == ERR["ALIGN"]
     assert _gemm(L, ld_sa=258) == ERR["ALIGN"]
     # the decode path for 16 < M <= 64 needs a workspace when it slices K; M <= 16 and prefill do not
-    need = L.fgb_gemm_workspace_bytes(32, 6144, 4096)
+    need = L.fgb_gemm_workspace_bytes(40, 6144, 4096)
     assert need > 0
-    assert _gemm(L, M=32, N=6144, K=4096, lda=4096, ldy=6144, ld_sa=32) == ERR["WORKSPACE"]
-    assert _gemm(L, M=32, N=6144, K=4096, lda=4096, ldy=6144, ld_sa=32, ws=FAKE, wsb=need - 1) == ERR["WORKSPACE"]
+    assert _gemm(L, M=40, N=6144, K=4096, lda=4096, ldy=6144, ld_sa=40) == ERR["WORKSPACE"]
+    assert _gemm(L, M=40, N=6144, K=4096, lda=4096, ldy=6144, ld_sa=40, ws=FAKE, wsb=need - 1) == ERR["WORKSPACE"]
+    # at most 32 rows with 32-63 K-blocks: workgroups of 2 or 4 waves over the whole K, no slices
+    assert L.fgb_gemm_workspace_bytes(32, 6144, 4096) == 0
+    assert L.fgb_gemm_workspace_bytes(17, 10240, 5248) == 0
+    assert L.fgb_gemm_workspace_bytes(32, 4096, 8192) > 0
     # weights of at most 16 MiB take the one-launch ring kernel at 16 < M <= 64
     assert L.fgb_gemm_workspace_bytes(64, 4096, 4096) == 0
     assert L.fgb_gemm_workspace_bytes(16, 4096, 4096) == 0

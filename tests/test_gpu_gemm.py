@@ -222,6 +222,18 @@ def test_decode_mid_rows_kernel(dev, M, fmt):
         _mid_rows_case(dev, M, N, K, fmt)
 
 
+@pytest.mark.parametrize("M", [17, 24, 32, 33])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_decode_mid_rows_fewer_waves(dev, M, fmt):
+    """At most 32 activation rows with 32-63 K-blocks: workgroups of 2 waves (N = 4096, K = 4608:
+    128 workgroups, 36 blocks) or 4 waves (N = 10240, K = 5248: 160 workgroups, 41 blocks, odd
+    against the ring depth) over the whole K, one launch; M = 33 takes the 8-wave kernel with K
+    slices on the same shapes."""
+    for (N, K) in [(4096, 4608), (10240, 5248)]:
+        assert (fgb.gemm_workspace_bytes(M, N, K) == 0) == (M <= 32)
+        _mid_rows_case(dev, M, N, K, fmt)
+
+
 @pytest.mark.parametrize("M,N,K", [(1000, 32768, 1024), (1700, 16384, 2048), (4096, 8192, 2048), (520, 65536, 1280)])
 @pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
 def test_persistent_prefill_tiles(dev, M, N, K, fmt):

@@ -150,7 +150,7 @@ def test_scaled_gemm_parity(dev, code, act, weight):
 # K slice (>= 160 weight blocks of 128 rows) or in several, with partials and the scaling
 # reduction (fewer blocks)
 DECODE_PATHS = [(4, 2048, 24576), (16, 2048, 24576), (17, 20480, 1024), (33, 20480, 1024), (64, 20480, 1024),
-                (40, 4096, 8192), (64, 4096, 14336)]
+                (40, 4096, 8192), (64, 4096, 14336), (24, 4096, 4608), (32, 10240, 5248)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_PATHS)
