@@ -192,23 +192,42 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
 // ---------------------------------------------------------------------------------------------
 namespace {
 
-template <int MODE>
+template <int MODE, int MTM>
 void launch_moe(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.N / 16), (unsigned)a.E), block(256);
   if (a.s_w_fmt == 0) {
-    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_small_kernel<4, 0, 0, MODE>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_decode_small_kernel<4, 0, 1, MODE>), grid, block, 0, stream, a);
+    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_small_kernel<4, 0, 0, MODE, 0, 0, MTM>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_decode_small_kernel<4, 0, 1, MODE, 0, 0, MTM>), grid, block, 0, stream, a);
   } else {
-    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_small_kernel<4, 1, 0, MODE>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_decode_small_kernel<4, 1, 1, MODE>), grid, block, 0, stream, a);
+    if (a.y_dtype == 0) hipLaunchKernelGGL((gemm_decode_small_kernel<4, 1, 0, MODE, 0, 0, MTM>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_decode_small_kernel<4, 1, 1, MODE, 0, 0, MTM>), grid, block, 0, stream, a);
   }
 }
 
 }  // namespace
 
+// Rows per weight pass: up to 32 (two 16-row tiles per weight fragment) when an expert can have
+// more than 16 rows and K has at least 32 blocks, else 16.  Measured (32 experts, graph loop,
+// interleaved A/B, bitwise equal outputs): 4096x7168 with 64-row batched slots for 64 / 32
+// tokens 230 -> 215 / 176 -> 173 us, 8 / 16 tokens within 1%; on 7168x2048 (4 K-blocks per
+// wave) two-tile passes were 7-10% slower below 64 tokens, passes of 64 rows (212 VGPRs: half
+// the waves per SIMD) slower everywhere but 4096x7168 at 64 tokens.
+namespace {
+int moe_rows_per_pass(const GemmArgs& a, int mode) {
+  const int64_t most = mode == 1 ? a.M : a.slot;  // most rows one expert can have
+  return most > 16 && a.K >= 32 * 128 ? 32 : 16;
+}
+}  // namespace
+
 hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, hipStream_t stream) {
-  if (mode == 1) launch_moe<1>(a, stream);
-  else launch_moe<2>(a, stream);
+  const bool two = moe_rows_per_pass(a, mode) == 32;
+  if (mode == 1) {
+    if (two) launch_moe<1, 2>(a, stream);
+    else launch_moe<1, 1>(a, stream);
+  } else {
+    if (two) launch_moe<2, 2>(a, stream);
+    else launch_moe<2, 1>(a, stream);
+  }
   return hipGetLastError();
 }
 

@@ -22,6 +22,8 @@
 //   * From bf16 activations, a few tokens: the per-wave ring kernel that quantizes each 1x128
 //     group itself before its MFMA.
 #pragma once
+#include <type_traits>
+
 #include "gemm_common.hpp"
 #include "internal.h"
 #include "quant_common.hpp"
@@ -724,14 +726,19 @@ constexpr int CHS = 2;  // K-blocks per register chunk in the small-M kernel (4:
 // MODE (MoE with at most 64 rows per expert, grid.y = expert e): 1 = the expert's rows are
 // offsets[e] .. offsets[e+1]-1 of the contiguous grouped layout; 2 = rows e*slot .. e*slot +
 // counts[e] - 1 of the masked batched layout.  The workgroup walks its expert's rows in passes of
-// 16 (a pass after the first re-reads the weight tile its CU has just streamed), and a workgroup
-// whose expert has no rows exits after its 4-byte count load, so only routed experts' weights
-// are read.  SCH and CODE as for the ring kernel (MoE layouts: scheme 0 only).
-template <int WK, int SWF, int OUT, int MODE = 0, int SCH = 0, int CODE = 0>
+// up to 16 * MT_MAX rows (MT_MAX = 2: two 16-row tiles share each weight fragment, one K-block
+// per register chunk), each pass streaming the weight tile again (a pass after the first mostly
+// from the last-level cache), and a workgroup whose expert has no rows exits after its 4-byte
+// count load, so only routed experts' weights are read.  Every row's sums are those of a 16-row
+// pass (same K split, block order and reduction order).  SCH and CODE as for the ring kernel
+// (MoE layouts: scheme 0 only).
+template <int WK, int SWF, int OUT, int MODE = 0, int SCH = 0, int CODE = 0, int MT_MAX = 1>
 __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) {
   static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
   static_assert(MODE == 0 || SCH == 0, "MoE layouts use the 1x128-group scheme");
-  __shared__ v4f red[WK > 1 ? WK - 1 : 1][64];
+  static_assert(MT_MAX == 1 || MT_MAX == 2, "16-row tiles per pass: 1 or 2");
+  static_assert(MODE != 0 || MT_MAX == 1, "at most 16 rows without an expert layout");
+  __shared__ v4f red[WK > 1 ? WK - 1 : 1][MT_MAX][64];
   __shared__ __attribute__((aligned(1024))) uint8_t tile[WK][CHS][16 * 128];  // per wave, per block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // this workgroup's rows: row_base .. r_end - 1 (MoE: the expert's rows, in passes of 16)
@@ -765,89 +772,122 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_small_kernel(GemmArgs p) 
   const int wo0 = swz(lane >> 3, lane & 7), wo1 = swz((lane >> 3) + 8, lane & 7);
   const int ro0 = swz(r, 2 * g), ro1 = swz(r, 2 * g + 1);
 
-  // One pass over the rows row_base .. row_base + M - 1 (M <= 16).
-  auto pass = [&](const int64_t row_base, const int64_t M) {
-    const int64_t m = row_base + (r < M ? r : M - 1);  // rows past M repeat row M-1
-    const uint8_t* arow = p.a_q + m * p.lda + (int64_t)kb0 * 128 + 32 * g;
-    const float* sarow = p.s_a + (int64_t)kb0 * p.ld_sa + m;
-    int4 wv[2][CHS][2], av[2][CHS][2];
-    float sav[2][CHS], swv[2][CHS];
+  // One pass over the rows row_base .. row_base + M - 1 (M <= 16 MT) as MT tiles of 16 rows.
+  auto pass = [&](auto mt_c, const int64_t row_base, const int64_t M) {
+    constexpr int MT = decltype(mt_c)::value;
+    constexpr int CH = MT == 1 ? CHS : 1;  // K-blocks per register chunk
+    const uint8_t* arow[MT];
+    const float* sarow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int64_t m = row_base + (16 * t + r < M ? 16 * t + r : M - 1);  // rows past M repeat row M-1
+      arow[t] = p.a_q + m * p.lda + (int64_t)kb0 * 128 + 32 * g;
+      sarow[t] = p.s_a + (int64_t)kb0 * p.ld_sa + m;
+    }
+    int4 wv[2][CH][2], av[2][CH][MT][2];
+    float sav[2][CH][MT], swv[2][CH];
     auto load_chunk = [&](int c, int buf) {
 #pragma unroll
-      for (int u = 0; u < CHS; ++u) {
+      for (int u = 0; u < CH; ++u) {
         if (c + u < nk) {
           const int64_t off = (int64_t)(c + u) * 128;
           wv[buf][u][0] = gload_i4(wline + off);
           wv[buf][u][1] = gload_i4(wline + 8 * K + off);
-          av[buf][u][0] = gload_i4(arow + off);
-          av[buf][u][1] = gload_i4(arow + off + 16);
-          if constexpr (SCH == 0) sav[buf][u] = gload<float>(sarow + (int64_t)(c + u) * p.ld_sa);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            av[buf][u][t][0] = gload_i4(arow[t] + off);
+            av[buf][u][t][1] = gload_i4(arow[t] + off + 16);
+            if constexpr (SCH == 0) sav[buf][u][t] = gload<float>(sarow[t] + (int64_t)(c + u) * p.ld_sa);
+          }
           if constexpr (SCH != 2) swv[buf][u] = load_sw<SWF>(p.s_w, swbase + c + u);
         }
       }
     };
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     auto compute_chunk = [&](int c, int buf) {
 #pragma unroll
-      for (int u = 0; u < CHS; ++u) {
+      for (int u = 0; u < CH; ++u) {
         if (c + u < nk) {
           // (one wave's LDS operations complete in order: the reads see the writes, and the next
           // chunk's writes to this tile follow these reads)
-          uint8_t* t = &tile[wave][u][0];
-          *reinterpret_cast<int4*>(t + wo0) = wv[buf][u][0];
-          *reinterpret_cast<int4*>(t + wo1) = wv[buf][u][1];
-          const int4 lo = *reinterpret_cast<const int4*>(t + ro0);
-          const int4 hi = *reinterpret_cast<const int4*>(t + ro1);
-          v8i af, bf;
+          uint8_t* tl = &tile[wave][u][0];
+          *reinterpret_cast<int4*>(tl + wo0) = wv[buf][u][0];
+          *reinterpret_cast<int4*>(tl + wo1) = wv[buf][u][1];
+          const int4 lo = *reinterpret_cast<const int4*>(tl + ro0);
+          const int4 hi = *reinterpret_cast<const int4*>(tl + ro1);
+          v8i af;
           af[0] = lo.x; af[1] = lo.y; af[2] = lo.z; af[3] = lo.w;
           af[4] = hi.x; af[5] = hi.y; af[6] = hi.z; af[7] = hi.w;
-          bf[0] = av[buf][u][0].x; bf[1] = av[buf][u][0].y; bf[2] = av[buf][u][0].z; bf[3] = av[buf][u][0].w;
-          bf[4] = av[buf][u][1].x; bf[5] = av[buf][u][1].y; bf[6] = av[buf][u][1].z; bf[7] = av[buf][u][1].w;
-          if constexpr (SCH == 0) acc += mfma_e4m3_16x16x128(af, bf) * (sav[buf][u] * swv[buf][u]);
-          else if constexpr (SCH == 1) acc += mfma_f8_16x16x128<CODE>(af, bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}) * swv[buf][u];
-          else acc = mfma_f8_16x16x128<CODE>(af, bf, acc);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            v8i bf;
+            bf[0] = av[buf][u][t][0].x; bf[1] = av[buf][u][t][0].y; bf[2] = av[buf][u][t][0].z; bf[3] = av[buf][u][t][0].w;
+            bf[4] = av[buf][u][t][1].x; bf[5] = av[buf][u][t][1].y; bf[6] = av[buf][u][t][1].z; bf[7] = av[buf][u][t][1].w;
+            if constexpr (SCH == 0) acc[t] += mfma_e4m3_16x16x128(af, bf) * (sav[buf][u][t] * swv[buf][u]);
+            else if constexpr (SCH == 1) acc[t] += mfma_f8_16x16x128<CODE>(af, bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}) * swv[buf][u];
+            else acc[t] = mfma_f8_16x16x128<CODE>(af, bf, acc[t]);
+          }
         }
       }
     };
     load_chunk(0, 0);
-    for (int c = 0; c < nk; c += 2 * CHS) {
-      if (c + CHS < nk) load_chunk(c + CHS, 1);
+    for (int c = 0; c < nk; c += 2 * CH) {
+      if (c + CH < nk) load_chunk(c + CH, 1);
       compute_chunk(c, 0);
-      if (c + CHS < nk) {
-        if (c + 2 * CHS < nk) load_chunk(c + 2 * CHS, 0);
-        compute_chunk(c + CHS, 1);
+      if (c + CH < nk) {
+        if (c + 2 * CH < nk) load_chunk(c + 2 * CH, 0);
+        compute_chunk(c + CH, 1);
       }
     }
-    auto finish = [&]() {
-      if (r < M) {
+    auto finish = [&](int t) {
+      const int64_t ml = 16 * t + r;
+      if (ml < M) {
         if constexpr (SCH != 0) {
           // scales that do not vary along K: the token's (or the tensor's), then the channels'
-          acc = acc * gload<float>(p.s_a + (p.a_kind == 2 ? 0 : row_base + r));
-          if constexpr (SCH == 2) acc = acc * gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n0 + 4 * g);
+          acc[t] = acc[t] * gload<float>(p.s_a + (p.a_kind == 2 ? 0 : row_base + ml));
+          if constexpr (SCH == 2) acc[t] = acc[t] * gload<v4f>(reinterpret_cast<const float*>(p.s_w) + n0 + 4 * g);
         }
-        store4<OUT>(p.y, p.ldy, row_base + r, n0 + 4 * g, acc);
+        store4<OUT>(p.y, p.ldy, row_base + ml, n0 + 4 * g, acc[t]);
       }
     };
     if constexpr (WK > 1) {
-      if (wave > 0) red[wave - 1][lane] = acc;
+      if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[wave - 1][t][lane] = acc[t];
+      }
       __syncthreads();
       if constexpr (MODE == 0) {
         if (wave > 0) return;
       }
       if (wave == 0) {
 #pragma unroll
-        for (int w = 0; w < WK - 1; ++w) acc += red[w][lane];
-        finish();
+        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+          for (int w = 0; w < WK - 1; ++w) acc[t] += red[w][t][lane];
+          finish(t);
+        }
       }
       if constexpr (MODE != 0) __syncthreads();  // the next pass rewrites red
     } else {
-      finish();
+#pragma unroll
+      for (int t = 0; t < MT; ++t) finish(t);
     }
   };
   if constexpr (MODE == 0) {
-    pass(0, p.M);
+    pass(std::integral_constant<int, 1>{}, 0, p.M);
   } else {
-    for (int64_t rb = row_base; rb < r_end; rb += 16) pass(rb, min((int64_t)16, r_end - rb));
+    for (int64_t rb = row_base; rb < r_end;) {
+      const int64_t left = r_end - rb;
+      if (MT_MAX == 2 && left > 16) {
+        pass(std::integral_constant<int, MT_MAX>{}, rb, left < 32 ? left : 32);
+        rb += 32;
+      } else {
+        pass(std::integral_constant<int, 1>{}, rb, left < 16 ? left : 16);
+        rb += 16;
+      }
+    }
   }
 }
 

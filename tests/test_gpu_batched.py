@@ -113,3 +113,39 @@ def test_grouped_decode_all_rows_in_one_expert(dev):
                   torch.from_numpy(sw[5]).to(dev), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(y, yd)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_moe_decode_two_tile_passes(dev, fmt):
+    """Experts with more than 16 rows and K of at least 32 blocks: the per-expert streaming kernel
+    takes 32 rows per weight pass (two 16-row tiles share each weight fragment).  Slot counts 0,
+    16, 17 (a one-row second tile), 33 (a two-tile pass and a one-row pass) and 64; against the
+    oracle, bf16 equal to the RNE of float32, padding untouched, and the grouped layout of the
+    same rows (33 in all, the same kernel) equal bit for bit."""
+    E, N, K, max_m = 5, 256, 4096, 64
+    counts = np.array([64, 0, 17, 33, 16])
+    x = workloads.activations(E * max_m, K, key=(3, 74, 0, 0))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, fmt, 11)
+    yref, valid = gemm.batched_ref(aq, sa, wq, sw, counts, max_m, fmt)
+    wqd, swd = torch.from_numpy(wq).to(dev), torch.from_numpy(sw).to(dev)
+    args = (torch.from_numpy(aq).to(dev), sa_device(sa, dev), wqd, swd,
+            torch.from_numpy(counts.astype(np.int32)).to(dev), max_m)
+    outs = {}
+    for dt in (torch.float32, torch.bfloat16):
+        out = torch.full((E * max_m, N), -7.0, dtype=dt, device=dev)
+        fgb.batched_gemm(*args, out=out)
+        torch.cuda.synchronize()
+        outs[dt] = out
+        o = out.float().cpu().numpy().astype(np.float64)
+        assert np.all(o[~valid] == -7.0), "padding rows were written"
+        (check_t1 if dt == torch.float32 else check_t2)(o[valid], yref[valid])
+    y32 = outs[torch.float32].cpu().numpy().astype(np.float64)
+    assert np.array_equal(bf16_tensor_to_f64(outs[torch.bfloat16])[valid], gemm.bf16_rne(y32[valid]))
+    # experts 2 and 3 alone in the grouped layout (33 rows in all: the same per-expert kernel)
+    sub = np.array([0, 0, 17, 33, 0])
+    rows = np.concatenate([np.arange(e * max_m, e * max_m + sub[e]) for e in range(E)])
+    yg = fgb.grouped_gemm(torch.from_numpy(aq[rows]).to(dev), sa_device(sa[rows], dev), wqd, swd,
+                          torch.from_numpy(workloads.offsets_from_counts(sub)).to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(yg.cpu().numpy().astype(np.float64), y32[rows])
