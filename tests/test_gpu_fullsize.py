@@ -87,8 +87,9 @@ def test_decode_full_shapes(dev, name, N, K):
 
 @pytest.mark.parametrize("proj", ["gate_up", "down"])
 def test_moe_grouped_full(dev, proj):
-    """32 experts, 4096 tokens routed top-8 with Zipf(1.1) expert popularity (32768 rows); the
-    first and last rows of six experts (the most and least loaded among them) are checked."""
+    """32 experts, 4096 tokens routed top-8 with Zipf(1.1) expert popularity (32768 rows); in
+    every expert its first and last rows, both sides of its first 256-row tile edge and two random
+    rows, on two sampled weight blocks (the last always)."""
     cfg = workloads.MOE
     E = cfg["E"]
     N, K = cfg[proj]
@@ -102,14 +103,14 @@ def test_moe_grouped_full(dev, proj):
     off = torch.from_numpy(offsets).to(dev)
     y = fgb.grouped_gemm(q, sa, wq.view(E, N, K), sw.view(E, N // 128, K // 128), off)
     torch.cuda.synchronize()
-    order = np.argsort(counts)
-    experts = np.unique(np.concatenate([order[:2], order[-2:], order[E // 2 - 1:E // 2 + 1]]))
     rng = np.random.default_rng(seed)
-    for e in experts:
-        if counts[e] == 0:
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 <= r0:
             continue
-        rows = np.unique([offsets[e], offsets[e + 1] - 1])
-        _, cols = _pick(rng, 1, N)
+        rows = [r0, r1 - 1] + [r for r in (r0 + 255, r0 + 256) if r < r1]
+        rows = np.unique(np.concatenate([rows, rng.integers(r0, r1, size=2)]))
+        _, cols = _pick(rng, 1, N, nblocks=2)
         aq, sa_o = blockquant.act_quant(_bits(x[_idx(rows, dev)]))
         wq_s, sw_s = blockquant.weight_quant(_bits(w[_idx(e * N + cols, dev)]), "f32")
         yref = gemm.gemm_ref(aq, sa_o, wq_s, sw_s, "f32")
