@@ -354,3 +354,59 @@ def test_repeated_runs_are_bitwise_identical(dev):
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32)), "grouped"
+
+
+def _random_operands(M, N, K, fmt, seed):
+    """Random finite E4M3 codes and positive scales (no quantization step: the GEMM alone)."""
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    rng = np.random.default_rng(seed)
+    aq = rng.choice(finite, size=(M, K))
+    wq = rng.choice(finite, size=(N, K))
+    sa = (rng.uniform(0.25, 4.0, size=(M, K // 128)) / 448).astype(np.float32)
+    if fmt == "f32":
+        sw = (rng.uniform(0.25, 4.0, size=(N // 128, K // 128)) / 448).astype(np.float32)
+    else:
+        sw = rng.integers(112, 124, size=(N // 128, K // 128), dtype=np.uint8)
+    return aq, sa, wq, sw
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 24, 64, 300])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_maximum_k(dev, M, fmt):
+    """K = 32768, the largest K the library accepts (256 K-blocks), on every M-dependent path at
+    N = 1024: the decode register kernel (M <= 16), the shared-ring kernel in 26 K slices with
+    the ordered reduction (M = 24, 64), prefill tiles (M = 300, the weight-block scales of a tile
+    staged at full length)."""
+    ops = _random_operands(M, 1024, 32768, fmt, seed=4000 + M)
+    yref = gemm.gemm_ref_fast(*ops, fmt)
+    y32 = _run(ops, dev, torch.float32).cpu().numpy()
+    check_t1(y32, yref)
+    y16 = _run(ops, dev, torch.bfloat16)
+    assert np.array_equal(bf16_tensor_to_f64(y16), gemm.bf16_rne(y32.astype(np.float64)))
+
+
+def test_activation_offsets_near_4gib(dev):
+    """M * K just below 2^32 (131071 rows of K = 32768, 4 GiB - 32 KiB of activation codes): the
+    copies' 32-bit row offsets run up to the limit the library validates.  Codes and scales are
+    drawn on the device; sampled rows (the first, both sides of the 2^31-byte offset, the last
+    tile's rows, the last) are checked against the oracle on the bytes the device holds."""
+    M, N, K = 131071, 256, 32768
+    assert M * K < 2 ** 32 <= (M + 1) * K
+    g = torch.Generator(device=dev)
+    g.manual_seed(31)
+    aq = torch.randint(0, 0x7F, (M, K), dtype=torch.uint8, device=dev, generator=g)
+    aq |= torch.randint(0, 2, (M, K), dtype=torch.uint8, device=dev, generator=g) << 7
+    ld_sa = (M + 3) // 4 * 4
+    sa = torch.rand((K // 128, ld_sa), device=dev, generator=g) * (3.75 / 448) + 0.25 / 448
+    _, _, wq_np, sw_np = _random_operands(1, N, K, "f32", seed=4100)
+    wq, sw = torch.from_numpy(wq_np).to(dev), torch.from_numpy(sw_np).to(dev)
+    y = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    half = (2 ** 31) // K
+    rows = np.unique(np.array([0, 1, half - 1, half, half + 1, M - 256, M - 200, M - 2, M - 1]))
+    ridx = torch.from_numpy(rows).to(dev)
+    aq_s = aq[ridx].cpu().numpy()
+    sa_s = sa[:, ridx].t().contiguous().cpu().numpy()
+    yref = gemm.gemm_ref(aq_s, sa_s, wq_np, sw_np, "f32")
+    check_t1(y[ridx].cpu().numpy(), yref)
