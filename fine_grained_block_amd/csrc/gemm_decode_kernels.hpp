@@ -10,15 +10,17 @@
 //     through LDS.  One launch.
 //   * 16 < M <= 64, weights of at most 16 MiB: the per-wave ring kernel with 32 or 64 activation
 //     rows, one launch.
-//   * 16 < M <= 64, larger weights: a workgroup of 8 waves per 128-row weight block over a K
-//     slice, weights, activations and their scales streamed through a 4-stage LDS ring shared by
-//     the waves; K is sliced only to occupy the CUs, and sliced shapes add their float32 partials
-//     [S][M][N] in a second, ordered launch.  (A reduction inside the same launch costs more on
+//   * 16 < M <= 64, larger weights: a workgroup of 2, 4 or 8 waves (16 weight rows each) over a
+//     K slice, weights, activations and their scales streamed through an LDS ring shared by the
+//     waves; 8-wave workgroups (one 128-row weight block) slice K only to occupy the CUs, and
+//     sliced shapes add their float32 partials [S][M][N] in a second, ordered launch; with at
+//     most 32 activation rows and 32-63 K-blocks, 2- or 4-wave workgroups cover the weight rows
+//     over the whole K in one launch.  (A reduction inside the same launch costs more on
 //     this multi-XCD part, whose L2s are not coherent with each other: with release fences the L2
 //     is written back; with the partials stored and loaded at device scope past the L2 and a
 //     counter electing the last slice, 1.7-2.4x slower than the second launch.)
 //   * MoE with at most 64 rows per expert: the M <= 16 register kernel per (16 weight rows,
-//     expert), walking the expert's rows in passes of 16.
+//     expert), walking the expert's rows in passes of 16 or 32.
 //   * From bf16 activations, a few tokens: the per-wave ring kernel that quantizes each 1x128
 //     group itself before its MFMA.
 #pragma once
