@@ -2,7 +2,7 @@
 entry point (fgb_w8a8_block_gemm, given a workspace) and the oracle, through the C-ABI.
 
 Two workspace-needing decode calls in a row, the second with a smaller plan, then calls that
-need no scratch (prefill, M <= 16); the library's scratch keeps the previous call's contents,
+need no scratch (prefill, M <= 16, 24 rows on 2-wave workgroups); the library's scratch keeps the previous call's contents,
 which must not matter.  Same kernels, so the outputs are equal bit for bit; both are also held
 to the oracle's tolerance."""
 import numpy as np
@@ -30,8 +30,10 @@ def _operands(M, N, K, seed):
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_noalloc_matches_workspace_entry(dev, out_dtype):
     # (64, 6144, 4096): 5 K slices, 7.9 MB of partials; (40, 1024, 16512): 15 slices, 2.4 MB;
-    # then a prefill call and an M <= 16 call, which use no scratch
-    shapes = [(64, 6144, 4096), (40, 1024, 16512), (300, 1024, 1024), (8, 2048, 2048)]
+    # then calls that use no scratch: prefill, M <= 16, and 24 rows over 32 K-blocks (2-wave
+    # workgroups over the whole K)
+    shapes = [(64, 6144, 4096), (40, 1024, 16512), (300, 1024, 1024), (8, 2048, 2048), (24, 6144, 4096)]
+    assert fgb.gemm_workspace_bytes(*shapes[4]) == 0
     assert fgb.gemm_workspace_bytes(*shapes[0]) > fgb.gemm_workspace_bytes(*shapes[1]) > 0
     for i, (M, N, K) in enumerate(shapes):
         ops = _operands(M, N, K, 500 + i)
