@@ -479,8 +479,8 @@ def main():
         print(json.dumps(t))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the layers would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -19,7 +19,7 @@ Pins (see tests/test_oracle_*.py): exhaustive code tables against the formats' p
 and NaN/inf sets and against torch's float8 dtypes; brute-force nearest-code searches for the
 encoders; closed forms for UE8M0; quantization invariants; hand-worked golden fixtures; a dense
 float64 brute force and an exact-integer special case for the GEMM.  Parity unpinned: none of
-the functions above; the GEMM's float32 summation order on the GPU is judged by tolerance.
+the functions above; the GEMM's float32 summation order on the GPU is held to a tolerance.
 """
 from . import fp8, blockquant, gemm, schemes  # noqa: F401
 from .fp8 import dec_e4m3, dec_e5m2, dec_ue8m0, enc_e4m3_sat, enc_e5m2, ue8m0_from_amax  # noqa: F401
