@@ -68,6 +68,69 @@ def test_deepseek_v3_prefill_m8192_ue8m0(dev, name, N, K):
     _check_dense(dev, workloads.DEEPSEEK_V3_PREFILL_M, N, K, "ue8m0", seed=sum(map(ord, name)) + 200)
 
 
+def _check_tiles_in_place(dev, M, N, K, fmt, seed):
+    """Every output tile at full size, without the oracle: a row's sums do not depend on where it
+    sits (same K-block order, same lane inside its 16-row MFMA tile), so permuting the weight
+    rows by whole 128-row blocks (with their scales) must permute the output columns, and
+    permuting the activation rows by groups of 16 (with their scales) must permute the output
+    rows, bit for bit.  A tile computed from the wrong operands or stored to the wrong place
+    (the persistent walk, the per-XCD order, the split between 256x256 and 256x128 tiles)
+    breaks the equality."""
+    x = workloads.device_bf16((M, K), seed, dev)
+    w = workloads.device_bf16((N, K), seed + 1, dev, outliers=False, std=0.02)
+    wq, sw = fgb.quantize_weight(w, "float" if fmt == "f32" else "ue8m0")
+    q, sa = fgb.quantize(x)
+    del x, w
+    y = fgb.gemm(q, sa, wq, sw)
+    rng = np.random.default_rng(seed)
+    pb = _idx(rng.permutation(N // 128), dev)
+    y_w = fgb.gemm(q, sa, wq.view(N // 128, 128, K)[pb].reshape(N, K).contiguous(), sw[pb].contiguous())
+    pg = rng.permutation(M // 16)
+    pr = _idx((pg[:, None] * 16 + np.arange(16)[None, :]).reshape(-1), dev)
+    sa_p = torch.zeros_like(sa)
+    sa_p[:, :M] = sa[:, pr]
+    y_a = fgb.gemm(q[pr].contiguous(), sa_p, wq, sw)
+    torch.cuda.synchronize()
+    expect_w = y.view(M, N // 128, 128)[:, pb].reshape(M, N)
+    assert torch.equal(y_w.view(torch.int16), expect_w.view(torch.int16))
+    assert torch.equal(y_a.view(torch.int16), y[pr].view(torch.int16))
+
+
+@pytest.mark.parametrize("name,N,K", workloads.DEEPSEEK_V3_LINEARS, ids=[s[0] for s in workloads.DEEPSEEK_V3_LINEARS])
+def test_deepseek_v3_prefill_m8192_every_tile_in_place(dev, name, N, K):
+    _check_tiles_in_place(dev, workloads.DEEPSEEK_V3_PREFILL_M, N, K, "ue8m0", seed=sum(map(ord, name)) + 300)
+
+
+@pytest.mark.parametrize("name,N,K", workloads.LLAMA3_8B_LINEARS, ids=[s[0] for s in workloads.LLAMA3_8B_LINEARS])
+def test_llama3_8b_prefill_m4096_every_tile_in_place(dev, name, N, K):
+    _check_tiles_in_place(dev, workloads.LLAMA3_8B_PREFILL_M, N, K, "f32", seed=sum(map(ord, name)) + 350)
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_moe_grouped_full_every_tile_in_place(dev, proj):
+    """The 32-expert grouped GEMM at full size: permuting every expert's weight rows by the same
+    whole 128-row blocks (with their scales) must permute the output columns bit for bit."""
+    cfg = workloads.MOE
+    E = cfg["E"]
+    N, K = cfg[proj]
+    _, offsets, _ = workloads.moe_routing(cfg["tokens"], E, cfg["topk"], cfg["zipf"])
+    T = int(offsets[-1])
+    seed = 600 if proj == "gate_up" else 650
+    x = workloads.device_bf16((T, K), seed, dev)
+    w = workloads.device_bf16((E * N, K), seed + 1, dev, outliers=False, std=0.02)
+    wq, sw = fgb.quantize_weight(w)
+    q, sa = fgb.quantize(x)
+    del x, w
+    off = torch.from_numpy(offsets).to(dev)
+    wq3, sw3 = wq.view(E, N, K), sw.view(E, N // 128, K // 128)
+    y = fgb.grouped_gemm(q, sa, wq3, sw3, off)
+    pb = _idx(np.random.default_rng(seed).permutation(N // 128), dev)
+    y_w = fgb.grouped_gemm(q, sa, wq3.view(E, N // 128, 128, K)[:, pb].reshape(E, N, K).contiguous(),
+                           sw3[:, pb].contiguous(), off)
+    torch.cuda.synchronize()
+    assert torch.equal(y_w.view(torch.int16), y.view(T, N // 128, 128)[:, pb].reshape(T, N).view(torch.int16))
+
+
 @pytest.mark.parametrize("name,N,K", workloads.DECODE_SHAPES, ids=[s[0] for s in workloads.DECODE_SHAPES])
 def test_decode_full_shapes(dev, name, N, K):
     """Every decode batch size at the full weight shape; all M rows are checked."""
