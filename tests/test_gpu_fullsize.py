@@ -132,6 +132,36 @@ def test_moe_grouped_full_every_tile_in_place(dev, proj):
 
 
 @pytest.mark.parametrize("name,N,K", workloads.DECODE_SHAPES, ids=[s[0] for s in workloads.DECODE_SHAPES])
+def test_decode_full_shapes_every_tile_in_place(dev, name, N, K):
+    """The decode kernels at every full decode shape (M = 1, 8, 32, 64: register, per-wave ring,
+    2/4/8-wave shared-ring kernels, K slices and their reduction): the permutation checks of
+    the prefill shapes, columns always, rows by 16-row groups where M has more than one."""
+    seed = sum(map(ord, name)) + 800
+    w = workloads.device_bf16((N, K), seed, dev, outliers=False, std=0.02)
+    wq, sw = fgb.quantize_weight(w)
+    del w
+    rng = np.random.default_rng(seed)
+    pb = _idx(rng.permutation(N // 128), dev)
+    wq_p = wq.view(N // 128, 128, K)[pb].reshape(N, K).contiguous()
+    sw_p = sw[pb].contiguous()
+    for M in (1, 8, 32, 64):
+        x = workloads.device_bf16((M, K), seed + M, dev)
+        q, sa = fgb.quantize(x)
+        y = fgb.gemm(q, sa, wq, sw)
+        y_w = fgb.gemm(q, sa, wq_p, sw_p)
+        torch.cuda.synchronize()
+        assert torch.equal(y_w.view(torch.int16), y.view(M, N // 128, 128)[:, pb].reshape(M, N).view(torch.int16)), M
+        if M >= 32:
+            pg = rng.permutation(M // 16)
+            pr = _idx((pg[:, None] * 16 + np.arange(16)[None, :]).reshape(-1), dev)
+            sa_p = torch.zeros_like(sa)
+            sa_p[:, :M] = sa[:, pr]
+            y_a = fgb.gemm(q[pr].contiguous(), sa_p, wq, sw)
+            torch.cuda.synchronize()
+            assert torch.equal(y_a.view(torch.int16), y[pr].view(torch.int16)), M
+
+
+@pytest.mark.parametrize("name,N,K", workloads.DECODE_SHAPES, ids=[s[0] for s in workloads.DECODE_SHAPES])
 def test_decode_full_shapes(dev, name, N, K):
     """Every decode batch size at the full weight shape; all M rows are checked."""
     seed = sum(map(ord, name)) + 300
