@@ -306,3 +306,41 @@ def test_moe_decode_shaped_full(dev, proj, tokens):
         yref = gemm.gemm_ref(aq, sa_o, wq_s, sw_s, "f32")
         check_t2(bf16_tensor_to_f64(y[_idx(rows, dev)][:, _idx(cols, dev)]), yref)
 
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+@pytest.mark.parametrize("tokens", [8, 64])
+def test_moe_decode_shaped_full_every_tile_in_place(dev, proj, tokens):
+    """The decode-shaped MoE calls at the full expert shapes (grouped 64 rows, batched 64-row
+    slots): permuting every expert's weight rows by the same whole 128-row blocks (with their
+    scales) must permute the output columns bit for bit."""
+    cfg = workloads.MOE
+    E = cfg["E"]
+    N, K = cfg[proj]
+    _, offsets, counts = workloads.moe_routing(tokens=tokens, key=(0, 9, tokens, 1))
+    seed = 950 + tokens + (0 if proj == "gate_up" else 50)
+    w = workloads.device_bf16((E * N, K), seed, dev, outliers=False, std=0.02)
+    wq, sw = fgb.quantize_weight(w)
+    del w
+    wq3, sw3 = wq.view(E, N, K), sw.view(E, N // 128, K // 128)
+    pb = _idx(np.random.default_rng(seed).permutation(N // 128), dev)
+    wq_p = wq3.view(E, N // 128, 128, K)[:, pb].reshape(E, N, K).contiguous()
+    sw_p = sw3[:, pb].contiguous()
+    if tokens == 8:
+        T = int(offsets[-1])
+        q, sa = fgb.quantize(workloads.device_bf16((T, K), seed + 1, dev))
+        off = torch.from_numpy(offsets).to(dev)
+        y = fgb.grouped_gemm(q, sa, wq3, sw3, off)
+        y_w = fgb.grouped_gemm(q, sa, wq_p, sw_p, off)
+        valid = torch.ones(T, dtype=torch.bool, device=dev)
+    else:
+        slot = 64
+        cnt = torch.from_numpy(np.minimum(counts, slot).astype(np.int32)).to(dev)
+        T = E * slot
+        q, sa = fgb.quantize(workloads.device_bf16((T, K), seed + 1, dev))
+        y = fgb.batched_gemm(q, sa, wq3, sw3, cnt, slot)
+        y_w = fgb.batched_gemm(q, sa, wq_p, sw_p, cnt, slot)
+        valid = (torch.arange(slot, device=dev)[None, :] < cnt[:, None]).reshape(-1)
+    torch.cuda.synchronize()
+    expect = y.view(T, N // 128, 128)[:, pb].reshape(T, N)
+    assert torch.equal(y_w[valid].view(torch.int16), expect[valid].view(torch.int16))
