@@ -410,3 +410,28 @@ def test_activation_offsets_near_4gib(dev):
     sa_s = sa[:, ridx].t().contiguous().cpu().numpy()
     yref = gemm.gemm_ref(aq_s, sa_s, wq_np, sw_np, "f32")
     check_t1(y[ridx].cpu().numpy(), yref)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 24, 40, 64])
+@pytest.mark.parametrize("N,K", [(1024, 2048), (6144, 4096), (2048, 24576), (1024, 16512)])
+def test_decode_strides_and_canaries(dev, M, N, K):
+    """Every decode kernel with row pitches above the row lengths (lda = K + 128, ld_sa 12 above M,
+    ldy = N + 64): equal bit for bit to the dense-layout call, and the bytes around the output
+    untouched.  The shapes reach the register kernel, the LDS-ring kernel (2048 x 24576), the
+    per-wave ring for 32/64 rows (1024 x 2048), the 2-wave and the sliced 8-wave shared-ring
+    kernels (6144 x 4096, 1024 x 16512)."""
+    aq, sa, wq, sw = _random_operands(M, N, K, "f32", seed=4200 + M + N)
+    aqd, sad, wqd, swd = upload(aq, sa, wq, sw, dev)
+    dense = fgb.gemm(aqd, sad, wqd, swd, out_dtype=torch.float32)
+    abuf = torch.zeros((M, K + 128), dtype=torch.uint8, device=dev)
+    abuf[:, :K] = aqd
+    ld_sa = (M + 3) // 4 * 4 + 12  # (the library takes 16-byte row pitches)
+    sbuf = torch.full((K // 128, ld_sa), 7.0, dtype=torch.float32, device=dev)
+    sbuf[:, :M] = sad[:, :M]
+    ybuf = torch.full((M + 2, N + 64), -7.0, dtype=torch.float32, device=dev)
+    fgb.gemm(abuf[:, :K], sbuf, wqd, swd, out=ybuf[1:M + 1, 32:N + 32])
+    torch.cuda.synchronize()
+    assert torch.equal(ybuf[1:M + 1, 32:N + 32].view(torch.int32), dense.view(torch.int32))
+    b = ybuf.cpu().numpy()
+    assert np.all(b[0] == -7) and np.all(b[M + 1] == -7)
+    assert np.all(b[:, :32] == -7) and np.all(b[:, N + 32:] == -7)
