@@ -149,3 +149,31 @@ def test_moe_decode_two_tile_passes(dev, fmt):
                           torch.from_numpy(workloads.offsets_from_counts(sub)).to(dev), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert np.array_equal(yg.cpu().numpy().astype(np.float64), y32[rows])
+
+
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_moe_decode_strides_and_canaries(dev, K):
+    """The per-expert streaming kernel (grouped, 40 rows in all; batched 48-row slots) with row
+    pitches above the row lengths (lda = K + 256, ld_sa 8 above the rows, ldy = N + 32): equal
+    bit for bit to the dense-layout calls, the bytes around the output untouched."""
+    E, N = 6, 512
+    counts = np.array([17, 0, 3, 9, 0, 11])
+    T = int(counts.sum())
+    x = workloads.activations(T, K, key=(3, 75, K, 0))
+    aq, sa = blockquant.act_quant(x)
+    wq, sw = _experts(E, N, K, "f32", 12)
+    wqd, swd = torch.from_numpy(wq).to(dev), torch.from_numpy(sw).to(dev)
+    off = torch.from_numpy(workloads.offsets_from_counts(counts)).to(dev)
+    aqd, sad = torch.from_numpy(aq).to(dev), sa_device(sa, dev)
+    dense = fgb.grouped_gemm(aqd, sad, wqd, swd, off, out_dtype=torch.float32)
+    abuf = torch.zeros((T, K + 256), dtype=torch.uint8, device=dev)
+    abuf[:, :K] = aqd
+    ld = sad.shape[1] + 8
+    sbuf = torch.full((K // 128, ld), 3.0, dtype=torch.float32, device=dev)
+    sbuf[:, :T] = sad[:, :T]
+    ybuf = torch.full((T + 2, N + 32), -7.0, dtype=torch.float32, device=dev)
+    fgb.grouped_gemm(abuf[:, :K], sbuf, wqd, swd, off, out=ybuf[1:T + 1, 16:N + 16])
+    torch.cuda.synchronize()
+    assert torch.equal(ybuf[1:T + 1, 16:N + 16].view(torch.int32), dense.view(torch.int32))
+    b = ybuf.cpu().numpy()
+    assert np.all(b[0] == -7) and np.all(b[T + 1] == -7) and np.all(b[:, :16] == -7) and np.all(b[:, N + 16:] == -7)
