@@ -125,3 +125,100 @@ def test_quantize_weight_mismatch():
         fgb.quantize_weight(torch.zeros((200, 256), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="on the GPU"):
         fgb.quantize_weight(torch.zeros((256, 256), dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("case", ["rows_not_e_slots", "counts_len", "counts_dtype", "w_2d"])
+def test_batched_shape_mismatch(case):
+    a_q, s_a, w_q, s_w = _ops(M=64, E=4)   # 4 slots of 16 rows
+    counts = torch.zeros(4, dtype=torch.int32)
+    max_m = 16
+    if case == "rows_not_e_slots":
+        max_m = 20
+    elif case == "counts_len":
+        counts = torch.zeros(3, dtype=torch.int32)
+    elif case == "counts_dtype":
+        counts = counts.to(torch.int64)
+    elif case == "w_2d":
+        w_q = w_q[0]
+    with pytest.raises(ValueError) as ei:
+        fgb.batched_gemm(a_q, s_a, w_q, s_w, counts, max_m)
+    assert "on the GPU" not in str(ei.value)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fgb.batched_gemm(*_ops(M=64, E=4), torch.zeros(4, dtype=torch.int32), 16)
+
+
+@pytest.mark.parametrize("case", ["token_len", "tensor_two", "channel_len", "block_shape", "act_kind", "w_shape",
+                                  "out_shape"])
+def test_scaled_gemm_shape_mismatch(case):
+    M, N, K = 24, 256, 512
+    a_q = torch.zeros((M, K), dtype=torch.uint8)
+    w_q = torch.zeros((N, K), dtype=torch.uint8)
+    s_a = torch.zeros(M, dtype=torch.float32)
+    s_w = torch.zeros(N, dtype=torch.float32)
+    act, out = "token", None
+    if case == "token_len":
+        s_a = torch.zeros(M + 1, dtype=torch.float32)
+    elif case == "tensor_two":
+        act, s_a = "tensor", torch.zeros(2, dtype=torch.float32)
+    elif case == "channel_len":
+        s_w = torch.zeros(N - 1, dtype=torch.float32)
+    elif case == "block_shape":
+        s_w = torch.zeros((2, 3), dtype=torch.float32)
+    elif case == "act_kind":
+        act = "group"
+    elif case == "w_shape":
+        w_q = torch.zeros((N, K + 128), dtype=torch.uint8)
+    elif case == "out_shape":
+        out = torch.zeros((M, N + 1), dtype=torch.float32)
+    with pytest.raises(ValueError) as ei:
+        fgb.scaled_gemm(a_q, s_a, w_q, s_w, act_scale=act, out=out)
+    assert "on the GPU" not in str(ei.value)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fgb.scaled_gemm(torch.zeros((M, K), dtype=torch.uint8), torch.zeros(M, dtype=torch.float32),
+                        torch.zeros((N, K), dtype=torch.uint8), torch.zeros(N, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("case", ["m_too_large", "x_dtype", "w_shape", "sw_shape", "out_shape"])
+def test_fused_quant_shape_mismatch(case):
+    M, N, K = 8, 256, 512
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    w_q = torch.zeros((N, K), dtype=torch.uint8)
+    s_w = torch.zeros((N // 128, K // 128), dtype=torch.float32)
+    out = None
+    if case == "m_too_large":
+        x = torch.zeros((65, K), dtype=torch.bfloat16)
+    elif case == "x_dtype":
+        x = x.float()
+    elif case == "w_shape":
+        w_q = torch.zeros((N, K - 128), dtype=torch.uint8)
+    elif case == "sw_shape":
+        s_w = torch.zeros((N // 128, K // 128 + 1), dtype=torch.float32)
+    elif case == "out_shape":
+        out = torch.zeros((M + 1, N), dtype=torch.bfloat16)
+    with pytest.raises(ValueError) as ei:
+        fgb.gemm_fused_quant(x, w_q, s_w, out=out)
+    assert "on the GPU" not in str(ei.value)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fgb.gemm_fused_quant(torch.zeros((M, K), dtype=torch.bfloat16), torch.zeros((N, K), dtype=torch.uint8),
+                             torch.zeros((N // 128, K // 128), dtype=torch.float32))
+
+
+def test_noalloc_and_scheme_quantizers_mismatch():
+    a_q, s_a, w_q, s_w = _ops()
+    with pytest.raises(ValueError):
+        fgb.gemm_noalloc(a_q, s_a, w_q, s_w, None)
+    with pytest.raises(ValueError):
+        fgb.gemm_noalloc(a_q, s_a, w_q, s_w, torch.zeros((96, 128), dtype=torch.bfloat16))
+    x = torch.zeros((10, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fgb.quantize_per_token(x, out=(torch.zeros((10, 256), dtype=torch.uint8), torch.zeros(9, dtype=torch.float32)))
+    with pytest.raises(ValueError):
+        fgb.quantize_static(x, torch.zeros(2, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        fgb.quantize_static(x, torch.ones(1, dtype=torch.float32), out=torch.zeros((10, 128), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        fgb.quantize_weight_per_channel(torch.zeros((200, 256), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="on the GPU"):
+        fgb.quantize_per_token(x)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fgb.quantize_static(x, torch.ones(1, dtype=torch.float32))
