@@ -56,6 +56,14 @@ __device__ __forceinline__ int4 gload_i4(const void* p) {
   return make_int4(v[0], v[1], v[2], v[3]);
 }
 
+// Data read for the last time (weights streamed by the decode kernels) goes with the non-temporal
+// hint: the 16-byte load below, and this cache-policy operand of the direct-to-LDS copies.
+constexpr int kLastReadAux = 2;
+__device__ __forceinline__ int4 gload_i4_last(const void* p) {
+  const v4i v = __builtin_nontemporal_load((const v4i __attribute__((address_space(1)))*)p);
+  return make_int4(v[0], v[1], v[2], v[3]);
+}
+
 // Weight-block scale as float32 from either storage format.
 template <int SWF>
 __device__ __forceinline__ float load_sw(const void* s_w, int64_t idx) {
