@@ -88,6 +88,24 @@ def test_static_quant_division_golden_pair(dev):
     assert np.all(q.cpu().numpy() == 0x10)
 
 
+@pytest.mark.parametrize("code", CODES)
+def test_quantizers_streamed_size_bit_exact(dev, code):
+    """Inputs of 16 MiB or more take the kernels' streamed form (non-temporal loads and stores):
+    per-token and static codes, and per-token scales, on sampled rows incl. the first and last."""
+    M, K = 2048, 4096  # 16 MiB of bf16
+    x = _x(M, K, 31)
+    xd = to_dev_bf16(x, dev)
+    q, s = fgb.quantize_per_token(xd, code)
+    st = np.float32(0.0123)
+    qs = fgb.quantize_static(xd, torch.tensor([st], dtype=torch.float32, device=dev), code)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(31).choice(M, 40, replace=False)]))
+    qe, se = schemes.token_quant(x[rows], code)
+    assert np.array_equal(q.cpu().numpy()[rows], qe)
+    assert np.array_equal(_f32_bits(s)[rows], se.view(np.uint32))
+    assert np.array_equal(qs.cpu().numpy()[rows], schemes.static_quant(x[rows], st, code))
+
+
 def test_e5m2_block_weight_quant_bit_exact(dev):
     w = _w(256, 1024, 5)
     wf = workloads.bf16_bits_to_f32(w)
