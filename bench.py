@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 MALL_BYTES = 256 << 20
+SMALL_PREFILL_MS = (65, 128, 256, 512)  # rows just above the decode sizes
 
 
 def parse():
@@ -263,7 +264,7 @@ def extra_suites(torch, fgb, workloads, np):
         flush_buf.sum()
 
     # decode — hipGraph loop over rotating weight copies (> 2x MALL in total)
-    dec, fused, fp8dyn = {}, {}, {}
+    dec, fused, fp8dyn, small = {}, {}, {}, {}
     for (name, N, K) in workloads.DECODE_SHAPES:
         w = workloads.device_bf16((N, K), next_seed(), dev, outliers=False, std=0.02)
         wq0, sw = fgb.quantize_weight(w)
@@ -297,10 +298,23 @@ def extra_suites(torch, fgb, workloads, np):
                                                                 out=y, workspace=ws), 4 * copies)
             dbytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
             fp8dyn[f"{name}_{N}x{K}_M{M}"] = dict(us=round(tdyn, 2), frac_hbm=round(dbytes / tdyn / 1e3 / PEAK_HBM_GBS, 3))
+        # a few rows above the decode sizes (batched decode, short prefill chunks): the prefill
+        # kernels, K-sliced where their tiles would leave most CUs idle
+        for M in SMALL_PREFILL_MS:
+            x = workloads.device_bf16((M, K), next_seed(), dev)
+            q, sa = fgb.quantize(x)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.zeros(max(256, fgb.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+            us = _graph_time(torch, lambda i: fgb.gemm(q, sa, wqs[i % copies], sw, out=y, workspace=ws), 4 * copies)
+            byts = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * K / 128 + 2 * M * N
+            small[f"{name}_{N}x{K}_M{M}"] = dict(us=round(us, 2), k_slices=fgb.gemm_workspace_bytes(M, N, K) // (4 * M * N) or 1,
+                                                  frac_hbm=round(byts / us / 1e3 / PEAK_HBM_GBS, 3),
+                                                  frac_mfma=round(2 * M * N * K / us / 1e6 / PEAK_FP8_TFLOPS, 3))
         del wqs, wq0, wcs, wc0
     out["decode"] = dec
     out["decode_fused_quant"] = fused
     out["decode_fp8_dynamic"] = fp8dyn
+    out["prefill_small_m"] = small
 
     # the other schemes at the Llama-3-8B prefill shapes (M = 4096), back to back: FP8_DYNAMIC
     # (per-token activations, per-channel weights, E4M3) and static per-tensor activations with

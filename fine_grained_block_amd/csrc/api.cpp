@@ -112,8 +112,9 @@ int fgb_weight_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
 }
 
 size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || M > 64 || N <= 0 || K <= 0 || N % FGB_BLOCK || K % FGB_BLOCK) return 0;
-  return fgb::decode_workspace_bytes(M, N, K);
+  if (M <= 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  if (N % FGB_BLOCK || K % FGB_BLOCK) return 0;
+  return M <= 64 ? fgb::decode_workspace_bytes(M, N, K) : fgb::prefill_workspace_bytes(M, N, K);
 }
 
 int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
@@ -123,16 +124,14 @@ int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64
   int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K);
   if (st != FGB_OK || M == 0) return st;
   const bool decode = M <= 64;
-  if (decode) {
-    const size_t need = fgb::decode_workspace_bytes(M, N, K);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FGB_ERR_WORKSPACE;
-    if (need > 0 && !aligned16(workspace)) return FGB_ERR_ALIGN;
-  }
+  const size_t need = decode ? fgb::decode_workspace_bytes(M, N, K) : fgb::prefill_workspace_bytes(M, N, K);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FGB_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return FGB_ERR_ALIGN;
   st = check_device();
   if (st != FGB_OK) return st;
   fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K, nullptr, 1};
   if (decode) return launch_status(fgb::launch_gemm_decode(a, workspace, (hipStream_t)stream));
-  return launch_status(fgb::launch_gemm_prefill(a, (hipStream_t)stream));
+  return launch_status(fgb::launch_gemm_prefill(a, workspace, (hipStream_t)stream));
 }
 
 int fgb_w8a8_block_gemm_noalloc(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
@@ -141,17 +140,17 @@ int fgb_w8a8_block_gemm_noalloc(const uint8_t* a_q, int64_t lda, const float* s_
   int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K);
   if (st != FGB_OK || M == 0) return st;
   const bool decode = M <= 64;
-  const size_t need = decode ? fgb::decode_workspace_bytes(M, N, K) : 0;
-  if (need > fgb::kDecodeScratchBytes) return FGB_ERR_WORKSPACE;
+  const size_t need = decode ? fgb::decode_workspace_bytes(M, N, K) : fgb::prefill_workspace_bytes(M, N, K);
+  if (need > fgb::kScratchBytes) return FGB_ERR_WORKSPACE;
   st = check_device();
   if (st != FGB_OK) return st;
   fgb::GemmArgs a{a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K, nullptr, 1};
-  if (!decode) return launch_status(fgb::launch_gemm_prefill(a, (hipStream_t)stream));
   void* ws = nullptr;
-  if (need > 0 && fgb::decode_scratch(&ws) != hipSuccess) {
+  if (need > 0 && fgb::scratch_address(&ws) != hipSuccess) {
     (void)hipGetLastError();
     return FGB_ERR_DEVICE;
   }
+  if (!decode) return launch_status(fgb::launch_gemm_prefill(a, ws, (hipStream_t)stream));
   return launch_status(fgb::launch_gemm_decode(a, ws, (hipStream_t)stream));
 }
 

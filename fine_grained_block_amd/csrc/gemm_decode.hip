@@ -231,15 +231,26 @@ hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, hipStream_t strea
   return hipGetLastError();
 }
 
+hipError_t launch_splitk_reduce(const float* ws, int S, int64_t M, int64_t N, void* y, int y_dtype, int64_t ldy,
+                                hipStream_t stream) {
+  const int64_t total = M * (N / 4);
+  const dim3 rgrid((unsigned)((total + 255) / 256));
+  if (y_dtype == 0)
+    hipLaunchKernelGGL(splitk_reduce_kernel<0>, rgrid, dim3(256), 0, stream, ws, S, M, N, y, ldy, nullptr, 0, nullptr);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, rgrid, dim3(256), 0, stream, ws, S, M, N, y, ldy, nullptr, 0, nullptr);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------------------------
 // Library-owned scratch for callers that cannot allocate (the no-allocation GEMM entry point).
 // One array per GPU, in the code object's device memory for as long as the library is loaded.
 // Host code never uses the array's name as an address: hipGetSymbolAddress gives each device's
 // own copy, looked up once per device and kept.
 // ---------------------------------------------------------------------------------------------
-static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-hipError_t decode_scratch(void** out) {
+hipError_t scratch_address(void** out) {
   static std::mutex mu;
   static void* ptrs[64] = {};
   int dev = -1;

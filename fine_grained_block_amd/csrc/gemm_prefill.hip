@@ -88,7 +88,69 @@ int64_t big_columns(int64_t M, int64_t N, int64_t K) {
   return best_c * Big::BN;
 }
 
-hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
+// K slices for launches whose output tiles would leave most CUs idle (M a little above the decode
+// sizes: e.g. 16 tiles of 256 x 128 for N = 4096 at M = 128, where one launch ran at 0.07 of HBM on
+// 4096 x 14336).  Tiles are 256 x 128 (128 x 128 when N % 256 != 0); the number of slices S
+// fills the CUs with one workgroup each (S * tiles <= CUs), keeps at least 4 K-blocks per slice
+// and at most 16 slices, and keeps the float32 partials (S * M * N * 4 bytes) within the
+// library's scratch size, so that the no-allocation entry point runs the same plan.  S = 1: the
+// tiles are not sliced (at least half the CUs get a tile, or the partials would not fit).  With
+// more than a quarter of the CUs busy unsliced, only slices of at least 16 K-blocks pay for the
+// partials and the second launch (measured: 28672 x 4096 at M = 65-128, 2 slices of 16 blocks,
+// 41-42 -> 34-38 us; 24576 x 1536, 2 slices of 6 blocks, 17.6-18.3 -> 19.5-23.9 us).
+int prefill_splits(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64 || N <= 0 || K <= 0 || N % 128 || K % KBYTES) return 1;
+  const bool half = N % Half::BN == 0;
+  const int64_t bm = half ? Half::BM : Narrow::BM, bn = half ? Half::BN : Narrow::BN;
+  const int64_t tiles = ((M + bm - 1) / bm) * (N / bn);
+  const int64_t cus = cu_count();
+  if (2 * tiles > cus) return 1;
+  const int64_t KB = K / KBYTES;
+  int64_t S = cus / tiles;
+  if (S > KB / 4) S = KB / 4;
+  if (S > 16) S = 16;
+  const int64_t fit = (int64_t)(kScratchBytes / ((size_t)M * (size_t)N * sizeof(float)));
+  if (S > fit) S = fit;
+  if (S < 2) return 1;
+  const int64_t kslice = (KB + S - 1) / S;
+  if (4 * tiles > cus && kslice < 16) return 1;
+  return (int)((KB + kslice - 1) / kslice);  // no empty slice
+}
+
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = prefill_splits(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+namespace {
+
+template <typename C>
+hipError_t launch_sliced(const GemmArgs& a, int S, float* ws, hipStream_t stream) {
+  const int KB = (int)(a.K / KBYTES);
+  GemmArgs b = a;
+  b.kslice = (KB + S - 1) / S;
+  b.y = ws;
+  b.y_dtype = 1;
+  b.ldy = a.N;
+  const int tiles_m = (int)((a.M + C::BM - 1) / C::BM), tiles_n = (int)(a.N / C::BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)S), block(C::THREADS);
+  if (a.s_w_fmt == 0)
+    hipLaunchKernelGGL((gemm_prefill_kernel<C, 0, 1, false, 0, 0, true>), grid, block, 0, stream, b, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_prefill_kernel<C, 1, 1, false, 0, 0, true>), grid, block, 0, stream, b, tiles_m, tiles_n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(ws, S, a.M, a.N, a.y, a.y_dtype, a.ldy, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_prefill(const GemmArgs& a, void* workspace, hipStream_t stream) {
+  const int S = prefill_splits(a.M, a.N, a.K);
+  if (S > 1) {
+    float* ws = reinterpret_cast<float*>(workspace);
+    return a.N % Half::BN == 0 ? launch_sliced<Half>(a, S, ws, stream) : launch_sliced<Narrow>(a, S, ws, stream);
+  }
   if (a.N % Big::BN != 0 || a.N % Half::BN != 0)
     return launch_cfg<Narrow, false>(a, (int)((a.M + Narrow::BM - 1) / Narrow::BM), stream);
   const int64_t n_big = big_columns(a.M, a.N, a.K);

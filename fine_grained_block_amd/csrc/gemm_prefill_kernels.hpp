@@ -109,9 +109,12 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row0, int lane)
 // 1 = weight blocks scaled per K-block, one activation scale per token or per tensor applied in
 // the epilogue; 2 = per-channel weight scales and per-token or per-tensor activation scales, both
 // applied in the epilogue, so the MFMAs accumulate in place with no per-block factor.  CODE: the
-// operands' format (0 E4M3, 1 E5M2; schemes 1 and 2 only).
-template <typename C, int SWF, int OUT, bool GROUPED, int SCH = 0, int CODE = 0>
+// operands' format (0 E4M3, 1 E5M2; schemes 1 and 2 only).  SPLIT: K-sliced launch (dense, scheme
+// 0, float32 output): workgroup (x, y) multiplies tile x over K-blocks y*kslice ..
+// min((y+1)*kslice, K/128) - 1 and writes its float32 partial tile to slice y of y = [S][M][ldy].
+template <typename C, int SWF, int OUT, bool GROUPED, int SCH = 0, int CODE = 0, bool SPLIT = false>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  static_assert(!SPLIT || (!GROUPED && SCH == 0 && OUT == 1), "K slices: dense block scheme, float32 partials");
   static_assert(SCH == 0 || SCH == 1 || SCH == 2, "scheme");
   static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
   // one __shared__ array per stage, so the compiler can tell in-flight copies from reads
@@ -124,7 +127,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   __shared__ __attribute__((aligned(16))) float sas2[C::STAGES > 2 ? C::BM : 4];
 
   const int64_t K = p.K, N = p.N;
-  const int KB = (int)(K / KBYTES);
+  const int KBF = (int)(K / KBYTES);  // K-blocks of a row (the row pitch of s_w)
+  // this workgroup's K-blocks: kb0 .. kb0 + KB - 1 (the whole row unless K is sliced)
+  const int kb0 = SPLIT ? (int)blockIdx.y * p.kslice : 0;
+  const int KB = SPLIT ? min(p.kslice, KBF - kb0) : KBF;
   const int NBLK = (int)(N / 128);
 
   // Grouped: tiles are numbered expert by expert, ceil(rows_e / BM) tile-rows each.  The grid is
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     row0 = (int64_t)r0 + (int64_t)(pid_m - cum) * C::BM;
     row_end = r1;
     wq += (int64_t)e * N * K;
-    sw_base = (int64_t)e * NBLK * KB;
+    sw_base = (int64_t)e * NBLK * KBF;
   } else {
     row0 = (int64_t)pid_m * C::BM;
     row_end = p.M;
@@ -263,9 +269,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.s_a, 0, -1, 0x00020000);
-    const uint32_t koff = (uint32_t)kb * KBYTES;
+    const uint32_t koff = (uint32_t)(kb0 + kb) * KBYTES;
     if (d == 0) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * sa_grp), 4, saoff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(sas + 64 * sa_grp), 4, saoff,
+                                               (uint32_t)((kb0 + kb) * p.ld_sa * 4), 0, 0);
     } else if (d <= C::W_LD) {
       const int i = d - 1;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rs, LPTR(st + (wave + i * C::WAVES) * 8 * KBYTES), 16, woff[i], koff, 0, 0);
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 #pragma unroll
     for (int j = 0; j < C::TM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // The weight-block scales of the tile's block rows, s_w[n0/128 + b, 0 .. KB-1] (either format,
+  // The weight-block scales of the tile's block rows, s_w[n0/128 + b, kb0 .. kb0+KB-1] (either format,
   // decoded to float32), are staged once in LDS (K <= 32768); a step reads its wave's value with
   // one broadcast LDS read.
   constexpr int NBT = C::BN / 128 > 0 ? C::BN / 128 : 1;
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
   if constexpr (SCH != 2) {
     for (int idx = tid; idx < NBT * KB; idx += C::THREADS) {
       const int b = idx / KB, k = idx - b * KB;
-      sws[b * 256 + k] = load_sw<SWF>(p.s_w, sw_base + (n0 / 128 + b) * KB + k);
+      sws[b * 256 + k] = load_sw<SWF>(p.s_w, sw_base + (n0 / 128 + b) * KBF + kb0 + k);
     }
     // own LDS writes complete before the first step's barrier (a barrier without a fence)
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
@@ -499,7 +506,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
       }
     }
   } else {
-    // lane holds 4 consecutive output features of one token per MFMA tile
+    // lane holds 4 consecutive output features of one token per MFMA tile (K-sliced: into this
+    // workgroup's slice of the partial sums)
+    void* const ydst = SPLIT ? (void*)(reinterpret_cast<float*>(p.y) + (int64_t)blockIdx.y * p.M * p.ldy) : p.y;
 #pragma unroll
     for (int j = 0; j < C::TM; ++j) {
       const int64_t m = row0 + wm * (C::BM / C::WM) + j * 16 + (lane & 15);
@@ -507,7 +516,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_prefill_kernel(GemmA
 #pragma unroll
         for (int i = 0; i < C::TN; ++i) {
           const int64_t n = n0 + wn * (C::BN / C::WN) + i * 16 + 4 * (lane >> 4);
-          store4<OUT>(p.y, p.ldy, m, n, acc[i][j]);
+          store4<OUT>(ydst, p.ldy, m, n, acc[i][j]);
         }
       }
     }

@@ -43,10 +43,19 @@ struct GemmArgs {
   // masked batched MoE layout (grouped only): expert e owns rows e*slot .. e*slot + counts[e] - 1,
   // counts[e] read from `offsets` (then E entries); 0 = contiguous rows from offsets [E+1]
   int64_t slot;
+  // K-sliced prefill launch only: K-blocks per slice (slice y starts at K-block y*kslice)
+  int kslice;
 };
 
-// Prefill (M > 64) dense GEMM and the grouped variant.
-hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream);
+// Prefill (M > 64) dense GEMM and the grouped variant.  Launches with too few output tiles to
+// occupy the CUs (M a little above the decode sizes, narrow N) slice K: float32 partials in
+// `workspace` (prefill_workspace_bytes), added in slice order by a second launch.
+int prefill_splits(int64_t M, int64_t N, int64_t K);
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_prefill(const GemmArgs& a, void* workspace, hipStream_t stream);
+// y[m, n] = sum over s of ws[s][m][n] in slice order, as bf16 (y_dtype 0) or float32
+hipError_t launch_splitk_reduce(const float* ws, int S, int64_t M, int64_t N, void* y, int y_dtype, int64_t ldy,
+                                hipStream_t stream);
 // compute units of the current device; output columns of a dense prefill GEMM (N % 256 == 0) that
 // run as 256 x 256 tiles (the rest as 256 x 128 tiles)
 int cu_count();
@@ -86,10 +95,11 @@ int decode_splits(int64_t M, int64_t N, int64_t K);
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream);
 
-// Scratch that the library owns for callers that cannot allocate: kDecodeScratchBytes per GPU
-// (covers every decode workspace: at most 64 x 49024 float32 partials, 12.25 MiB).
-constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+// Scratch that the library owns for callers that cannot allocate: kScratchBytes per GPU.  It
+// covers every workspace of the GEMM: the decode plans need at most 64 x 49024 float32 partials
+// (12.25 MiB), and the K-sliced prefill plan is capped at this size.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
 // The current device's scratch address (looked up once per device).
-hipError_t decode_scratch(void** out);
+hipError_t scratch_address(void** out);
 
 }  // namespace fgb

@@ -68,9 +68,13 @@ hipError_t launch_gemm_scaled_decode(const GemmArgs& a, int sch, int, void* ws, 
 hipError_t launch_encode(const float*, uint8_t*, int64_t, int, int, hipStream_t) { return launched("encode"); }
 hipError_t launch_decode(const uint8_t*, float*, int64_t, int, hipStream_t) { return launched("decode"); }
 hipError_t launch_selftest_quotients(unsigned long long*, hipStream_t) { return launched("selftest"); }
-hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t) {
+hipError_t launch_gemm_prefill(const GemmArgs& a, void* ws, hipStream_t) {
   record(a);
+  g_stub.workspace = ws;
   return launched("gemm_prefill");
+}
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return (M == 128 && N == 4096 && K == 4096) ? (size_t)g_stub.prefill_ws_query : 0;
 }
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t) {
   record(a);
@@ -94,7 +98,7 @@ hipError_t launch_gemm_moe_decode(const GemmArgs& a, int mode, hipStream_t) {
   g_stub.K = mode;  // (the driver checks which layout reached the launcher)
   return launched("moe_decode");
 }
-hipError_t decode_scratch(void** out) {
+hipError_t scratch_address(void** out) {
   *out = (void*)0x200000;  // stands for the library's scratch address
   return hipSuccess;
 }

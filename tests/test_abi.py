@@ -97,9 +97,26 @@ def test_gemm_validation(L):
     assert L.fgb_gemm_workspace_bytes(64, 4096, 4096) == 0
     assert L.fgb_gemm_workspace_bytes(16, 4096, 4096) == 0
     assert L.fgb_gemm_workspace_bytes(1, 4096, 4096) == 0
-    assert L.fgb_gemm_workspace_bytes(128, 4096, 4096) == 0
     # unsliced 16 < M <= 64 shapes (224 workgroups of 128 weight rows) need none either
     assert L.fgb_gemm_workspace_bytes(64, 28672, 4096) == 0
+    # prefill (M > 64): K is sliced when the 256x128 tiles (128x128 when N % 256 != 0) would
+    # occupy fewer than half of the 256 CUs (the count the query assumes without a device):
+    # S = min(CUs / tiles, K-blocks / 4, 16, 32 MiB / (M*N*4)), then S * M * N float32 partials
+    MiB = 1 << 20
+    assert L.fgb_gemm_workspace_bytes(128, 4096, 4096) == 8 * 128 * 4096 * 4      # 16 tiles, 32 K-blocks
+    assert L.fgb_gemm_workspace_bytes(128, 4096, 14336) == 16 * 128 * 4096 * 4    # 16 tiles, 112 K-blocks
+    assert L.fgb_gemm_workspace_bytes(65, 28672, 4096) == 2 * 65 * 28672 * 4      # 112 tiles, 16-block slices
+    assert L.fgb_gemm_workspace_bytes(65, 24576, 1536) == 0                       # 96 tiles, 6-block slices
+    assert L.fgb_gemm_workspace_bytes(128, 7168, 18432) == 9 * 128 * 7168 * 4     # 28 tiles
+    assert L.fgb_gemm_workspace_bytes(200, 1152, 1024) == 2 * 200 * 1152 * 4      # 128x128 tiles, 8 K-blocks
+    assert L.fgb_gemm_workspace_bytes(4096, 4096, 4096) == 0                      # 512 tiles
+    assert L.fgb_gemm_workspace_bytes(1024, 28672, 4096) == 0                     # partials above 32 MiB
+    assert L.fgb_gemm_workspace_bytes(128, 4096, 512) == 0                        # 4 K-blocks: one slice
+    for M, N, K in [(65, 512, 2048), (128, 4096, 14336), (512, 4096, 14336), (300, 1024, 1024)]:
+        assert L.fgb_gemm_workspace_bytes(M, N, K) <= 32 * MiB
+    need = L.fgb_gemm_workspace_bytes(128, 4096, 4096)
+    assert _gemm(L, M=128, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=128) == ERR["WORKSPACE"]
+    assert _gemm(L, M=128, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=128, ws=FAKE, wsb=need - 16) == ERR["WORKSPACE"]
 
 
 def test_fused_quant_workspace(L):
@@ -135,7 +152,8 @@ def test_check_expert_offsets_validation(L):
 
 @pytest.mark.skipif(_has_gpu(), reason="fake pointers must not reach a real device")
 def test_valid_arguments_stop_at_device_check(L):
-    assert _gemm(L) == ERR["DEVICE"]
+    assert _gemm(L, ws=FAKE, wsb=L.fgb_gemm_workspace_bytes(256, 512, 1024)) == ERR["DEVICE"]  # K-sliced prefill
+    assert _gemm(L, M=512, N=512, K=512, lda=512, ld_sa=512) == ERR["DEVICE"]  # unsliced prefill, no workspace
     assert L.fgb_act_quant_group128(FAKE, 64, 1024, 1024, FAKE, 1024, FAKE, 64, None) == ERR["DEVICE"]
     assert L.fgb_fp8_decode(FAKE, FAKE, 256, 0, None) == ERR["DEVICE"]
 
