@@ -114,7 +114,7 @@ int fgb_weight_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
 size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
   if (N % FGB_BLOCK || K % FGB_BLOCK) return 0;
-  return M <= 64 ? fgb::decode_workspace_bytes(M, N, K) : fgb::prefill_workspace_bytes(M, N, K);
+  return fgb::use_decode(M, K) ? fgb::decode_workspace_bytes(M, N, K) : fgb::prefill_workspace_bytes(M, N, K);
 }
 
 int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64_t ld_sa,
@@ -123,7 +123,7 @@ int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64
                         size_t workspace_bytes, void* stream) {
   int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K);
   if (st != FGB_OK || M == 0) return st;
-  const bool decode = M <= 64;
+  const bool decode = fgb::use_decode(M, K);
   const size_t need = decode ? fgb::decode_workspace_bytes(M, N, K) : fgb::prefill_workspace_bytes(M, N, K);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FGB_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return FGB_ERR_ALIGN;
@@ -139,7 +139,7 @@ int fgb_w8a8_block_gemm_noalloc(const uint8_t* a_q, int64_t lda, const float* s_
                                 int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
   int st = validate_gemm(a_q, lda, s_a, ld_sa, w_q, s_w, s_w_fmt, y, y_dtype, ldy, M, N, K);
   if (st != FGB_OK || M == 0) return st;
-  const bool decode = M <= 64;
+  const bool decode = fgb::use_decode(M, K);
   const size_t need = decode ? fgb::decode_workspace_bytes(M, N, K) : fgb::prefill_workspace_bytes(M, N, K);
   if (need > fgb::kScratchBytes) return FGB_ERR_WORKSPACE;
   st = check_device();

@@ -1,4 +1,4 @@
-// gemm_decode.hip — path selection and launches of the decode (M <= 64) block-scaled FP8 GEMM
+// gemm_decode.hip — path selection and launches of the decode (M <= 128) block-scaled FP8 GEMM
 // kernels of gemm_decode_kernels.hpp, and the scratch the library owns for callers that cannot
 // allocate.
 #include <mutex>
@@ -39,7 +39,7 @@ bool decode_ring(int64_t N, int64_t K) { return N * K >= kRingMinWeightBytes && 
 // weights the per-wave copies of all activation rows cost more than the second launch.
 bool ring_mid_rows(int64_t N, int64_t K) { return N * K <= (16ll << 20); }
 
-// K-blocks per workgroup of the 16 < M <= 64 kernel.  One slice when the weight blocks alone give
+// K-blocks per workgroup of the 16 < M <= 128 kernel.  One slice when the weight blocks alone give
 // 160 or more workgroups; otherwise slices for about 224 workgroups (one per CU, most of the
 // 256), each at least 8 blocks long (shorter slices spend their time filling the ring and their
 // partials cost more than the extra CUs bring; measured on the decode shapes).
@@ -52,7 +52,7 @@ int mid_kpw(int64_t N, int64_t K) {
   return (KB + S - 1) / S;
 }
 
-// Waves (16 weight rows each) per workgroup of the 16 < M <= 64 kernel.  With at most 32
+// Waves (16 weight rows each) per workgroup of the 16 < M <= 128 kernel.  With at most 32
 // activation rows and 32-63 K-blocks, workgroups of 2 or 4 waves cover the weight rows without K
 // slices (one launch), 2 when that gives at most 256 workgroups, else 4 up to 512; otherwise 8
 // (one 128-row block).  Measured (graph loop, interleaved A/B, at M = 17/24/32): 6144x4096 with 2
@@ -67,7 +67,7 @@ int mid_waves(int64_t M, int64_t N, int64_t K) {
 }
 
 int decode_splits(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16 || ring_mid_rows(N, K)) return 1;  // these kernels need no workspace
+  if (M <= 16 || (M <= 64 && ring_mid_rows(N, K))) return 1;  // these kernels need no workspace
   if (mid_waves(M, N, K) < 8) return 1;
   const int KB = (int)(K / 128);
   const int kpw = mid_kpw(N, K);
@@ -104,7 +104,7 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
 #undef FGB_RING
     return hipGetLastError();
   }
-  if (a.M > 16 && ring_mid_rows(a.N, a.K)) {
+  if (a.M > 16 && a.M <= 64 && ring_mid_rows(a.N, a.K)) {
     const dim3 grid((unsigned)(a.N / 16));
 #define FGB_RING_MID(SWF, OUT)                                                                                   \
   do {                                                                                                           \
@@ -150,7 +150,8 @@ hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t st
   hipLaunchKernelGGL((gemm_decode_mid_kernel<NW_, MT_, D_, SWF, OUT>), grid, block, 0, stream, a, kpw, S, ws)
 #define FGB_MID_MT(SWF, OUT)                                    \
   do {                                                          \
-    if (a.M > 32) FGB_MID(8, 4, kMidStages, SWF, OUT);          \
+    if (a.M > 64) FGB_MID(8, 8, kMidStages, SWF, OUT);          \
+    else if (a.M > 32) FGB_MID(8, 4, kMidStages, SWF, OUT);     \
     else if (nw == 2) FGB_MID(2, 2, 6, SWF, OUT);               \
     else if (nw == 4) FGB_MID(4, 2, 4, SWF, OUT);               \
     else FGB_MID(8, 2, kMidStages, SWF, OUT);                   \

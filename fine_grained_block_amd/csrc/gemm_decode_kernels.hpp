@@ -527,7 +527,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_decode_fused_quant_small_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// 16 < M <= 64: a workgroup of NW waves owns 16*NW weight rows (16 per wave; 8 waves: one 128-row
+// 16 < M <= 128: a workgroup of NW waves owns 16*NW weight rows (16 per wave; 8 waves: one 128-row
 // weight block) over a slice of K-blocks.  The rows, the 16*MT activation rows (rows >= M repeat
 // row M-1; their results are dropped) and the activation scales of each K-block stream through a
 // ring of D LDS stages shared by the waves, with whole-line buffer-form direct copies issued D-1
@@ -541,13 +541,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_decode_mid_kernel(GemmArgs p,
   static_assert(SCH != 0 || CODE == 0, "the 1x128-group scheme runs on E4M3 operands");
   static_assert(NW == 2 || NW == 4 || NW == 8, "2, 4 or 8 waves");
   constexpr int MROWS = 16 * MT;
-  constexpr int WB = 16 * NW * 128, AB = MROWS * 128, SB = 64 * 4;
+  constexpr int WB = 16 * NW * 128, AB = MROWS * 128, SB = (MT == 8 ? 128 : 64) * 4;
   constexpr int STAGE = WB + AB + SB;
   constexpr int A_GRP = MROWS / 8;                      // 8-row copy groups of the activation rows
   constexpr int A_PER = A_GRP >= NW ? A_GRP / NW : 1;   // activation copies per wave per block
-  constexpr int OPS = 2 + A_PER + (SCH == 0 ? 1 : 0);   // copies per wave per block: W, A, scales
+  constexpr int SA_CP = MT == 8 ? 2 : 1;                // 64-token copies of the activation scales
+  constexpr int OPS = 2 + A_PER + (SCH == 0 ? SA_CP : 0);  // copies per wave per block: W, A, scales
   static_assert(D >= 3 && (D - 2) * OPS <= 63, "three or more stages, in-flight copies within vmcnt");
-  static_assert(MT == 2 || MT == 4, "32 or 64 activation rows");
+  static_assert(MT == 2 || MT == 4 || MT == 8, "32, 64 or 128 activation rows");
+  static_assert(MT != 8 || NW == 8, "128 activation rows: 8 waves");
   static_assert(D * STAGE + 1024 <= 160 * 1024, "the ring fits in LDS");
   // one array: the stages' LDS reads are asm blocks that wait for themselves (below), so the
   // compiler need not tell the stages apart
@@ -580,6 +582,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_decode_mid_kernel(GemmArgs p,
     aoff[j] = (uint32_t)(m * p.lda + (((lane & 7) ^ swz_g(r)) * 16));
   }
   const uint32_t soff = (uint32_t)((lane < M ? lane : M - 1) * 4);
+  const uint32_t soff2 = (uint32_t)((lane + 64 < M ? lane + 64 : M - 1) * 4);  // tokens 64..127
 
   auto issue = [&](int kk, uint8_t* st) {
 #if defined(__HIP_DEVICE_COMPILE__)  // (the builtins exist in the device pass only)
@@ -595,8 +598,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_decode_mid_kernel(GemmArgs p,
 #pragma unroll
     for (int j = 0; j < A_PER; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, LPTR(st + WB + agrp[j] * 1024), 16, aoff[j], koff, 0, 0);
-    if constexpr (SCH == 0)
+    if constexpr (SCH == 0) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(st + WB + AB), 4, soff, (uint32_t)(kb * p.ld_sa * 4), 0, 0);
+      if constexpr (MT == 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rs, LPTR(st + WB + AB + 256), 4, soff2, (uint32_t)(kb * p.ld_sa * 4),
+                                                 0, 0);
+    }
 #endif
   };
   auto stage = [&](int i) -> uint8_t* { return ring + i * STAGE; };
@@ -645,6 +652,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_decode_mid_kernel(GemmArgs p,
           : "v"(w0), "v"(w1), "v"(a0), "v"(a1), "v"(sp)
           : "memory");
     } else {
+      // (MT == 8: token tiles 4..7 follow in a second block)
       asm volatile(
           "ds_read_b128 %0, %14\n\t"
           "ds_read_b128 %1, %15\n\t"
@@ -665,6 +673,28 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_decode_mid_kernel(GemmArgs p,
             "=&v"(ah[2]), "=&v"(al[3]), "=&v"(ah[3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3])
           : "v"(w0), "v"(w1), "v"(a0), "v"(a1), "v"(sp)
           : "memory");
+      if constexpr (MT == 8) {
+        asm volatile(
+            "ds_read_b128 %0, %12 offset:8192\n\t"
+            "ds_read_b128 %1, %13 offset:8192\n\t"
+            "ds_read_b128 %2, %12 offset:10240\n\t"
+            "ds_read_b128 %3, %13 offset:10240\n\t"
+            "ds_read_b128 %4, %12 offset:12288\n\t"
+            "ds_read_b128 %5, %13 offset:12288\n\t"
+            "ds_read_b128 %6, %12 offset:14336\n\t"
+            "ds_read_b128 %7, %13 offset:14336\n\t"
+            "ds_read_b32 %8, %14 offset:256\n\t"
+            "ds_read_b32 %9, %14 offset:320\n\t"
+            "ds_read_b32 %10, %14 offset:384\n\t"
+            "ds_read_b32 %11, %14 offset:448\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(al[MT > 4 ? 4 : 0]), "=&v"(ah[MT > 4 ? 4 : 0]), "=&v"(al[MT > 5 ? 5 : 0]),
+              "=&v"(ah[MT > 5 ? 5 : 0]), "=&v"(al[MT > 6 ? 6 : 0]), "=&v"(ah[MT > 6 ? 6 : 0]),
+              "=&v"(al[MT > 7 ? 7 : 0]), "=&v"(ah[MT > 7 ? 7 : 0]), "=&v"(sa[MT > 4 ? 4 : 0]),
+              "=&v"(sa[MT > 5 ? 5 : 0]), "=&v"(sa[MT > 6 ? 6 : 0]), "=&v"(sa[MT > 7 ? 7 : 0])
+            : "v"(a0), "v"(a1), "v"(sp)
+            : "memory");
+      }
     }
     v8i wf;
     wf[0] = wl[0]; wf[1] = wl[1]; wf[2] = wl[2]; wf[3] = wl[3];

@@ -1,4 +1,4 @@
-// gemm_prefill.hip — launches of the prefill (M > 64) block-scaled FP8 GEMM kernels of
+// gemm_prefill.hip — launches of the prefill block-scaled FP8 GEMM kernels (dense: M > 128) of
 // gemm_prefill_kernels.hpp, dense and grouped (MoE), for gfx950.
 //
 // A dense GEMM splits its output columns between 256 x 256 and 256 x 128 tiles so that the tiles

@@ -83,9 +83,18 @@ hipError_t launch_gemm_decode_fused_small(const GemmArgs& a, const uint16_t* x, 
 // waves per 16-row workgroup that split K in the M <= 16 decode kernels
 int decode_small_waves(int64_t N, int64_t K);
 
-// Decode path selection (M <= 64): the LDS-ring kernel for M <= 16 (large weights, long rows);
+// Whether the block GEMM takes the decode (weight-streaming) kernels: up to 64 rows, and 65-128
+// rows when K has at most 64 blocks (the shared-ring kernel with 128 activation rows); otherwise
+// the prefill tiles.  Measured (graph loop) at 65 / 128 rows against the K-sliced prefill launch:
+// 4096x4096 13.9 / 16.2 vs 16.7 / 21.4 us, 6144x4096 15.3 / 19.3 vs 17.3 / 21.3, 24576x1536
+// 15.3 / 16.2 vs 17.0 / 18.3, 28672x4096 35.6 / 35.5 vs 34.4 / 40.2; with long rows the prefill
+// slices were ahead (7168x18432 42.7 / 43.9 vs 34.7 / 39.7 us, 4096x14336 23.5 / 25.9 vs 22.6 / 27.3).
+constexpr int64_t kDecodeMaxM = 128;
+constexpr bool use_decode(int64_t M, int64_t K) { return M <= 64 || (M <= kDecodeMaxM && K <= 64 * 128); }
+
+// Decode path selection (M <= kDecodeMaxM): the LDS-ring kernel for M <= 16 (large weights, long rows);
 // the per-wave ring kernel for 16 < M <= 64 (small weights); the K-blocks per workgroup of the
-// shared-ring 16 < M <= 64 kernel and its number of slices (> 1: partials and a second launch).
+// shared-ring 16 < M <= 128 kernel and its number of slices (> 1: partials and a second launch).
 bool decode_ring(int64_t N, int64_t K);
 bool ring_mid_rows(int64_t N, int64_t K);
 int mid_kpw(int64_t N, int64_t K);
@@ -96,8 +105,8 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_decode(const GemmArgs& a, void* workspace, hipStream_t stream);
 
 // Scratch that the library owns for callers that cannot allocate: kScratchBytes per GPU.  It
-// covers every workspace of the GEMM: the decode plans need at most 64 x 49024 float32 partials
-// (12.25 MiB), and the K-sliced prefill plan is capped at this size.
+// covers every workspace of the GEMM: the decode plans need at most 128 x 49024 float32 partials
+// (24.5 MiB), and the K-sliced prefill plan is capped at this size.
 constexpr size_t kScratchBytes = (size_t)32 << 20;
 // The current device's scratch address (looked up once per device).
 hipError_t scratch_address(void** out);

@@ -105,7 +105,7 @@ int fgb_weight_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
                               int s_w_fmt, void* stream);
 
 /* Host query: workspace bytes fgb_w8a8_block_gemm needs for this shape (0 if none): the K-sliced
- * decode plans (16 < M <= 64) and the K-sliced prefill plan (M > 64 with too few output tiles to
+ * decode plans (16 < M <= 128) and the K-sliced prefill plan (prefill shapes with too few output tiles to
  * occupy the GPU, at most 32 MiB).  fgb_w8a8_scaled_gemm follows the same decode plan and needs
  * the workspace only for M <= 64. */
 size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -121,9 +121,10 @@ size_t fgb_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   s_w   [N/128, K/128] row-major, float32 or UE8M0 bytes per s_w_fmt;
  *   y     [M, ldy] row-major, bf16 bit patterns or float32 per y_dtype.
  * Size limits (FGB_ERR_SHAPE otherwise): K <= 32768; M*lda, N*K and (K/128)*ld_sa*4 below 2^32.
- * M <= 64 selects the decode (weight-streaming) kernels; for 16 < M <= 64 they may slice K.
- * M > 64 selects the prefill (matrix-core tile) kernels; when their output tiles would occupy
- * fewer than half of the compute units (e.g. N = 4096 at M = 128), K is sliced as well.  A
+ * M <= 64, and 64 < M <= 128 with K <= 8192, select the decode (weight-streaming) kernels; for
+ * 16 < M they may slice K.  Other shapes select the prefill (matrix-core tile) kernels; when their
+ * output tiles would occupy fewer than half of the compute units (e.g. N = 4096 at M = 256), K is
+ * sliced as well.  A
  * sliced shape needs `workspace` of fgb_gemm_workspace_bytes(M, N, K) bytes: device, 16-byte
  * aligned, float32 partial sums added in slice order by a second launch; contents on entry are
  * ignored; 0 bytes (NULL allowed) when the shape is not sliced; FGB_ERR_WORKSPACE if missing or
@@ -141,7 +142,7 @@ int fgb_w8a8_block_gemm(const uint8_t* a_q, int64_t lda, const float* s_a, int64
  * Same arguments, kernels and results as fgb_w8a8_block_gemm; the calls that need a workspace
  * (K-sliced decode and prefill plans) use a scratch array that the library owns instead: 32 MiB
  * per GPU, held until the process ends (every workspace fits: the decode plans need at most
- * 12.25 MiB, the prefill plan is capped at 32 MiB; a shape needing more returns
+ * 24.5 MiB, the prefill plan is capped at 32 MiB; a shape needing more returns
  * FGB_ERR_WORKSPACE).  Allocates nothing.  All calls on one GPU share that GPU's scratch, so
  * calls that may overlap on one GPU (different streams without ordering) race and must not be
  * issued; calls ordered on one stream are fine.  The scratch needs no initial contents.

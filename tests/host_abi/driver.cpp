@@ -70,11 +70,11 @@ int main() {
   EXPECT(fgb_gemm_workspace_bytes(32, 4096, 4096) > 0, 1);
   // prefill with K slices: the plan's workspace is required as well
   g_stub.prefill_ws_query = 8u << 20;
-  EXPECT(fgb_gemm_workspace_bytes(128, 4096, 4096), (size_t)8 << 20);
-  EXPECT(gemm(128, 4096, 4096, 4096, 128, 4096), FGB_ERR_WORKSPACE);
-  EXPECT(gemm(128, 4096, 4096, 4096, 128, 4096, 0, 0, F, F, (8u << 20) - 16), FGB_ERR_WORKSPACE);
-  EXPECT(gemm(128, 4096, 4096, 4096, 128, 4096, 0, 0, F, F + 4, 8u << 20), FGB_ERR_ALIGN);
-  EXPECT(gemm(128, 4096, 4096, 4096, 128, 4096, 0, 0, F, F, 8u << 20), FGB_OK);
+  EXPECT(fgb_gemm_workspace_bytes(256, 4096, 4096), (size_t)8 << 20);
+  EXPECT(gemm(256, 4096, 4096, 4096, 256, 4096), FGB_ERR_WORKSPACE);
+  EXPECT(gemm(256, 4096, 4096, 4096, 256, 4096, 0, 0, F, F, (8u << 20) - 16), FGB_ERR_WORKSPACE);
+  EXPECT(gemm(256, 4096, 4096, 4096, 256, 4096, 0, 0, F, F + 4, 8u << 20), FGB_ERR_ALIGN);
+  EXPECT(gemm(256, 4096, 4096, 4096, 256, 4096, 0, 0, F, F, 8u << 20), FGB_OK);
   if (strcmp(g_stub.last, "gemm_prefill") || g_stub.workspace != P(F)) failures++;
   // the no-allocation variant: no workspace argument; decode calls get the library's scratch
   auto noalloc = [](int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ld_sa, int64_t ldy) {
@@ -86,7 +86,7 @@ int main() {
   EXPECT(noalloc(256, 512, 1024, 1024, 256, 512), FGB_OK);
   if (strcmp(g_stub.last, "gemm_prefill")) failures++;
   if (g_stub.workspace != nullptr) failures++;  // no workspace needed: none passed
-  EXPECT(noalloc(128, 4096, 4096, 4096, 128, 4096), FGB_OK);  // K-sliced prefill: the scratch
+  EXPECT(noalloc(256, 4096, 4096, 4096, 256, 4096), FGB_OK);  // K-sliced prefill: the scratch
   if (strcmp(g_stub.last, "gemm_prefill") || g_stub.workspace != P(0x200000)) failures++;
   EXPECT(noalloc(8, 4096, 4096, 4096, 8, 4096), FGB_OK);
   if (g_stub.workspace != nullptr) failures++;  // no workspace needed: none passed

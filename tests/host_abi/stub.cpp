@@ -74,7 +74,7 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, void* ws, hipStream_t) {
   return launched("gemm_prefill");
 }
 size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  return (M == 128 && N == 4096 && K == 4096) ? (size_t)g_stub.prefill_ws_query : 0;
+  return (M == 256 && N == 4096 && K == 4096) ? (size_t)g_stub.prefill_ws_query : 0;
 }
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t) {
   record(a);

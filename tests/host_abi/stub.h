@@ -14,6 +14,6 @@ struct StubState {
   int64_t M, N, K, E;   // sizes the last GEMM launcher received
   const void* workspace;
   uint64_t ws_bytes_query;  // what decode_workspace_bytes returns for (32, 4096, 4096)
-  uint64_t prefill_ws_query;  // what prefill_workspace_bytes returns for (128, 4096, 4096)
+  uint64_t prefill_ws_query;  // what prefill_workspace_bytes returns for (256, 4096, 4096)
 };
 extern StubState g_stub;

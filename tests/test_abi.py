@@ -99,24 +99,33 @@ def test_gemm_validation(L):
     assert L.fgb_gemm_workspace_bytes(1, 4096, 4096) == 0
     # unsliced 16 < M <= 64 shapes (224 workgroups of 128 weight rows) need none either
     assert L.fgb_gemm_workspace_bytes(64, 28672, 4096) == 0
-    # prefill (M > 64): K is sliced when the 256x128 tiles (128x128 when N % 256 != 0) would
+    # 65-128 rows with K <= 8192: the shared-ring decode kernel with 128 activation rows, K-sliced
+    # by the same rule as at 33-64 rows (the per-wave ring kernel of 4096x4096 stops at 64 rows);
+    # longer rows take the prefill tiles
+    assert L.fgb_gemm_workspace_bytes(128, 4096, 4096) == 4 * 128 * 4096 * 4     # 32 blocks of 128 rows
+    assert L.fgb_gemm_workspace_bytes(100, 28672, 4096) == 0                     # 224 weight blocks
+    assert L.fgb_gemm_workspace_bytes(65, 4096, 14336) == 16 * 65 * 4096 * 4     # prefill: 16 tiles, 16 slices
+    # prefill (M > 128): K is sliced when the 256x128 tiles (128x128 when N % 256 != 0) would
     # occupy fewer than half of the 256 CUs (the count the query assumes without a device):
     # S = min(CUs / tiles, K-blocks / 4, 16, 32 MiB / (M*N*4)), then S * M * N float32 partials
     MiB = 1 << 20
-    assert L.fgb_gemm_workspace_bytes(128, 4096, 4096) == 8 * 128 * 4096 * 4      # 16 tiles, 32 K-blocks
-    assert L.fgb_gemm_workspace_bytes(128, 4096, 14336) == 16 * 128 * 4096 * 4    # 16 tiles, 112 K-blocks
-    assert L.fgb_gemm_workspace_bytes(65, 28672, 4096) == 2 * 65 * 28672 * 4      # 112 tiles, 16-block slices
-    assert L.fgb_gemm_workspace_bytes(65, 24576, 1536) == 0                       # 96 tiles, 6-block slices
-    assert L.fgb_gemm_workspace_bytes(128, 7168, 18432) == 9 * 128 * 7168 * 4     # 28 tiles
+    assert L.fgb_gemm_workspace_bytes(256, 4096, 4096) == 8 * 256 * 4096 * 4      # 32 tiles, 32 K-blocks
+    assert L.fgb_gemm_workspace_bytes(256, 4096, 14336) == 8 * 256 * 4096 * 4     # capped at 32 MiB
+    assert L.fgb_gemm_workspace_bytes(129, 28672, 4096) == 0                      # 224 tiles
+    assert L.fgb_gemm_workspace_bytes(192, 14336, 4096) == 2 * 192 * 14336 * 4    # 112 tiles, 16-block slices
+    assert L.fgb_gemm_workspace_bytes(192, 12288, 1536) == 0                      # 96 tiles, 6-block slices
+    assert L.fgb_gemm_workspace_bytes(384, 7168, 18432) == 3 * 384 * 7168 * 4     # 84 tiles, 48-block slices
     assert L.fgb_gemm_workspace_bytes(200, 1152, 1024) == 2 * 200 * 1152 * 4      # 128x128 tiles, 8 K-blocks
     assert L.fgb_gemm_workspace_bytes(4096, 4096, 4096) == 0                      # 512 tiles
     assert L.fgb_gemm_workspace_bytes(1024, 28672, 4096) == 0                     # partials above 32 MiB
-    assert L.fgb_gemm_workspace_bytes(128, 4096, 512) == 0                        # 4 K-blocks: one slice
-    for M, N, K in [(65, 512, 2048), (128, 4096, 14336), (512, 4096, 14336), (300, 1024, 1024)]:
+    assert L.fgb_gemm_workspace_bytes(256, 4096, 512) == 0                        # 4 K-blocks: one slice
+    for M, N, K in [(130, 512, 2048), (256, 4096, 14336), (512, 4096, 14336), (300, 1024, 1024),
+                    (128, 7168, 18432), (65, 49024, 128 * 8)]:
         assert L.fgb_gemm_workspace_bytes(M, N, K) <= 32 * MiB
-    need = L.fgb_gemm_workspace_bytes(128, 4096, 4096)
-    assert _gemm(L, M=128, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=128) == ERR["WORKSPACE"]
-    assert _gemm(L, M=128, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=128, ws=FAKE, wsb=need - 16) == ERR["WORKSPACE"]
+    for M in (128, 256):
+        need = L.fgb_gemm_workspace_bytes(M, 4096, 4096)
+        assert _gemm(L, M=M, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=M) == ERR["WORKSPACE"]
+        assert _gemm(L, M=M, N=4096, K=4096, lda=4096, ldy=4096, ld_sa=M, ws=FAKE, wsb=need - 16) == ERR["WORKSPACE"]
 
 
 def test_fused_quant_workspace(L):

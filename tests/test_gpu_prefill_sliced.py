@@ -1,5 +1,6 @@
-"""GPU parity: the K-sliced prefill launch (M > 64 with too few output tiles to occupy the CUs)
-against the oracle, through the C-ABI.
+"""GPU parity for the rows just above the decode sizes, against the oracle, through the C-ABI:
+65-128 rows on the shared-ring decode kernel with 128 activation rows (K <= 8192), and the K-sliced
+prefill launch (longer rows, or M > 128, with too few output tiles to occupy the CUs).
 
 Each slice multiplies its K-blocks into a float32 partial tile; a second launch adds the slices in
 order.  The oracle's result is the same sum over K-blocks (Transformers "Fine-grained FP8", intro:
@@ -21,7 +22,27 @@ pytestmark = pytest.mark.gpu
 
 # (M, N, K): 256x128 tiles with 4 slices; 33 K-blocks in 7 slices of 5 (the last one 3);
 # 3 slices of 4 blocks; 128x128 tiles (N % 256 != 0); 3 tile-rows with a ragged last one
-SHAPES = [(65, 512, 2048), (96, 768, 4224), (128, 1024, 1536), (200, 1152, 1024), (300, 2048, 2048)]
+SHAPES = [(130, 512, 2048), (160, 768, 4224), (256, 1024, 1536), (200, 1152, 1024), (300, 2048, 2048)]
+
+# (M, N, K) on the 128-row decode kernel: 2 K slices; 4 slices; 6 slices; 4 slices of 32 weight
+# blocks; one K-block, unsliced; 37 K-blocks in slices of 10 (the last one 7)
+DECODE_128 = [(65, 1024, 2048), (96, 2048, 4096), (128, 512, 6144), (100, 4096, 4096), (128, 256, 128),
+              (77, 1280, 4736)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_128)
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_decode_128_rows_parity(dev, M, N, K, fmt):
+    ops = oracle_operands(M, N, K, key=6, fmt=fmt)
+    yref = ref(*ops, fmt=fmt)
+    aq, sa, wq, sw = upload(*ops, dev)
+    y32 = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.float32)
+    y16 = fgb.gemm(aq, sa, wq, sw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y32 = y32.cpu().numpy()
+    check_t1(y32, yref)
+    check_t2(bf16_tensor_to_f64(y16), yref)
+    assert np.array_equal(bf16_tensor_to_f64(y16), gemm.bf16_rne(y32.astype(np.float64)))
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -44,7 +65,7 @@ def test_sliced_parity(dev, M, N, K, fmt):
 def test_sliced_exact_integers(dev):
     """All scales 1 and every partial and total sum an integer below 2^24: float32 output equal
     to the oracle bit for bit, whatever the slicing."""
-    M, N, K = 128, 1024, 4096
+    M, N, K = 192, 1024, 4096
     assert fgb.gemm_workspace_bytes(M, N, K) > 0
     rng = np.random.default_rng(11)
     ints = np.array([-3, -2, -1, 0, 1, 2, 3], dtype=np.float32)
@@ -93,9 +114,11 @@ def test_sliced_strides_guards_and_repeats(dev):
 
 
 @pytest.mark.parametrize("name,N,K", workloads.DECODE_SHAPES, ids=[s[0] for s in workloads.DECODE_SHAPES])
-def test_sliced_full_decode_shapes(dev, name, N, K):
-    """The full decode weight shapes at M = 65, 128, 256, 512 (batched decode and short prefill
-    chunks), quantized on the device as in the benchmark: sampled rows and weight blocks against
+def test_rows_above_decode_full_shapes(dev, name, N, K):
+    """The full decode weight shapes at M = 65 and 128 (the 128-row decode kernel where K <= 8192,
+    else K-sliced prefill tiles) and 256 and 512 (prefill tiles, K-sliced where they leave most
+    CUs idle): batched decode and short prefill
+    chunks, quantized on the device as in the benchmark.  Sampled rows and weight blocks against
     the oracle, and every output tile in place (a permutation of the weight blocks permutes the
     output columns bit for bit)."""
     seed = sum(map(ord, name)) + 900

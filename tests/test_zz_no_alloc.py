@@ -30,9 +30,11 @@ def _operands(M, N, K, seed):
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_noalloc_matches_workspace_entry(dev, out_dtype):
     # (64, 6144, 4096): 5 K slices, 7.9 MB of partials; (40, 1024, 16512): 15 slices, 2.4 MB;
-    # then calls that use no scratch: prefill, M <= 16, and 24 rows over 32 K-blocks (2-wave
-    # workgroups over the whole K)
-    shapes = [(64, 6144, 4096), (40, 1024, 16512), (300, 1024, 1024), (8, 2048, 2048), (24, 6144, 4096)]
+    # then a K-sliced prefill call (2 slices, in the scratch), calls that use no scratch (M <= 16,
+    # and 24 rows over 32 K-blocks on 2-wave workgroups over the whole K), and 100 rows on the
+    # 128-row decode kernel with 4 K slices
+    shapes = [(64, 6144, 4096), (40, 1024, 16512), (300, 1024, 1024), (8, 2048, 2048), (24, 6144, 4096),
+              (100, 2048, 4096)]
     assert fgb.gemm_workspace_bytes(*shapes[4]) == 0
     assert fgb.gemm_workspace_bytes(*shapes[0]) > fgb.gemm_workspace_bytes(*shapes[1]) > 0
     for i, (M, N, K) in enumerate(shapes):
