@@ -1,8 +1,9 @@
 """GPU: the no-allocation GEMM entry point (fgb_w8a8_block_gemm_noalloc) against the existing
 entry point (fgb_w8a8_block_gemm, given a workspace) and the oracle, through the C-ABI.
 
-Two workspace-needing decode calls in a row, the second with a smaller plan, then calls that
-need no scratch (prefill, M <= 16, 24 rows on 2-wave workgroups); the library's scratch keeps the previous call's contents,
+Two workspace-needing decode calls in a row, the second with a smaller plan, a K-sliced prefill
+call, calls that need no scratch (M <= 16, 24 rows on 2-wave workgroups), and 100 rows on the
+128-row decode kernel with K slices; the library's scratch keeps the previous call's contents,
 which must not matter.  Same kernels, so the outputs are equal bit for bit; both are also held
 to the oracle's tolerance."""
 import numpy as np
