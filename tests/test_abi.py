@@ -105,6 +105,11 @@ def test_gemm_validation(L):
     assert L.fgb_gemm_workspace_bytes(128, 4096, 4096) == 4 * 128 * 4096 * 4     # 32 blocks of 128 rows
     assert L.fgb_gemm_workspace_bytes(100, 28672, 4096) == 0                     # 224 weight blocks
     assert L.fgb_gemm_workspace_bytes(65, 4096, 14336) == 16 * 65 * 4096 * 4     # prefill: 16 tiles, 16 slices
+    # the boundaries of the decode route: K = 8192 (64 blocks) and 128 rows
+    assert L.fgb_gemm_workspace_bytes(100, 4096, 8192) == 7 * 100 * 4096 * 4     # decode, 7 slices of 10
+    assert L.fgb_gemm_workspace_bytes(100, 4096, 8320) == 13 * 100 * 4096 * 4    # prefill, 13 slices of 5
+    assert L.fgb_gemm_workspace_bytes(128, 4096, 8192) == 7 * 128 * 4096 * 4     # decode
+    assert L.fgb_gemm_workspace_bytes(129, 4096, 8192) == 8 * 129 * 4096 * 4     # prefill, 32 tiles
     # prefill (M > 128): K is sliced when the 256x128 tiles (128x128 when N % 256 != 0) would
     # occupy fewer than half of the 256 CUs (the count the query assumes without a device):
     # S = min(CUs / tiles, K-blocks / 4, 16, 32 MiB / (M*N*4)), then S * M * N float32 partials
