@@ -143,3 +143,26 @@ def test_rows_above_decode_full_shapes(dev, name, N, K):
         aq, sa_o = blockquant.act_quant(_bits(x[_idx(rows, dev)]))
         yref = gemm.gemm_ref(aq, sa_o, wq_s, sw_s, "f32")
         check_t2(bf16_tensor_to_f64(y[_idx(rows, dev)][:, _idx(cols, dev)]), yref)
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(65, 701)), 128 * int(rng.integers(1, 17)), 128 * int(rng.integers(1, 41)),
+             "f32" if i % 2 == 0 else "ue8m0") for i in range(n)]
+
+
+@pytest.mark.parametrize("M,N,K,fmt", _random_shapes(24, 2024))
+def test_random_shapes_around_the_routes(dev, M, N, K, fmt):
+    """Seeded random shapes across the 128-row decode route, the K-sliced prefill launch and the
+    unsliced tiles (M 65-700, N up to 2048, K up to 5120, either scale format) against the
+    oracle, float32 and bf16."""
+    ops = oracle_operands(M, N, K, key=M + N + K, fmt=fmt)
+    yref = ref(*ops, fmt=fmt)
+    d = upload(*ops, dev)
+    y32 = fgb.gemm(*d, out_dtype=torch.float32)
+    y16 = fgb.gemm(*d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y32 = y32.cpu().numpy()
+    check_t1(y32, yref)
+    check_t2(bf16_tensor_to_f64(y16), yref)
+    assert np.array_equal(bf16_tensor_to_f64(y16), gemm.bf16_rne(y32.astype(np.float64)))
